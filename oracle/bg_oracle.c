@@ -1,0 +1,433 @@
+/*
+ * bg_oracle.c -- plain, slow CPU oracle.  TEST INFRASTRUCTURE ONLY (see
+ * bg_oracle.h for who may load it and for the passages each part follows).
+ *
+ * Every exact sum goes through one wide two's-complement fixed-point
+ * accumulator (the "wide accumulator that holds every magnitude, one rounding
+ * closes it" idea that "Taming Bitwise Behavior", section 1, lists among the
+ * ways to compute exactly).  Nothing is blocked, fused or reordered beyond
+ * what the descriptor states.
+ */
+#include "bg_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* bit views                                                                */
+/* ------------------------------------------------------------------------ */
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+int or_abi_version(void) { return 1; }
+
+/* fp32 -> bf16: keep the upper 16 bits, rounding the dropped lower 16 bits to
+ * nearest with ties to even; NaN becomes the quiet NaN 0x7fc0 with its sign. */
+uint16_t or_bf16_rne(float x)
+{
+    uint32_t u = f32_bits(x);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+    uint32_t upper = u >> 16;
+    uint32_t lower = u & 0xffffu;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u; /* carries into the exponent, to inf at the top */
+    return (uint16_t)upper;
+}
+
+void or_bf16_rne_n(const float* x, uint16_t* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) y[i] = or_bf16_rne(x[i]);
+}
+
+float or_f32_from_bf16(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+float or_f32_from_i32(int32_t v) { return (float)v; }
+
+/* ------------------------------------------------------------------------ */
+/* wide fixed-point accumulator                                             */
+/* bit p of the 768-bit two's-complement integer stands for 2^(p - KOFF).   */
+/* bf16 products reach down to 2^-266 and fp32 to 2^-149; the top of any sum */
+/* of at most a few hundred bf16 products or fp32 values stays below 2^300. */
+/* ------------------------------------------------------------------------ */
+#define NL 12
+#define KOFF 400
+
+typedef struct { uint64_t w[NL]; } kacc;
+
+static void kacc_add(kacc* a, int neg, uint64_t mag, int exp2)
+{
+    if (mag == 0) return;
+    int pos = exp2 + KOFF;
+    if (pos < 0 || pos + 64 >= NL * 64 - 16) abort(); /* outside the modelled range */
+    int li = pos >> 6, sh = pos & 63;
+    uint64_t lo = mag << sh;
+    uint64_t hi = sh ? (mag >> (64 - sh)) : 0;
+    if (!neg) {
+        unsigned __int128 s = (unsigned __int128)a->w[li] + lo;
+        a->w[li] = (uint64_t)s;
+        uint64_t c = (uint64_t)(s >> 64);
+        s = (unsigned __int128)a->w[li + 1] + hi + c;
+        a->w[li + 1] = (uint64_t)s;
+        c = (uint64_t)(s >> 64);
+        for (int i = li + 2; c && i < NL; i++) {
+            s = (unsigned __int128)a->w[i] + c;
+            a->w[i] = (uint64_t)s;
+            c = (uint64_t)(s >> 64);
+        }
+    } else {
+        uint64_t x = a->w[li];
+        a->w[li] = x - lo;
+        uint64_t b = x < lo;
+        uint64_t t = hi + b; /* hi < 2^63, cannot wrap */
+        x = a->w[li + 1];
+        a->w[li + 1] = x - t;
+        b = x < t;
+        for (int i = li + 2; b && i < NL; i++) {
+            x = a->w[i];
+            a->w[i] = x - 1;
+            b = (x == 0);
+        }
+    }
+}
+
+static int kbit(const uint64_t* m, int p) { return (int)((m[p >> 6] >> (p & 63)) & 1u); }
+
+static int kany_below(const uint64_t* m, int p) /* any set bit in [0, p) */
+{
+    for (int i = 0; i < (p >> 6); i++)
+        if (m[i]) return 1;
+    if (p & 63) return (m[p >> 6] & ((1ull << (p & 63)) - 1)) != 0;
+    return 0;
+}
+
+static uint64_t kbits(const uint64_t* m, int p, int n) /* bits [p, p+n), n <= 32 */
+{
+    uint64_t v = 0;
+    for (int i = n - 1; i >= 0; i--) v = (v << 1) | (uint64_t)kbit(m, p + i);
+    return v;
+}
+
+/* Round the accumulator's exact value to fp32 (RNE or RZ).  An exact zero is
+ * +0 unless every term was a negative zero (IEEE: x + (-x) = +0 under RNE). */
+static float kacc_round_f32(const kacc* a, int mode, int all_neg_zero)
+{
+    uint64_t m[NL];
+    memcpy(m, a->w, sizeof m);
+    int neg = (int)(m[NL - 1] >> 63);
+    if (neg) { /* magnitude = two's-complement negation */
+        uint64_t c = 1;
+        for (int i = 0; i < NL; i++) {
+            uint64_t x = ~m[i];
+            m[i] = x + c;
+            c = (c && m[i] == 0) ? 1 : 0;
+        }
+    }
+    int h = -1;
+    for (int i = NL - 1; i >= 0; i--)
+        if (m[i]) { h = i * 64 + 63 - __builtin_clzll(m[i]); break; }
+    if (h < 0) return all_neg_zero ? -0.0f : 0.0f;
+
+    uint32_t sign = neg ? 0x80000000u : 0u;
+    int e = h - KOFF; /* exponent of the leading bit */
+    if (e > 127)
+        return bits_f32(sign | (mode == OR_ROUND_RNE ? 0x7f800000u : 0x7f7fffffu));
+    int lp = (e >= -126) ? h - 23 : (-149 + KOFF); /* position of the kept LSB */
+    uint64_t kept = kbits(m, lp, (e >= -126) ? 24 : (h - lp + 1));
+    int guard = kbit(m, lp - 1);
+    int sticky = kany_below(m, lp - 1);
+    if (mode == OR_ROUND_RNE && guard && (sticky || (kept & 1u))) kept += 1;
+    uint32_t bits;
+    if (e >= -126)
+        bits = ((uint32_t)(e + 127) << 23) + (uint32_t)(kept - (1ull << 23));
+    else
+        bits = (uint32_t)kept; /* a carry into 2^23 lands on the smallest normal */
+    return bits_f32(sign | bits);
+}
+
+float or_f32_round_sum(int n, const int32_t* sign, const uint64_t* mag,
+                       const int32_t* exp2, int round_mode)
+{
+    kacc a;
+    memset(&a, 0, sizeof a);
+    int all_neg_zero = 1;
+    for (int i = 0; i < n; i++) {
+        if (mag[i] || !sign[i]) all_neg_zero = 0;
+        kacc_add(&a, sign[i], mag[i], exp2[i]);
+    }
+    return kacc_round_f32(&a, round_mode, all_neg_zero);
+}
+
+/* ------------------------------------------------------------------------ */
+/* one matrix instruction                                                   */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int neg;
+    uint64_t mag;  /* value = (-1)^neg * mag * 2^exp2 */
+    int exp2;
+    int align_e;   /* exponent used for the max-exponent alignment */
+    int is_zero;
+} term;
+
+static int bf16_special(uint16_t h) { return ((h >> 7) & 0xff) == 0xff; }
+
+static term bf16_product(uint16_t a, uint16_t b, int exp_mode)
+{
+    term t;
+    int ea = (a >> 7) & 0xff, eb = (b >> 7) & 0xff;
+    uint64_t ma = (uint64_t)(a & 0x7f) | (ea ? 0x80u : 0u);
+    uint64_t mb = (uint64_t)(b & 0x7f) | (eb ? 0x80u : 0u);
+    int Ea = ea ? ea - 127 : -126; /* exponent of the 1.f (or 0.f) form */
+    int Eb = eb ? eb - 127 : -126;
+    t.neg = ((a ^ b) >> 15) & 1;
+    t.mag = ma * mb;            /* exact: at most 16 bits */
+    t.exp2 = Ea + Eb - 14;      /* two 7-bit fractions */
+    t.is_zero = (t.mag == 0);
+    if (exp_mode == OR_EXP_RAW) t.align_e = Ea + Eb; /* significand in [1,4) */
+    else t.align_e = t.is_zero ? 0 : (63 - __builtin_clzll(t.mag)) + t.exp2;
+    return t;
+}
+
+static term f32_term(float x, int exp_mode)
+{
+    term t;
+    uint32_t u = f32_bits(x);
+    int e = (u >> 23) & 0xff;
+    t.neg = (int)(u >> 31);
+    t.mag = (u & 0x7fffffu) | (e ? 0x800000u : 0u);
+    int E = e ? e - 127 : -126;
+    t.exp2 = E - 23;
+    t.is_zero = (t.mag == 0);
+    if (exp_mode == OR_EXP_RAW) t.align_e = E;
+    else t.align_e = t.is_zero ? 0 : (63 - __builtin_clzll(t.mag)) + t.exp2;
+    return t;
+}
+
+/* cut a term to a multiple of 2^lpos (the window's lowest kept bit) */
+static void window_cut(term* t, int lpos, int trunc)
+{
+    if (t->is_zero || t->exp2 >= lpos) return;
+    int sh = lpos - t->exp2;
+    uint64_t kept = sh >= 64 ? 0 : (t->mag >> sh);
+    int lost = sh >= 64 ? (t->mag != 0) : ((t->mag & ((1ull << sh) - 1)) != 0);
+    if (trunc == OR_TRUNC_FLOOR && t->neg && lost) kept += 1; /* toward -inf */
+    t->mag = kept;
+    t->exp2 = lpos;
+}
+
+/* exact sum of terms, window-cut when frac_bits != OR_EXACT, rounded once */
+static float fused_sum(term* ts, int n, const or_mfma_model* m)
+{
+    int all_neg_zero = 1;
+    for (int i = 0; i < n; i++)
+        if (!(ts[i].is_zero && ts[i].neg)) all_neg_zero = 0;
+    if (m->frac_bits != OR_EXACT) {
+        int have = 0, emax = 0;
+        for (int i = 0; i < n; i++)
+            if (!ts[i].is_zero && (!have || ts[i].align_e > emax)) { emax = ts[i].align_e; have = 1; }
+        if (have)
+            for (int i = 0; i < n; i++) window_cut(&ts[i], emax - m->frac_bits, m->trunc);
+    }
+    kacc a;
+    memset(&a, 0, sizeof a);
+    for (int i = 0; i < n; i++) kacc_add(&a, ts[i].neg, ts[i].mag, ts[i].exp2);
+    return kacc_round_f32(&a, m->round, all_neg_zero);
+}
+
+float or_mfma_bf16(const or_mfma_model* m, float acc,
+                   const uint16_t* a, const uint16_t* b, int k)
+{
+    if (k <= 0 || k > 64 || m->group <= 0 || k % m->group) return bits_f32(0x7fc00000u);
+
+    /* infinities and NaNs: the result is special whatever the order */
+    int special = isnan(acc) || isinf(acc);
+    for (int j = 0; j < k; j++) special |= bf16_special(a[j]) | bf16_special(b[j]);
+    if (special) {
+        double s = (double)acc;
+        for (int j = 0; j < k; j++) s += (double)or_f32_from_bf16(a[j]) * (double)or_f32_from_bf16(b[j]);
+        if (isnan(s)) return bits_f32(0x7fc00000u);
+        if (isinf(s)) return (float)s;
+        /* a special input that vanished cannot happen (inf*finite != 0) */
+        return bits_f32(0x7fc00000u);
+    }
+
+    int order[64];
+    for (int i = 0; i < k; i++) order[i] = (m->slot_order[0] < 0) ? i : m->slot_order[i];
+
+    term ts[65];
+    for (int g0 = 0; g0 < k; g0 += m->group) {
+        int n = 0;
+        if (m->acc_in_group) ts[n++] = f32_term(acc, m->exp_mode);
+        for (int i = g0; i < g0 + m->group; i++) ts[n++] = bf16_product(a[order[i]], b[order[i]], m->exp_mode);
+        float s = fused_sum(ts, n, m);
+        if (m->acc_in_group) acc = s;
+        else acc = acc + s; /* a separate fp32 add, RNE */
+    }
+    return acc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM walk, split-K and the combine                                       */
+/* ------------------------------------------------------------------------ */
+int or_split_cuts(int64_t K, int S, int64_t unit, int64_t* cuts)
+{
+    if (S < 1 || K < 0 || unit < 1) return -1;
+    cuts[0] = 0;
+    if (S == 1) { cuts[1] = K; return 0; }
+    int64_t span = (K / (unit * S)) * unit;
+    if (span <= 0) return -1;
+    for (int s = 1; s < S; s++) cuts[s] = (int64_t)s * span;
+    cuts[S] = K;
+    return 0;
+}
+
+float or_tree_balanced(float* v, int n)
+{
+    if (n <= 0) return 0.0f;
+    while (n > 1) {
+        int w = 0;
+        for (int i = 0; i + 1 < n; i += 2) v[w++] = v[i] + v[i + 1];
+        if (n & 1) v[w++] = v[n - 1]; /* odd element carried up unchanged */
+        n = w;
+    }
+    return v[0];
+}
+
+float or_gemm_elem(const or_gemm_desc* d, int64_t K,
+                   const uint16_t* arow, const uint16_t* brow, float* partials)
+{
+    float p[64];
+    int ik = d->instr_k;
+    uint16_t ab[64], bb[64];
+    (void)K;
+    for (int s = 0; s < d->n_split; s++) {
+        float acc = 0.0f;
+        for (int64_t k0 = d->cuts[s]; k0 < d->cuts[s + 1]; k0 += ik) {
+            for (int j = 0; j < ik; j++) {
+                int64_t k = k0 + j;
+                int live = k < d->cuts[s + 1];      /* short last turn: zero padded */
+                ab[j] = live ? arow[k] : (uint16_t)0;
+                bb[j] = live ? brow[k] : (uint16_t)0;
+            }
+            acc = or_mfma_bf16(&d->model, acc, ab, bb, ik);
+        }
+        p[s] = acc;
+    }
+    if (partials) memcpy(partials, p, sizeof(float) * (size_t)d->n_split);
+    float c;
+    if (d->combine == OR_COMBINE_SEQUENTIAL) {
+        c = p[0];
+        for (int s = 1; s < d->n_split; s++) c = c + p[s];
+    } else {
+        c = or_tree_balanced(p, d->n_split);
+    }
+    return c;
+}
+
+static void store_out(const or_gemm_desc* d, void* out, int64_t idx, float v)
+{
+    if (d->out_type == OR_OUT_BF16) ((uint16_t*)out)[idx] = or_bf16_rne(v);
+    else ((float*)out)[idx] = v;
+}
+
+void or_gemm_bf16(const or_gemm_desc* d, int64_t M, int64_t N, int64_t K,
+                  const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                  void* C, int64_t ldc, int32_t n_threads)
+{
+    int64_t total = M * N;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int64_t i = 0; i < total; i++) {
+        int64_t m = i / N, n = i % N;
+        float v = or_gemm_elem(d, K, A + m * lda, B + n * ldb, NULL);
+        store_out(d, C, m * ldc + n, v);
+    }
+}
+
+void or_gemm_bf16_points(const or_gemm_desc* d, int64_t K,
+                         const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         int64_t n_pts, const int64_t* m_idx, const int64_t* n_idx,
+                         void* out, int32_t n_threads)
+{
+#pragma omp parallel for schedule(dynamic, 4) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int64_t i = 0; i < n_pts; i++) {
+        float v = or_gemm_elem(d, K, A + m_idx[i] * lda, B + n_idx[i] * ldb, NULL);
+        store_out(d, out, i, v);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 with power-of-two weight scales                                     */
+/* ------------------------------------------------------------------------ */
+int or_w8a8_pow2(int64_t M, int64_t N, int64_t K,
+                 const int8_t* A, int64_t lda, const int8_t* W, int64_t ldw,
+                 const float* a_scale, const float* w_scale,
+                 uint16_t* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
+                 int32_t n_threads)
+{
+    int bad = 0;
+    int64_t total = M * N;
+#pragma omp parallel for schedule(dynamic, 64) num_threads(n_threads > 0 ? n_threads : 1) reduction(| : bad)
+    for (int64_t i = 0; i < total; i++) {
+        int64_t m = i / N, n = i % N;
+        int64_t acc = 0;
+        for (int64_t k = 0; k < K; k++) acc += (int64_t)A[m * lda + k] * (int64_t)W[n * ldw + k];
+        if (acc > INT32_MAX || acc < INT32_MIN) { bad = 1; continue; }
+        float f = or_f32_from_i32((int32_t)acc); /* RNE above 2^24 */
+        float t = f * w_scale[n];                 /* exact for a power of two */
+        float u = t * a_scale[m];                 /* one RNE */
+        if (Y) Y[m * ldy + n] = or_bf16_rne(u);
+        if (acc_out) acc_out[m * ld_acc + n] = (int32_t)acc;
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fixed-order reductions                                                   */
+/* ------------------------------------------------------------------------ */
+static float load_x(int in_type, const void* X, int64_t idx)
+{
+    if (in_type == OR_IN_BF16) return or_f32_from_bf16(((const uint16_t*)X)[idx]);
+    return ((const float*)X)[idx];
+}
+
+void or_reduce(int in_type, int axis, int64_t rows, int64_t cols,
+               const void* X, int64_t ldx, int32_t leaf_len, int32_t sq_fused,
+               float* out_sum, float* out_sumsq, int32_t n_threads)
+{
+    int64_t n_out = (axis == OR_AXIS_ROW) ? rows : cols;
+    int64_t n = (axis == OR_AXIS_ROW) ? cols : rows;
+    if (leaf_len < 1) return;
+    int64_t n_leaf = (n + leaf_len - 1) / leaf_len;
+#pragma omp parallel num_threads(n_threads > 0 ? n_threads : 1)
+    {
+        float* ls = (float*)malloc(sizeof(float) * (size_t)(n_leaf > 0 ? n_leaf : 1));
+        float* lq = (float*)malloc(sizeof(float) * (size_t)(n_leaf > 0 ? n_leaf : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t o = 0; o < n_out; o++) {
+            for (int64_t l = 0; l < n_leaf; l++) {
+                int64_t j0 = l * leaf_len;
+                int64_t j1 = j0 + leaf_len < n ? j0 + leaf_len : n;
+                float s = 0.0f, q = 0.0f;
+                for (int64_t j = j0; j < j1; j++) {
+                    int64_t idx = (axis == OR_AXIS_ROW) ? o * ldx + j : j * ldx + o;
+                    float x = load_x(in_type, X, idx);
+                    if (j == j0) {          /* no +0 seed */
+                        s = x;
+                        q = x * x;
+                    } else {
+                        s = s + x;
+                        if (sq_fused) q = fmaf(x, x, q);
+                        else { float xx = x * x; q = q + xx; }
+                    }
+                }
+                ls[l] = s;
+                lq[l] = q;
+            }
+            if (out_sum) out_sum[o] = n_leaf ? or_tree_balanced(ls, (int)n_leaf) : 0.0f;
+            if (out_sumsq) out_sumsq[o] = n_leaf ? or_tree_balanced(lq, (int)n_leaf) : 0.0f;
+        }
+        free(ls);
+        free(lq);
+    }
+}

@@ -1,0 +1,154 @@
+/*
+ * bg_oracle.h -- CPU oracle for the fixed-order GEMM and reductions.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the bench may load this library.  It shares no code,
+ * header, table or helper with the GPU library; the only thing both sides
+ * agree on is the descriptor (a JSON document) and the seeded input bytes.
+ *
+ * Everything here is written to be read against the pages, not to be fast:
+ *   - "Taming Bitwise Behavior in GPU Kernels with Tensor Core" (arXiv
+ *     2609.11356), section 3.1 (dependence tree of a reduction), section
+ *     3.2.1 (tensor-core semantics: one rounding per instruction over an exact
+ *     sum), section 3.2.2 (instruction_k, k_loop_step, split-K span / k_cuts /
+ *     partial_dtype / merge_dtype, "a second kernel sums the parts"), section 4
+ *     (the +L/-L/r walks), section 5.1 (count-up, neighbours-first tree).
+ *   - "GPU Arithmetic Emulator" README, section "Tensor Core Matmul": block
+ *     FMA with products kept exact, a max exponent over products and
+ *     accumulator, an alignment window of 2+23+neab bits with truncation, an
+ *     integer sum, truncation to fp32; CoFDA (chained groups) vs FDA.
+ *   - "Deterministic LLM Inference Across GPU Kernels: Power-of-Two INT8
+ *     Quantization Scales ...", section II (Y = (A W^T) s_a s_w with exact
+ *     INT32 accumulation; power-of-two commutation).
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ * (the emulator page's rule: keep the host compiler from fusing mul+add).
+ */
+#ifndef BG_ORACLE_H
+#define BG_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- one matrix instruction, as a model ---------------------------------
+ * The pages give two readings of how one tensor-core instruction sums its
+ * products (they disagree even for NVIDIA, and neither measures gfx950):
+ *   family E ("Taming", 3.2.1): acc <- round(acc + sum_j a_j b_j), the sum
+ *            exact, one rounding.  Here: frac_bits = OR_EXACT.
+ *   family B (emulator README): products exact; e_max over the products and
+ *            the accumulator; every term cut to a window whose lowest kept bit
+ *            sits frac_bits below e_max (2+23+neab window -> frac_bits =
+ *            23+neab); integer sum; truncation to fp32.
+ * Both are instances of one parameterised step: the products of a group (and
+ * optionally the accumulator) are aligned to their largest exponent, cut to a
+ * window (or not), summed exactly and rounded once.  Groups of `group`
+ * products are chained in slot order (CoFDA when group < instruction_k).
+ * Which member describes a given instruction is an experimental fact that the
+ * black-box probe settles; this file only evaluates a member faithfully. */
+#define OR_EXACT (-1)
+
+enum { OR_ROUND_RNE = 0, OR_ROUND_RZ = 1 };
+enum { OR_EXP_RAW = 0,   /* product exponent = ea + eb, significand in [1,4) */
+       OR_EXP_NORM = 1 }; /* exponent of the leading set bit of the exact value */
+enum { OR_TRUNC_TOWARD_ZERO = 0, OR_TRUNC_FLOOR = 1 };
+
+typedef struct {
+    int32_t group;        /* products per fused group, 1..instruction_k       */
+    int32_t frac_bits;    /* window bits below e_max, or OR_EXACT             */
+    int32_t exp_mode;     /* OR_EXP_RAW | OR_EXP_NORM                         */
+    int32_t acc_in_group; /* 1: acc is aligned with the group's products;
+                             0: group summed alone, rounded, then an fp32 add */
+    int32_t round;        /* OR_ROUND_RNE | OR_ROUND_RZ for a group's result  */
+    int32_t trunc;        /* OR_TRUNC_TOWARD_ZERO | OR_TRUNC_FLOOR            */
+    int32_t slot_order[64]; /* slot_order[i] = the k of the i-th product fed
+                               to the adder; identity when slot_order[0] < 0   */
+} or_mfma_model;
+
+/* ---- scalar primitives --------------------------------------------------- */
+uint16_t or_bf16_rne(float x);              /* fp32 -> bf16, ties to even     */
+float    or_f32_from_bf16(uint16_t h);      /* exact                          */
+float    or_f32_from_i32(int32_t v);        /* RNE (C conversion, default FE) */
+void     or_bf16_rne_n(const float* x, uint16_t* y, int64_t n);
+float    or_f32_round_sum(int n, const int32_t* sign, const uint64_t* mag,
+                          const int32_t* exp2, int round_mode);
+            /* exact sum of n terms (-1)^sign * mag * 2^exp2, rounded once */
+
+/* One instruction: acc' = MFMA(acc, a[0..k), b[0..k)) under model m.
+ * a and b are bf16 bit patterns indexed by k. */
+float or_mfma_bf16(const or_mfma_model* m, float acc,
+                   const uint16_t* a, const uint16_t* b, int k);
+
+/* ---- GEMM walk ----------------------------------------------------------
+ * C = A * B^T with A [M][lda] and B [N][ldb] bf16 (K contiguous in both).
+ * For every (m, n) and split s: acc = +0; for k-blocks of instr_k in
+ * ascending k inside [cuts[s], cuts[s+1]) (the last block zero-padded):
+ * acc = MFMA(acc, block).  Partials combined by `combine`, then rounded once
+ * to out_type. */
+enum { OR_COMBINE_BALANCED = 0, OR_COMBINE_SEQUENTIAL = 1 };
+enum { OR_OUT_F32 = 0, OR_OUT_BF16 = 1 };
+
+typedef struct {
+    or_mfma_model model;
+    int32_t instr_k;
+    int32_t n_split;
+    int64_t cuts[65];   /* n_split + 1 cut points, cuts[0] = 0, cuts[S] = K */
+    int32_t combine;
+    int32_t out_type;
+} or_gemm_desc;
+
+/* Cut rule "unit 256, remainder last": span = floor(K / (unit*S)) * unit for
+ * every split but the last; the last gets the rest.  Returns 0, or -1 when a
+ * span would be empty. */
+int or_split_cuts(int64_t K, int S, int64_t unit, int64_t* cuts);
+
+/* Balanced tree, neighbours first, an odd last element carried up unchanged.
+ * Overwrites v. */
+float or_tree_balanced(float* v, int n);
+
+/* one output element; partials (length n_split) may be NULL */
+float or_gemm_elem(const or_gemm_desc* d, int64_t K,
+                   const uint16_t* arow, const uint16_t* brow, float* partials);
+
+/* Full output.  C is float [M][ldc] or uint16 [M][ldc] per out_type. */
+void or_gemm_bf16(const or_gemm_desc* d, int64_t M, int64_t N, int64_t K,
+                  const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                  void* C, int64_t ldc, int32_t n_threads);
+
+/* Selected outputs (m_idx[i], n_idx[i]); out is float or uint16 per out_type. */
+void or_gemm_bf16_points(const or_gemm_desc* d, int64_t K,
+                         const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         int64_t n_pts, const int64_t* m_idx, const int64_t* n_idx,
+                         void* out, int32_t n_threads);
+
+/* ---- W8A8 with power-of-two weight scales ------------------------------
+ * acc = sum_k A[m][k] * W[n][k] exactly (plain definition, int64, must fit
+ * int32); y = bf16_rne( fp32( fp32(acc) * w_scale[n] ) * a_scale[m] ).
+ * Returns 0, or -1 if some accumulator left the int32 range. */
+int or_w8a8_pow2(int64_t M, int64_t N, int64_t K,
+                 const int8_t* A, int64_t lda, const int8_t* W, int64_t ldw,
+                 const float* a_scale, const float* w_scale,
+                 uint16_t* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
+                 int32_t n_threads);
+
+/* ---- fixed-order reductions ---------------------------------------------
+ * out[i] = balanced tree over leaf sums; a leaf is leaf_len consecutive
+ * elements of the reduced axis folded in index order with no +0 seed
+ * (sum: s = x0, s = s + xi; sumsq: s = x0*x0, s = fma(xi, xi, s) when
+ * sq_fused, else s = s + xi*xi with two roundings).  The last leaf may be
+ * short.  axis 0: reduce along a row (one output per row); axis 1: reduce
+ * down a column (one output per column). */
+enum { OR_IN_F32 = 0, OR_IN_BF16 = 1 };
+enum { OR_AXIS_ROW = 0, OR_AXIS_COL = 1 };
+void or_reduce(int in_type, int axis, int64_t rows, int64_t cols,
+               const void* X, int64_t ldx, int32_t leaf_len, int32_t sq_fused,
+               float* out_sum, float* out_sumsq, int32_t n_threads);
+
+int or_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,138 @@
+"""Pins for the oracle's model of one matrix instruction.
+
+Family E ("Taming Bitwise Behavior", section 3.2.1) is checked against the
+exact rational sum with an independently written correct rounding; family B
+(emulator README, "Tensor Core Matmul") against an independent big-integer
+restatement of its four steps.  Both draw ordinary and exponent-spread inputs,
+since narrow exponents hide a regrouping ("Taming", appendix E)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from exact import family_b_instr, family_e_instr
+
+
+def _cases(seed, n, k, spread):
+    if spread:
+        a = synth.bf16_spread(seed, (n, k), -30, 30)
+        b = synth.bf16_spread(seed + 1, (n, k), -30, 30)
+        acc = synth.f32_spread(seed + 2, (n,), -50, 50)
+    else:
+        a = synth.bf16_normal(seed, (n, k))
+        b = synth.bf16_normal(seed + 1, (n, k))
+        acc = synth.f32_normal(seed + 2, (n,), 0.0, 4.0)
+    acc[: n // 8] = 0.0  # instructions that start a chain
+    return acc, a, b
+
+
+@pytest.mark.parametrize("k", [16, 32])
+@pytest.mark.parametrize("spread", [False, True])
+def test_family_e_is_exact_sum_one_rounding(k, spread):
+    acc, a, b = _cases(100 + k + spread, 600, k, spread)
+    got = oracle.mfma_bf16_batch(oracle.family_e(k), acc, a, b)
+    for i in range(len(acc)):
+        ref = family_e_instr(acc[i], a[i], b[i])
+        assert got[i].tobytes() == np.float32(ref).tobytes(), i
+
+
+@pytest.mark.parametrize("nfma,neab", [(8, 1), (16, 2), (4, 0), (16, 1)])
+@pytest.mark.parametrize("spread", [False, True])
+def test_family_b_matches_four_step_restatement(nfma, neab, spread):
+    acc, a, b = _cases(200 + nfma + neab + spread, 600, 16, spread)
+    got = oracle.mfma_bf16_batch(oracle.family_b(nfma, neab), acc, a, b)
+    for i in range(len(acc)):
+        ref = family_b_instr(acc[i], a[i], b[i], nfma, neab)
+        assert got[i].tobytes() == np.float32(ref).tobytes(), (i, got[i], ref)
+
+
+def _model_grid(k=16):
+    for group, fb, em, aig, rnd in itertools.product(
+            [1, 2, 4, 8, 16], [None, 23, 24, 25, 26], ["raw", "norm"], [True, False], ["rne", "rz"]):
+        if k % group:
+            continue
+        yield {"group": group, "frac_bits": fb, "exp_mode": em, "acc_in_group": aig,
+               "round": rnd, "trunc": "toward_zero"}
+
+
+def test_small_integers_are_exact_under_every_model():
+    """Integer inputs whose sum fits the significand give the exact integer
+    whatever the grouping, window or rounding."""
+    rng = np.random.default_rng(9)
+    a = synth.f32_to_bf16_bits(rng.integers(-4, 5, size=(40, 16)).astype(np.float32))
+    b = synth.f32_to_bf16_bits(rng.integers(-4, 5, size=(40, 16)).astype(np.float32))
+    acc = rng.integers(-1000, 1000, size=40).astype(np.float32)
+    exact = acc.astype(np.int64) + (synth.bf16_bits_to_f32(a).astype(np.int64) *
+                                    synth.bf16_bits_to_f32(b).astype(np.int64)).sum(1)
+    for model in _model_grid():
+        got = oracle.mfma_bf16_batch(model, acc, a, b)
+        assert np.array_equal(got.astype(np.int64), exact), model
+
+
+def test_zero_products_are_neutral():
+    """Padding a short turn with zero products changes nothing: a zero has no
+    exponent to raise the alignment maximum and adds nothing to the sum.  So
+    inside one group the place of the zeros, and their sign, cannot matter."""
+    acc, a, b = _cases(300, 200, 16, True)
+    a[:, 10:] = 0
+    b[:, 10:] = 0
+    P = list(range(10, 16)) + list(range(10))  # zeros moved to the front
+    for model in [oracle.family_e(16), oracle.family_b(16, 1), oracle.family_b(16, 2),
+                  dict(oracle.family_b(16, 1), exp_mode="norm")]:
+        full = oracle.mfma_bf16_batch(model, acc, a, b)
+        front = oracle.mfma_bf16_batch(model, acc, a[:, P], b[:, P])
+        assert np.array_equal(full.view(np.uint32), front.view(np.uint32)), model
+        a2 = a.copy()
+        a2[:, 10:] = 0x8000  # -0 times +0 is a negative zero product
+        neg = oracle.mfma_bf16_batch(model, acc, a2, b)
+        assert np.array_equal(full.view(np.uint32), neg.view(np.uint32)), model
+
+
+def test_slot_order_permutes_the_feed():
+    """A model with slot order P on (a, b) equals the k-ordered model on
+    (a[P], b[P])."""
+    acc, a, b = _cases(400, 200, 16, True)
+    P = [0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15]
+    base = oracle.family_b(4, 1)
+    perm = dict(base, slot_order=P)
+    x = oracle.mfma_bf16_batch(perm, acc, a, b)
+    y = oracle.mfma_bf16_batch(base, acc, a[:, P], b[:, P])
+    assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    z = oracle.mfma_bf16_batch(base, acc, a, b)
+    assert not np.array_equal(x.view(np.uint32), z.view(np.uint32))  # the order matters here
+
+
+def test_grouping_is_visible_to_a_cancelling_pair():
+    """'Taming' section 4: r placed beside a cancelling +L/-L pair survives an
+    exact-sum instruction (the pair cancels before the one rounding) but is
+    absorbed where the pair straddles two chained groups (the first group
+    rounds r + L to L)."""
+    L, r = np.float32(1024.0), np.float32(2.0 ** -15)
+    one = synth.f32_to_bf16_bits(np.float32(1.0))
+    a = np.zeros(16, dtype=np.uint16)
+    b = np.full(16, one, dtype=np.uint16)
+    a[0] = synth.f32_to_bf16_bits(r)
+    a[3] = synth.f32_to_bf16_bits(L)
+    a[4] = synth.f32_to_bf16_bits(-L)
+    exact16 = oracle.mfma_bf16(oracle.family_e(16), 0.0, a, b)
+    chained4 = oracle.mfma_bf16(dict(oracle.family_e(16), group=4), 0.0, a, b)
+    assert exact16 == r and chained4 == 0.0
+    a[3], a[4] = 0, 0
+    a[5], a[6] = synth.f32_to_bf16_bits(L), synth.f32_to_bf16_bits(-L)
+    assert oracle.mfma_bf16(dict(oracle.family_e(16), group=4), 0.0, a, b) == r
+
+
+def test_specials():
+    one = synth.f32_to_bf16_bits(np.float32(1.0))
+    inf = np.uint16(0x7F80)
+    a = np.full(16, one, dtype=np.uint16)
+    b = np.zeros(16, dtype=np.uint16)
+    a[2], b[2] = inf, one
+    for model in [oracle.family_e(16), oracle.family_b(8, 1)]:
+        assert oracle.mfma_bf16(model, 1.0, a, b) == np.inf
+        assert np.isnan(oracle.mfma_bf16(model, -np.inf, a, b))
+        b2 = b.copy()
+        b2[2] = 0
+        assert np.isnan(oracle.mfma_bf16(model, 1.0, a, b2))  # inf * 0
