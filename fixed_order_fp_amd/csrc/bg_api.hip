@@ -1,0 +1,395 @@
+// bg_api.hip -- the C ABI of libbitgemm: descriptor validation, order
+// signature, launch plans, and the entry points declared in bitgemm.h.
+//
+// A descriptor is a frozen record of the fields that decide the arithmetic;
+// two equal records owe each other the same bits ("Taming Bitwise Behavior",
+// section 4).  The schedule sub-struct is excluded from the signature: it only
+// chooses tiles and waves (section 3.2.2; appendix E).  A descriptor this build
+// cannot realise exactly is refused, never replaced by another order (the
+// "GPU Mechanism" page's forced-algorithm refusal).
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "bg_internal.h"
+
+#ifndef BG_PROFILE_HASH
+#define BG_PROFILE_HASH 0ull
+#endif
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bg_status fail(bg_status s, const std::string& msg)
+{
+    g_last_error = msg;
+    return s;
+}
+
+// ---- device check: gfx950 only, cached per device ------------------------
+std::mutex g_arch_mu;
+std::vector<int> g_arch_ok;  // -1 unknown, 0 no, 1 yes
+
+bg_status check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BG_E_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if ((int)g_arch_ok.size() <= dev) g_arch_ok.resize(dev + 1, -1);
+    if (g_arch_ok[dev] < 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(BG_E_HIP, "hipGetDeviceProperties failed");
+        g_arch_ok[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 0;
+    }
+    if (!g_arch_ok[dev]) return fail(BG_E_ARCH, "libbitgemm runs on gfx950 (MI355X) only");
+    return BG_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- order signature: FNV-1a 64 over the order fields, two lanes ----------
+struct Fnv {
+    uint64_t h[2] = {0xcbf29ce484222325ull, 0x84222325cbf29ce4ull};
+    void bytes(const void* p, size_t n)
+    {
+        const unsigned char* b = (const unsigned char*)p;
+        for (size_t i = 0; i < n; i++) {
+            h[0] = (h[0] ^ b[i]) * 0x100000001b3ull;
+            h[1] = (h[1] ^ (unsigned char)(b[i] + 0x5b)) * 0x100000001b3ull;
+        }
+    }
+    void u32(uint32_t v) { bytes(&v, 4); }
+    void i64(int64_t v) { bytes(&v, 8); }
+    void u64(uint64_t v) { bytes(&v, 8); }
+};
+
+int instruction_k(uint32_t mfma)
+{
+    switch (mfma) {
+    case BG_MFMA_F32_32X32X16_BF16: return 16;
+    case BG_MFMA_F32_16X16X32_BF16: return 32;
+    case BG_MFMA_I32_32X32X32_I8: return 32;
+    case BG_MFMA_I32_16X16X64_I8: return 64;
+    default: return 0;
+    }
+}
+
+// Cut points for K; BG_OK or BG_E_INVALID.
+bg_status make_cuts(const bg_gemm_desc* d, int64_t K, int64_t* cuts)
+{
+    const int S = (int)d->split_k;
+    if (S < 1 || S > BG_MAX_SPLIT) return fail(BG_E_INVALID, "split_k must be in 1..64");
+    if (K < 1) return fail(BG_E_INVALID, "K must be >= 1");
+    if (d->cut_rule == BG_CUT_EXPLICIT) {
+        if (d->cuts[0] != 0 || d->cuts[S] != K)
+            return fail(BG_E_INVALID, "explicit cuts must start at 0 and end at K");
+        for (int s = 0; s < S; s++) {
+            if (d->cuts[s] >= d->cuts[s + 1]) return fail(BG_E_INVALID, "explicit cuts must increase");
+            cuts[s] = d->cuts[s];
+        }
+        cuts[S] = K;
+        return BG_OK;
+    }
+    if (d->cut_rule != BG_CUT_UNIT_REMAINDER_LAST) return fail(BG_E_INVALID, "unknown cut_rule");
+    if (d->cut_unit < 1) return fail(BG_E_INVALID, "cut_unit must be >= 1");
+    cuts[0] = 0;
+    if (S == 1) {
+        cuts[1] = K;
+        return BG_OK;
+    }
+    const int64_t unit = d->cut_unit;
+    const int64_t span = (K / (unit * S)) * unit;
+    if (span <= 0) return fail(BG_E_INVALID, "a split would be empty: K < unit * split_k");
+    for (int s = 1; s < S; s++) cuts[s] = (int64_t)s * span;
+    cuts[S] = K;
+    return BG_OK;
+}
+
+// Field checks shared by the GEMM entry points.
+bg_status check_common_order(const bg_gemm_desc* d)
+{
+    if (!d) return fail(BG_E_INVALID, "descriptor is NULL");
+    if (d->version != 1) return fail(BG_E_INVALID, "descriptor version must be 1");
+    if (d->k_order != BG_K_ASCENDING) return fail(BG_E_INVALID, "unknown k_order");
+    if (d->short_turn == BG_SHORT_TURN_FIRST)
+        return fail(BG_E_UNSUPPORTED, "short_turn FIRST is not built: a short turn runs last");
+    if (d->short_turn != BG_SHORT_TURN_LAST) return fail(BG_E_INVALID, "unknown short_turn");
+    if (d->k_slot_layout == BG_SLOTS_STRIDED)
+        return fail(BG_E_UNSUPPORTED, "strided k slots are not built");
+    if (d->k_slot_layout != BG_SLOTS_CONTIGUOUS) return fail(BG_E_INVALID, "unknown k_slot_layout");
+    if (d->acc_update == BG_ACC_SEPARATE_ADD)
+        return fail(BG_E_UNSUPPORTED, "acc_update SEPARATE_ADD is not built");
+    if (d->acc_update != BG_ACC_IN_MFMA) return fail(BG_E_INVALID, "unknown acc_update");
+    if (d->odd_rule != BG_ODD_CARRY_LAST) return fail(BG_E_INVALID, "unknown odd_rule");
+    if (d->rounding_point != BG_ROUND_AFTER_COMBINE_RNE) return fail(BG_E_INVALID, "unknown rounding_point");
+    if (d->mfma_profile_hash != BG_PROFILE_HASH)
+        return fail(BG_E_PROFILE, "descriptor's MFMA profile hash is not the one this library was built for");
+    return BG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bg_abi_version(void) { return BG_ABI_VERSION; }
+
+uint64_t bg_profile_hash(void) { return BG_PROFILE_HASH; }
+
+const char* bg_last_error(void) { return g_last_error.c_str(); }
+
+const char* bg_status_str(bg_status s)
+{
+    switch (s) {
+    case BG_OK: return "ok";
+    case BG_E_INVALID: return "invalid argument";
+    case BG_E_UNSUPPORTED: return "unsupported descriptor";
+    case BG_E_WORKSPACE: return "workspace missing or too small";
+    case BG_E_ALIGN: return "misaligned pointer or leading dimension";
+    case BG_E_ARCH: return "device is not gfx950";
+    case BG_E_PROFILE: return "MFMA profile mismatch";
+    case BG_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+bg_status bg_desc_default_gemm(bg_gemm_desc* d)
+{
+    if (!d) return fail(BG_E_INVALID, "descriptor is NULL");
+    *d = bg_gemm_desc{};
+    d->version = 1;
+    d->a_type = BG_BF16;
+    d->b_type = BG_BF16;
+    d->acc_type = BG_FP32;
+    d->out_type = BG_BF16;
+    d->mfma = BG_MFMA_F32_32X32X16_BF16;
+    d->acc_update = BG_ACC_IN_MFMA;
+    d->k_order = BG_K_ASCENDING;
+    d->short_turn = BG_SHORT_TURN_LAST;
+    d->k_slot_layout = BG_SLOTS_CONTIGUOUS;
+    d->split_k = 1;
+    d->cut_rule = BG_CUT_UNIT_REMAINDER_LAST;
+    d->cut_unit = 256;
+    d->partial_type = BG_FP32;
+    d->merge_type = BG_FP32;
+    d->combine = BG_COMBINE_BALANCED;
+    d->odd_rule = BG_ODD_CARRY_LAST;
+    d->rounding_point = BG_ROUND_AFTER_COMBINE_RNE;
+    d->epilogue = BG_EPI_NONE;
+    d->mfma_profile_hash = BG_PROFILE_HASH;
+    return BG_OK;
+}
+
+bg_status bg_desc_default_reduce(bg_reduce_desc* d)
+{
+    if (!d) return fail(BG_E_INVALID, "descriptor is NULL");
+    *d = bg_reduce_desc{};
+    d->version = 1;
+    d->in_type = BG_FP32;
+    d->acc_type = BG_FP32;
+    d->op = BG_RED_SUM_AND_SUMSQ;
+    d->axis = BG_AXIS_ROW;
+    d->leaf_len = 32;
+    d->leaf_order = BG_LEAF_SEQUENTIAL_NO_SEED;
+    d->sq_fma = BG_SQ_FUSED;
+    d->tree = BG_TREE_BALANCED;
+    d->odd_rule = BG_ODD_CARRY_LAST;
+    d->out_type = BG_FP32;
+    return BG_OK;
+}
+
+bg_status bg_desc_signature(const bg_gemm_desc* d, uint64_t sig[2])
+{
+    if (!d || !sig) return fail(BG_E_INVALID, "NULL argument");
+    Fnv f;
+    f.u32(d->version);
+    f.u32(d->a_type);
+    f.u32(d->b_type);
+    f.u32(d->acc_type);
+    f.u32(d->out_type);
+    f.u32(d->mfma);
+    f.u32(d->acc_update);
+    f.u32(d->k_order);
+    f.u32(d->short_turn);
+    f.u32(d->k_slot_layout);
+    f.u32(d->split_k);
+    f.u32(d->cut_rule);
+    if (d->cut_rule == BG_CUT_EXPLICIT) {
+        const uint32_t S = d->split_k <= BG_MAX_SPLIT ? d->split_k : BG_MAX_SPLIT;
+        for (uint32_t s = 0; s <= S; s++) f.i64(d->cuts[s]);
+    } else {
+        f.u32(d->cut_unit);
+    }
+    f.u32(d->partial_type);
+    f.u32(d->merge_type);
+    f.u32(d->combine);
+    f.u32(d->odd_rule);
+    f.u32(d->rounding_point);
+    f.u32(d->epilogue);
+    f.u64(d->mfma_profile_hash);
+    sig[0] = f.h[0];
+    sig[1] = f.h[1];
+    return BG_OK;
+}
+
+bg_status bg_reduce_desc_signature(const bg_reduce_desc* d, uint64_t sig[2])
+{
+    if (!d || !sig) return fail(BG_E_INVALID, "NULL argument");
+    Fnv f;
+    f.u32(0x52454455u);  // a tag so that no reduce signature equals a gemm one
+    f.u32(d->version);
+    f.u32(d->in_type);
+    f.u32(d->acc_type);
+    f.u32(d->op);
+    f.u32(d->axis);
+    f.u32(d->leaf_len);
+    f.u32(d->leaf_order);
+    f.u32(d->sq_fma);
+    f.u32(d->tree);
+    f.u32(d->odd_rule);
+    f.u32(d->out_type);
+    sig[0] = f.h[0];
+    sig[1] = f.h[1];
+    return BG_OK;
+}
+
+bg_status bg_gemm_split_cuts(const bg_gemm_desc* d, int64_t K, int64_t* cuts)
+{
+    if (!d || !cuts) return fail(BG_E_INVALID, "NULL argument");
+    return make_cuts(d, K, cuts);
+}
+
+bg_status bg_gemm_workspace_bytes(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, size_t* bytes)
+{
+    (void)K;
+    if (!d || !bytes) return fail(BG_E_INVALID, "NULL argument");
+    if (M < 0 || N < 0) return fail(BG_E_INVALID, "negative size");
+    if (d->split_k < 1 || d->split_k > BG_MAX_SPLIT) return fail(BG_E_INVALID, "split_k must be in 1..64");
+    *bytes = d->split_k > 1 ? (size_t)d->split_k * (size_t)M * (size_t)N * sizeof(float) : 0;
+    return BG_OK;
+}
+
+bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, void* C, int64_t ldc, void* ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    bg_status st = check_common_order(d);
+    if (st != BG_OK) return st;
+    if (d->a_type != BG_BF16 || d->b_type != BG_BF16)
+        return fail(BG_E_INVALID, "bg_gemm_bf16 takes bf16 operands");
+    if (d->acc_type != BG_FP32) return fail(BG_E_INVALID, "bf16 GEMM accumulates in fp32");
+    if (d->out_type != BG_FP32 && d->out_type != BG_BF16) return fail(BG_E_INVALID, "out_type must be fp32 or bf16");
+    if (d->mfma != BG_MFMA_F32_32X32X16_BF16 && d->mfma != BG_MFMA_F32_16X16X32_BF16)
+        return fail(BG_E_INVALID, "mfma must be a bf16 instruction");
+    if (d->partial_type != BG_FP32 || d->merge_type != BG_FP32)
+        return fail(BG_E_UNSUPPORTED, "only fp32 partials merged in fp32 are built");
+    if (d->combine == BG_COMBINE_SEQUENTIAL) return fail(BG_E_UNSUPPORTED, "sequential combine is not built");
+    if (d->combine != BG_COMBINE_BALANCED) return fail(BG_E_INVALID, "unknown combine");
+    if (d->epilogue != BG_EPI_NONE) return fail(BG_E_INVALID, "bg_gemm_bf16 has no epilogue");
+    if (M < 0 || N < 0) return fail(BG_E_INVALID, "negative size");
+    if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+
+    bg::GemmPlan p{};
+    p.S = (int)d->split_k;
+    st = make_cuts(d, K, p.cuts.c);
+    if (st != BG_OK) return st;
+    for (int s = 0; s <= p.S; s++)
+        if (p.cuts.c[s] % 8) return fail(BG_E_UNSUPPORTED, "cut points must be multiples of 8");
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 8 || ldb % 8 || ldc % 8)
+        return fail(BG_E_ALIGN, "pointers must be 16-byte aligned and leading dimensions multiples of 8");
+    if (p.S > 1) {
+        const size_t need = (size_t)p.S * (size_t)M * (size_t)N * sizeof(float);
+        if (!ws || ws_bytes < need) return fail(BG_E_WORKSPACE, "split-K needs S*M*N*4 bytes of workspace");
+        if (!aligned16(ws)) return fail(BG_E_ALIGN, "workspace must be 16-byte aligned");
+    }
+    p.mfma = (int)d->mfma;
+    p.out_bf16 = d->out_type == BG_BF16;
+    const bg_gemm_schedule& s = d->sched;
+    if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
+        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n))
+            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves) is not compiled in");
+        p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
+    } else {
+        // speed only: the largest tile that still gives the chip enough workgroups
+        const bool i32 = p.mfma == BG_MFMA_F32_32X32X16_BF16;
+        const int64_t wg128 = ((M + 127) / 128) * ((N + 127) / 128) * p.S;
+        const int64_t wg64 = ((M + 63) / 64) * ((N + 63) / 64) * p.S;
+        if (M >= 128 && N >= 128 && wg128 >= 256) {
+            p.bm = 128, p.bn = 128, p.bk = 64, p.waves_m = 2, p.waves_n = 2;
+        } else if (M > 32 && wg64 >= 128) {
+            p.bm = 64, p.bn = 64, p.bk = 64, p.waves_m = 2, p.waves_n = 2;
+        } else if (i32) {
+            p.bm = 32, p.bn = 32, p.bk = 64, p.waves_m = 1, p.waves_n = 1;
+        } else {
+            p.bm = 32, p.bn = 32, p.bk = 64, p.waves_m = 1, p.waves_n = 1;
+        }
+    }
+    st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_gemm_bf16(p, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc,
+                                        (float*)ws, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
+bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, const int8_t* A,
+                            int64_t lda, const int8_t* W, int64_t ldw, const float* a_scale,
+                            const float* w_scale, void* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
+                            hipStream_t stream)
+{
+    (void)d, (void)M, (void)N, (void)K, (void)A, (void)lda, (void)W, (void)ldw, (void)a_scale;
+    (void)w_scale, (void)Y, (void)ldy, (void)acc_out, (void)ld_acc, (void)stream;
+    return fail(BG_E_UNSUPPORTED, "W8A8 path not built yet");
+}
+
+bg_status bg_reduce_workspace_bytes(const bg_reduce_desc* d, int64_t rows, int64_t cols, size_t* bytes)
+{
+    (void)d, (void)rows, (void)cols;
+    if (bytes) *bytes = 0;
+    return fail(BG_E_UNSUPPORTED, "reductions not built yet");
+}
+
+bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols, const void* X, int64_t ldx,
+                         float* out_sum, float* out_sumsq, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    (void)d, (void)rows, (void)cols, (void)X, (void)ldx, (void)out_sum, (void)out_sumsq, (void)ws;
+    (void)ws_bytes, (void)stream;
+    return fail(BG_E_UNSUPPORTED, "reductions not built yet");
+}
+
+bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                                  int64_t ldb, float* C, int64_t ldc, int32_t split_k, hipStream_t stream)
+{
+    (void)M, (void)N, (void)K, (void)A, (void)lda, (void)B, (void)ldb, (void)C, (void)ldc, (void)split_k;
+    (void)stream;
+    return fail(BG_E_UNSUPPORTED, "free-order twin not built yet");
+}
+
+bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, int64_t cols, const void* X,
+                               int64_t ldx, float* out_sum, float* out_sumsq, hipStream_t stream)
+{
+    (void)axis, (void)in_type, (void)rows, (void)cols, (void)X, (void)ldx, (void)out_sum, (void)out_sumsq;
+    (void)stream;
+    return fail(BG_E_UNSUPPORTED, "free-order twin not built yet");
+}
+
+bg_status bg_probe_mfma(uint32_t mfma, int64_t n_cases, const void* A, const void* B, const void* C, void* D,
+                        hipStream_t stream)
+{
+    if (instruction_k(mfma) == 0) return fail(BG_E_INVALID, "unknown mfma");
+    if (n_cases < 0 || n_cases > 0x7fffffff) return fail(BG_E_INVALID, "n_cases out of range");
+    if (n_cases == 0) return BG_OK;
+    if (!A || !B || !C || !D) return fail(BG_E_INVALID, "NULL tensor");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D))
+        return fail(BG_E_ALIGN, "probe tiles must be 16-byte aligned");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_probe((int)mfma, n_cases, A, B, C, D, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
+}  // extern "C"

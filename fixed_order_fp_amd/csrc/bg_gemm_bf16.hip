@@ -1,0 +1,365 @@
+// bg_gemm_bf16.hip -- order-fixed bf16 GEMM C = A * B^T for gfx950, and the
+// fixed-order split-K combine.
+//
+// Order ("Taming Bitwise Behavior", 3.2.1-3.2.2): every output element owns
+// one fp32 accumulator per split, started at +0; the split's k range is walked
+// in blocks of instruction_k in ascending k, one MFMA per block, the short last
+// block zero-padded.  The tile sizes and the wave grid decide only which lane
+// owns which element and how many blocks one LDS turn holds, never which
+// products meet in one instruction or in which order the instructions reach
+// an accumulator -- so they are free speed knobs.  Split partials are written
+// in fp32 and summed by a second kernel, a balanced tree over the split index
+// (neighbours first, an odd one carried up), with no atomics; the cast to the
+// output type happens once, after the combine.
+//
+// Data path: A [BM][BK] and B [BN][BK] tiles move global -> registers -> LDS
+// (16 B per lane, coalesced along K, 16-B chunks XOR-swizzled by row so that
+// the MFMA operand reads, 16 B per lane down 32 rows, hit distinct banks),
+// double-buffered with one barrier per turn; MFMA operands are read from LDS
+// in the placement of the instruction (lane half h holds k 8h..8h+7).
+#include "bg_internal.h"
+
+namespace bg {
+
+namespace {
+
+constexpr int kChunk = 8;  // bf16 per 16-byte chunk
+
+template <int INSTR>
+struct MfmaShape;
+template <>
+struct MfmaShape<BG_MFMA_F32_32X32X16_BF16> {
+    static constexpr int M = 32, N = 32, K = 16, ACC = 16;
+    typedef f32x16 acc_t;
+};
+template <>
+struct MfmaShape<BG_MFMA_F32_16X16X32_BF16> {
+    static constexpr int M = 16, N = 16, K = 32, ACC = 4;
+    typedef f32x4 acc_t;
+};
+
+template <int INSTR>
+__device__ __forceinline__ typename MfmaShape<INSTR>::acc_t mfma(bf16x8 a, bf16x8 b,
+                                                                 typename MfmaShape<INSTR>::acc_t c)
+{
+    if constexpr (INSTR == BG_MFMA_F32_32X32X16_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte chunk of a row: 8 bf16 at k .. k+7, zero beyond k_end or when
+// the row is out of range.
+__device__ __forceinline__ u32x4 load_chunk(const uint16_t* row_ptr, bool row_ok, int64_t k,
+                                            int64_t k_end)
+{
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (!row_ok || k >= k_end) return v;
+    if (k + kChunk <= k_end) return *(const u32x4*)(row_ptr + k);
+    uint16_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) h[j] = (k + j < k_end) ? row_ptr[k + j] : (uint16_t)0;
+    v[0] = h[0] | ((uint32_t)h[1] << 16);
+    v[1] = h[2] | ((uint32_t)h[3] << 16);
+    v[2] = h[4] | ((uint32_t)h[5] << 16);
+    v[3] = h[6] | ((uint32_t)h[7] << 16);
+    return v;
+}
+
+// LDS position (in u32x4 units) of chunk kc of a tile row; chunks of one row
+// are permuted by the low bits of the row index.
+template <int BK>
+__device__ __forceinline__ int lds_slot(int row, int kc)
+{
+    constexpr int CPR = BK / kChunk;  // chunks per row
+    constexpr int MASK = CPR < 8 ? CPR - 1 : 7;
+    return row * CPR + (kc ^ (row & MASK));
+}
+
+template <int INSTR, int BM, int BN, int BK, int WM, int WN, bool OUT_BF16, bool PARTIAL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M, int64_t N, Cuts cuts)
+{
+    typedef MfmaShape<INSTR> S;
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+    constexpr int TM = WTM / S::M, TN = WTN / S::N;
+    constexpr int CPR = BK / kChunk;
+    constexpr int A_CHUNKS = BM * CPR, B_CHUNKS = BN * CPR;
+    constexpr int A_PER_T = (A_CHUNKS + NT - 1) / NT, B_PER_T = (B_CHUNKS + NT - 1) / NT;
+    static_assert(WTM % S::M == 0 && WTN % S::N == 0, "wave tile must hold whole MFMA blocks");
+    static_assert(BK % S::K == 0, "k tile must hold whole instructions");
+
+    __shared__ u32x4 lds_a[2][BM * CPR];
+    __shared__ u32x4 lds_b[2][BN * CPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    const int split = blockIdx.z;
+    const int64_t k_begin = cuts.c[split];
+    const int64_t k_end = cuts.c[split + 1];
+    const int n_turns = (int)((k_end - k_begin + BK - 1) / BK);
+
+    typename S::acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < S::ACC; e++) acc[i][j][e] = 0.0f;
+
+    u32x4 ra[A_PER_T], rb[B_PER_T];
+
+    auto global_load = [&](int turn) {
+        const int64_t kb = k_begin + (int64_t)turn * BK;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; i++) {
+            const int c = tid + i * NT;
+            if (A_CHUNKS % NT == 0 || c < A_CHUNKS) {
+                const int row = c / CPR, kc = c % CPR;
+                const int64_t gm = m0 + row;
+                ra[i] = load_chunk(A + gm * lda, gm < M, kb + kc * kChunk, k_end);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; i++) {
+            const int c = tid + i * NT;
+            if (B_CHUNKS % NT == 0 || c < B_CHUNKS) {
+                const int row = c / CPR, kc = c % CPR;
+                const int64_t gn = n0 + row;
+                rb[i] = load_chunk(B + gn * ldb, gn < N, kb + kc * kChunk, k_end);
+            }
+        }
+    };
+    auto lds_store = [&](int stage) {
+#pragma unroll
+        for (int i = 0; i < A_PER_T; i++) {
+            const int c = tid + i * NT;
+            if (A_CHUNKS % NT == 0 || c < A_CHUNKS) lds_a[stage][lds_slot<BK>(c / CPR, c % CPR)] = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; i++) {
+            const int c = tid + i * NT;
+            if (B_CHUNKS % NT == 0 || c < B_CHUNKS) lds_b[stage][lds_slot<BK>(c / CPR, c % CPR)] = rb[i];
+        }
+    };
+    auto compute = [&](int stage) {
+        // lane's operand row within a block and its chunk offset in a k block
+        const int r_in = lane % S::M;
+        const int kc_in = lane / S::M;  // 0..1 (32x32x16) or 0..3 (16x16x32)
+#pragma unroll
+        for (int ks = 0; ks < BK / S::K; ks++) {
+            bf16x8 a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int row = wm * WTM + i * S::M + r_in;
+                a[i] = __builtin_bit_cast(bf16x8, lds_a[stage][lds_slot<BK>(row, ks * (S::K / kChunk) + kc_in)]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int row = wn * WTN + j * S::N + r_in;
+                b[j] = __builtin_bit_cast(bf16x8, lds_b[stage][lds_slot<BK>(row, ks * (S::K / kChunk) + kc_in)]);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) acc[i][j] = mfma<INSTR>(a[i], b[j], acc[i][j]);
+        }
+    };
+
+    if (n_turns > 0) {
+        global_load(0);
+        lds_store(0);
+        __syncthreads();
+        for (int t = 0; t < n_turns; t++) {
+            if (t + 1 < n_turns) global_load(t + 1);
+            compute(t & 1);
+            if (t + 1 < n_turns) lds_store((t + 1) & 1);
+            __syncthreads();
+        }
+    }
+
+    // epilogue: partial to the workspace, or the one rounding to the output
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < S::ACC; e++) {
+                int rm, cn;
+                if constexpr (S::M == 32) {
+                    rm = 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+                    cn = lane % 32;
+                } else {
+                    rm = 4 * (lane / 16) + e;
+                    cn = lane % 16;
+                }
+                const int64_t gm = m0 + wm * WTM + i * S::M + rm;
+                const int64_t gn = n0 + wn * WTN + j * S::N + cn;
+                if (gm < M && gn < N) {
+                    const float v = acc[i][j][e];
+                    if constexpr (PARTIAL)
+                        ws[((int64_t)split * M + gm) * N + gn] = v;
+                    else if constexpr (OUT_BF16)
+                        ((uint16_t*)C)[gm * ldc + gn] = bf16_rne(v);
+                    else
+                        ((float*)C)[gm * ldc + gn] = v;
+                }
+            }
+}
+
+// Balanced tree over v[0..n), neighbours first, an odd last element carried
+// up unchanged.  With n a compile-time constant the loops unroll and v stays
+// in registers.
+template <int NS>
+__device__ __forceinline__ float tree_fixed(float (&v)[NS])
+{
+    int n = NS;
+#pragma unroll
+    for (int level = 0; level < 7; level++) {
+        if (n <= 1) break;
+        int w = 0;
+#pragma unroll
+        for (int i = 0; i + 1 < NS; i += 2)
+            if (i + 1 < n) v[w++] = v[i] + v[i + 1];
+        if (n & 1) v[w++] = v[n - 1];
+        n = w;
+    }
+    return v[0];
+}
+
+__device__ __forceinline__ float tree_dyn(float* v, int n)
+{
+    while (n > 1) {
+        int w = 0;
+        for (int i = 0; i + 1 < n; i += 2) v[w++] = v[i] + v[i + 1];
+        if (n & 1) v[w++] = v[n - 1];
+        n = w;
+    }
+    return v[0];
+}
+
+template <int NS, bool OUT_BF16>
+__global__ __launch_bounds__(256) void splitk_combine_kernel(const float* __restrict__ ws, int S,
+                                                             int64_t M, int64_t N, void* __restrict__ C,
+                                                             int64_t ldc)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N, n = idx % N;
+    const int64_t plane = M * N;
+    float r;
+    if constexpr (NS > 0) {
+        float v[NS];
+#pragma unroll
+        for (int s = 0; s < NS; s++) v[s] = ws[s * plane + idx];
+        r = tree_fixed<NS>(v);
+    } else {
+        float v[BG_MAX_SPLIT];
+        for (int s = 0; s < S; s++) v[s] = ws[s * plane + idx];
+        r = tree_dyn(v, S);
+    }
+    if constexpr (OUT_BF16)
+        ((uint16_t*)C)[m * ldc + n] = bf16_rne(r);
+    else
+        ((float*)C)[m * ldc + n] = r;
+}
+
+template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+hipError_t launch_tile(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                       const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws,
+                       hipStream_t stream)
+{
+    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.S);
+    dim3 block(64 * WM * WN);
+    if (p.S > 1)
+        hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, true>), grid, block, 0,
+                           stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+    else if (p.out_bf16)
+        hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, true, false>), grid, block, 0,
+                           stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, false>), grid, block, 0,
+                           stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+    return hipGetLastError();
+}
+
+template <bool OUT_BF16>
+hipError_t launch_combine(int S, int64_t M, int64_t N, const float* ws, void* C, int64_t ldc,
+                          hipStream_t stream)
+{
+    const int64_t total = M * N;
+    dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define BG_COMBINE_CASE(NS)                                                                        \
+    case NS:                                                                                       \
+        hipLaunchKernelGGL((splitk_combine_kernel<NS, OUT_BF16>), grid, block, 0, stream, ws, S, M, \
+                           N, C, ldc);                                                             \
+        break;
+    switch (S) {
+        BG_COMBINE_CASE(2)
+        BG_COMBINE_CASE(3)
+        BG_COMBINE_CASE(4)
+        BG_COMBINE_CASE(5)
+        BG_COMBINE_CASE(6)
+        BG_COMBINE_CASE(7)
+        BG_COMBINE_CASE(8)
+        BG_COMBINE_CASE(16)
+    default:
+        hipLaunchKernelGGL((splitk_combine_kernel<0, OUT_BF16>), grid, block, 0, stream, ws, S, M, N,
+                           C, ldc);
+    }
+#undef BG_COMBINE_CASE
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// The tile shapes compiled in: (instruction, BM, BN, BK, waves_m, waves_n).
+#define BG_GEMM_TILES(X)                                            \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2)                \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2)                  \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 64, 1, 2)                  \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 64, 1, 1)                  \
+    X(BG_MFMA_F32_16X16X32_BF16, 128, 128, 64, 2, 2)                \
+    X(BG_MFMA_F32_16X16X32_BF16, 64, 64, 64, 2, 2)                  \
+    X(BG_MFMA_F32_16X16X32_BF16, 32, 32, 64, 1, 1)                  \
+    X(BG_MFMA_F32_16X16X32_BF16, 16, 32, 64, 1, 2)
+
+bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n)
+{
+#define BG_HAS(I, BM_, BN_, BK_, WM_, WN_) \
+    if (mfma == I && bm == BM_ && bn == BN_ && bk == BK_ && waves_m == WM_ && waves_n == WN_) return true;
+    BG_GEMM_TILES(BG_HAS)
+#undef BG_HAS
+    return false;
+}
+
+hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                            int64_t lda, const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws,
+                            hipStream_t stream)
+{
+    (void)K;
+    hipError_t err = hipErrorInvalidValue;
+    bool found = false;
+#define BG_LAUNCH(I, BM_, BN_, BK_, WM_, WN_)                                                           \
+    if (!found && p.mfma == I && p.bm == BM_ && p.bn == BN_ && p.bk == BK_ && p.waves_m == WM_ &&      \
+        p.waves_n == WN_) {                                                                              \
+        found = true;                                                                                    \
+        err = launch_tile<I, BM_, BN_, BK_, WM_, WN_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream);    \
+    }
+    BG_GEMM_TILES(BG_LAUNCH)
+#undef BG_LAUNCH
+    if (!found || err != hipSuccess) return found ? err : hipErrorInvalidValue;
+    if (p.S > 1) {
+        if (p.out_bf16) return launch_combine<true>(p.S, M, N, ws, C, ldc, stream);
+        return launch_combine<false>(p.S, M, N, ws, C, ldc, stream);
+    }
+    return hipSuccess;
+}
+
+}  // namespace bg

@@ -1,0 +1,55 @@
+// bg_internal.h -- shared device types and host launcher declarations of
+// libbitgemm (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bitgemm.h"
+
+namespace bg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest, ties to even; a NaN becomes the quiet
+// NaN 0x7fc0 carrying the input's sign.
+__device__ __forceinline__ uint16_t bf16_rne(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---- plans handed from the C ABI layer to the launchers -------------------
+struct Cuts {
+    int64_t c[BG_MAX_SPLIT + 1];
+};
+
+struct GemmPlan {
+    int S;           // splits
+    Cuts cuts;       // cut points, cuts.c[0] = 0, cuts.c[S] = K
+    int mfma;        // bg_mfma
+    bool out_bf16;   // rounding point target
+    int bm, bn, bk;  // schedule
+    int waves_m, waves_n;
+};
+
+hipError_t launch_probe(int mfma, int64_t n_cases, const void* A, const void* B, const void* C,
+                        void* D, hipStream_t stream);
+
+hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K,
+                            const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                            void* C, int64_t ldc, float* ws, hipStream_t stream);
+
+// which tile shapes the GEMM kernel is instantiated for
+bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n);
+
+}  // namespace bg

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and its host-side descriptor logic (defaults, order
+signature, cut rule, workspace size, refusals) behaves as documented."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitgemm.h")
+
+
+@pytest.fixture(scope="module")
+def bg():
+    import fixed_order_fp_amd as bg
+    if not os.path.exists(bg.LIB_PATH):
+        from fixed_order_fp_amd import build
+        build.build()
+    bg.lib()
+    return bg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(bg):
+    names = declared_functions()
+    assert len(names) >= 15
+    L = C.CDLL(bg.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding covers every one of them
+    assert set(names) <= set(bg.exported_symbols())
+
+
+def test_abi_version_and_profile(bg):
+    assert bg.lib().bg_abi_version() == 1
+    prof = bg.load_profile()
+    from fixed_order_fp_amd.build import profile_hash
+    assert bg.profile_hash() == profile_hash()
+    assert prof["status"] == "measured"
+
+
+def test_signature_covers_order_fields_only(bg):
+    d1 = bg.gemm_desc({})
+    d2 = bg.gemm_desc({"schedule": {"bm": 64, "bn": 64, "bk": 64, "waves_m": 2, "waves_n": 2}})
+    assert bg.signature(d1) == bg.signature(d2)  # a speed knob moves no bit
+    for change in ({"split_k": 2}, {"mfma": "F32_16X16X32_BF16"}, {"out_type": "fp32"},
+                   {"cut_unit": 128}, {"mfma_profile_hash": 1}):
+        assert bg.signature(bg.gemm_desc(change)) != bg.signature(d1), change
+    r1, r2 = bg.reduce_desc({}), bg.reduce_desc({"schedule": {"leaves_per_wg": 8}})
+    assert bg.signature(r1) == bg.signature(r2)
+    assert bg.signature(bg.reduce_desc({"sq_fma": "unfused"})) != bg.signature(r1)
+
+
+def test_cut_rule_and_workspace(bg):
+    for S, spans in ((1, [9728]), (2, [4864, 4864]), (4, [2304] * 3 + [2816]),
+                     (8, [1024] * 7 + [2560]), (16, [512] * 15 + [2048])):
+        cuts = bg.split_cuts(bg.gemm_desc({"split_k": S}), 9728)
+        assert [cuts[i + 1] - cuts[i] for i in range(S)] == spans
+    assert bg.split_cuts(bg.gemm_desc({"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 256, 512]}),
+                         512) == [0, 256, 512]
+    assert bg.gemm_workspace_bytes(bg.gemm_desc({"split_k": 16}), 256, 2560, 9728) == 16 * 256 * 2560 * 4
+    assert bg.gemm_workspace_bytes(bg.gemm_desc({}), 4000, 9728, 2560) == 0
+    with pytest.raises(bg.BgError, match="BG_E_INVALID"):
+        bg.split_cuts(bg.gemm_desc({"split_k": 2}), 256)  # an empty span
+
+
+def _call_gemm(bg, d, M=32, N=64, K=512, lda=512, ptr=0x1000):
+    return bg.lib().bg_gemm_bf16(C.byref(d), M, N, K, C.c_void_p(ptr), lda, C.c_void_p(ptr), K,
+                                 C.c_void_p(ptr), N, None, 0, None)
+
+
+def test_refusals_before_any_launch(bg):
+    """Invalid or unsupported descriptors are refused synchronously, before the
+    device is touched (the pointers here are never dereferenced)."""
+    cases = [
+        ({"split_k": 0}, 1),                     # BG_E_INVALID
+        ({"version": 2}, 1),
+        ({"acc_update": 1}, 2),                  # BG_E_UNSUPPORTED: separate add
+        ({"short_turn": 1}, 2),                  # short turn first
+        ({"k_slot_layout": 1}, 2),               # strided slots
+        ({"combine": "SEQUENTIAL"}, 2),
+        ({"partial_type": "bf16"}, 2),
+        ({"mfma_profile_hash": 12345}, 6),       # BG_E_PROFILE
+        ({"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 100, 512]}, 2),  # cut not a multiple of 8
+        ({"split_k": 2}, 3),                     # BG_E_WORKSPACE: none given
+        ({"schedule": {"bm": 48, "bn": 48, "bk": 64, "waves_m": 1, "waves_n": 1}}, 2),
+    ]
+    for spec, want in cases:
+        st = _call_gemm(bg, bg.gemm_desc(spec))
+        assert st == want, (spec, st, bg.lib().bg_last_error())
+        assert bg.lib().bg_last_error()
+    assert _call_gemm(bg, bg.gemm_desc({}), lda=513) == 4     # BG_E_ALIGN
+    assert _call_gemm(bg, bg.gemm_desc({}), ptr=0x1004) == 4
+    assert _call_gemm(bg, bg.gemm_desc({}), M=0) == 0          # nothing to do

@@ -1,0 +1,143 @@
+"""GPU tests of the order-fixed bf16 GEMM through the C ABI.
+
+Model-free checks first (exact integers, all-ones counts, schedule and
+repeat invariance, batch invariance), then parity with the oracle under the
+measured instruction model: 0 ULP on fp32 and bf16 outputs."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import (from_dev_u16, oracle_desc, print_case, require_gpu, to_dev_u16)
+
+pytestmark = pytest.mark.gpu
+
+INSTRS = ["F32_32X32X16_BF16", "F32_16X16X32_BF16"]
+SCHEDULES = {
+    "F32_32X32X16_BF16": [dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2),
+                          dict(bm=64, bn=64, bk=64, waves_m=2, waves_n=2),
+                          dict(bm=32, bn=64, bk=64, waves_m=1, waves_n=2),
+                          dict(bm=32, bn=32, bk=64, waves_m=1, waves_n=1)],
+    "F32_16X16X32_BF16": [dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2),
+                          dict(bm=64, bn=64, bk=64, waves_m=2, waves_n=2),
+                          dict(bm=32, bn=32, bk=64, waves_m=1, waves_n=1),
+                          dict(bm=16, bn=32, bk=64, waves_m=1, waves_n=2)],
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def run_gemm(spec, A, B, out="fp32"):
+    """A, B: numpy bf16 bits.  Returns numpy fp32 or bf16 bits."""
+    import torch
+    import fixed_order_fp_amd as bg
+    d = bg.gemm_desc(spec, out_type=out)
+    M, K = A.shape
+    N = B.shape[0]
+    dA, dB = to_dev_u16(A), to_dev_u16(B)
+    dC = torch.empty((M, N), dtype=torch.float32 if out == "fp32" else torch.int16, device="cuda")
+    nws = bg.gemm_workspace_bytes(d, M, N, K)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    bg.gemm_bf16(d, dA, dB, dC, ws)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy() if out == "fp32" else from_dev_u16(dC)
+
+
+# ---------------------------------------------------------------------------
+# model-free
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("instr", INSTRS)
+@pytest.mark.parametrize("K", [16, 24, 40, 136])
+def test_small_integers_exact(instr, K):
+    """Entries in {-4..4}: every order gives the exact integer (the K = 16
+    small-integer workload, plus ragged K with a zero-padded short turn)."""
+    print_case("small_int", instr, K)
+    A, B = synth.gemm_small_int(K=K)
+    for sched in SCHEDULES[instr]:
+        C = run_gemm({"mfma": instr, "schedule": sched}, A, B)
+        exact = synth.bf16_bits_to_f32(A).astype(np.int64) @ synth.bf16_bits_to_f32(B).astype(np.int64).T
+        assert np.array_equal(C.astype(np.int64), exact), sched
+
+
+@pytest.mark.parametrize("instr", INSTRS)
+@pytest.mark.parametrize("K,S", [(512, 1), (512, 2), (9728, 1), (9728, 4), (9728, 16), (1000, 3)])
+def test_all_ones_count_every_k(instr, K, S):
+    """All-ones operands: every output is exactly K for every split."""
+    print_case("all_ones", instr, K, S)
+    A = np.full((40, K), 0x3F80, dtype=np.uint16)
+    B = np.full((72, K), 0x3F80, dtype=np.uint16)
+    C = run_gemm({"mfma": instr, "split_k": S}, A, B)
+    assert np.all(C == K)
+
+
+@pytest.mark.parametrize("instr", INSTRS)
+def test_schedules_do_not_move_bits(instr):
+    """Every compiled tile shape and wave grid returns identical bytes
+    ('Taming Bitwise Behavior' 3.2.2: BLOCK_M/N/K are speed knobs)."""
+    print_case("schedules", instr)
+    A = synth.bf16_spread(31, (97, 600), -20, 20)
+    B = synth.bf16_spread(32, (136, 600), -20, 20)
+    for S in (1, 2):
+        outs = [run_gemm({"mfma": instr, "split_k": S, "schedule": s}, A, B) for s in SCHEDULES[instr]]
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("instr", INSTRS)
+def test_repeats_are_identical(instr):
+    print_case("repeats", instr)
+    A, B = synth.gemm_small()
+    first = run_gemm({"mfma": instr, "split_k": 2}, A, B)
+    for _ in range(10):
+        assert np.array_equal(run_gemm({"mfma": instr, "split_k": 2}, A, B).view(np.uint32),
+                              first.view(np.uint32))
+
+
+def test_rows_do_not_depend_on_batch_size():
+    """Batch invariance on the batch-sweep recipe (reduced N): row i is the
+    same for every M > i, with one descriptor for every M."""
+    print_case("batch_invariance")
+    X, W = synth.bf16_normal(1003, (512, 2560)), synth.bf16_normal(2003, (384, 2560), 0.0, 0.02)
+    full = run_gemm({}, X, W, out="bf16")
+    for M in (1, 8, 64, 300):
+        assert np.array_equal(run_gemm({}, X[:M], W, out="bf16"), full[:M]), M
+
+
+# ---------------------------------------------------------------------------
+# parity with the oracle (needs the measured instruction model)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("instr", INSTRS)
+@pytest.mark.parametrize("out", ["fp32", "bf16"])
+def test_small_gemm_parity(instr, out):
+    """The 32x64x512 workload, split-K = 2 cut at 256, partials combined as
+    (p0 + p1); also S = 1 and 4; 0 ULP against the oracle."""
+    import oracle
+    A, B = synth.gemm_small()
+    for S, cuts in ((2, [0, 256, 512]), (1, None), (4, None)):
+        print_case("small_parity", instr, out, S)
+        spec = {"mfma": instr, "split_k": S}
+        if cuts:
+            spec.update(cut_rule="EXPLICIT", cuts=cuts)
+        if S == 4:
+            spec["cut_unit"] = 64
+        got = run_gemm(spec, A, B, out=out)
+        ref = oracle.gemm_bf16(oracle_desc(dict(spec, out_type=out), instr), A, B)
+        assert np.array_equal(got.view(np.uint16 if out == "bf16" else np.uint32),
+                              ref.view(np.uint16 if out == "bf16" else np.uint32))
+
+
+@pytest.mark.parametrize("instr", INSTRS)
+def test_spread_parity_ragged(instr):
+    """Exponent-spread inputs, ragged M, N, K spanning several tiles and a
+    short last turn, S in {1, 3}: 0 ULP against the oracle."""
+    import oracle
+    A = synth.bf16_spread(41, (150, 712), -25, 25)
+    B = synth.bf16_spread(42, (200, 712), -25, 25)  # N = 200: ldc a multiple of 8
+    for S in (1, 3):
+        print_case("spread_parity", instr, S)
+        spec = {"mfma": instr, "split_k": S, "cut_unit": 64}
+        got = run_gemm(spec, A, B)
+        ref = oracle.gemm_bf16(oracle_desc(spec, instr), A, B)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
