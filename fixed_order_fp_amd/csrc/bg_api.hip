@@ -129,6 +129,21 @@ bg_status check_common_order(const bg_gemm_desc* d)
     return BG_OK;
 }
 
+// Speed only: a tile shape for the problem (measured on MI355X: the 128x128
+// direct-to-LDS tile, two workgroups per CU, leads from M = 64 up; below
+// that 64x64 register-staged tiles give the most workgroups).
+void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
+{
+    auto set = [&](int bm, int bn, int wm, int wn, int direct) {
+        p.bm = bm, p.bn = bn, p.bk = 64, p.waves_m = wm, p.waves_n = wn, p.direct = direct;
+    };
+    const bool i32 = p.mfma == BG_MFMA_F32_32X32X16_BF16;
+    if (M > 32 && N >= 128 && (M >= 128 || i32)) set(128, 128, 2, 2, i32 ? 1 : 0);
+    else if (M > 16 || i32) set(64, 64, 2, 2, 0);
+    else set(32, 32, 1, 1, 0);
+    (void)N;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,24 +323,14 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
     p.mfma = (int)d->mfma;
     p.out_bf16 = d->out_type == BG_BF16;
     const bg_gemm_schedule& s = d->sched;
+    p.group_m = s.group_m;
     if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
-        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n))
-            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves) is not compiled in");
+        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path))
+            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path) is not compiled in");
         p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
+        p.direct = s.load_path;
     } else {
-        // speed only: the largest tile that still gives the chip enough workgroups
-        const bool i32 = p.mfma == BG_MFMA_F32_32X32X16_BF16;
-        const int64_t wg128 = ((M + 127) / 128) * ((N + 127) / 128) * p.S;
-        const int64_t wg64 = ((M + 63) / 64) * ((N + 63) / 64) * p.S;
-        if (M >= 128 && N >= 128 && wg128 >= 256) {
-            p.bm = 128, p.bn = 128, p.bk = 64, p.waves_m = 2, p.waves_n = 2;
-        } else if (M > 32 && wg64 >= 128) {
-            p.bm = 64, p.bn = 64, p.bk = 64, p.waves_m = 2, p.waves_n = 2;
-        } else if (i32) {
-            p.bm = 32, p.bn = 32, p.bk = 64, p.waves_m = 1, p.waves_n = 1;
-        } else {
-            p.bm = 32, p.bn = 32, p.bk = 64, p.waves_m = 1, p.waves_n = 1;
-        }
+        choose_gemm_tile(p, M, N);
     }
     st = check_device();
     if (st != BG_OK) return st;

@@ -21,7 +21,7 @@
 
 namespace bg {
 
-namespace {
+namespace gemm_impl {
 
 constexpr int kChunk = 8;  // bf16 per 16-byte chunk
 
@@ -213,6 +213,189 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
             }
 }
 
+// 16 bytes from global memory into LDS at lds_dst + 16 * lane (the LDS
+// address is taken from the wave's first lane).  The explicit address-space
+// casts keep the host pass of a templated kernel well-formed.
+__device__ __forceinline__ void lds_copy16(const void* src, u32x4* lds_dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs in turn, so
+// consecutive ids land on different L2s; renumber them so that each XCD gets
+// one contiguous run of tiles, then walk that run GROUP_M tile-rows at a time
+// (column-major inside a group) so that neighbours share A rows and B columns.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int group_m, int& tm, int& tn)
+{
+    const int T = tiles_m * tiles_n;
+    const int q = T / 8, r = T % 8;
+    const int x = b % 8, j = b / 8;
+    const int bb = x * q + (x < r ? x : r) + j;  // a bijection on [0, T)
+    const int per_group = group_m * tiles_n;
+    const int g = bb / per_group;
+    const int first_m = g * group_m;
+    const int gsize = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in = bb - g * per_group;
+    tm = first_m + in % gsize;
+    tn = in / gsize;
+}
+
+// The same order as gemm_bf16_kernel, with the operand tiles copied from
+// global memory straight into LDS (global_load_lds_dwordx4: lane i of a wave
+// writes the 16 bytes it loads to LDS base + 16 i), so no VGPRs and no LDS
+// store instructions are spent on staging.  A chunk's LDS slot is fixed by the
+// lane that loads it; the lane picks the global chunk (row, logical k chunk)
+// that belongs in that slot under the row-XOR swizzle.  Rows past M or N read
+// a clamped row: those results are never stored.  A turn that would run past
+// the split's k_end is staged through registers with zero fill instead, so a
+// short last turn is zero-padded exactly as in the register path.
+template <int INSTR, int BM, int BN, int WM, int WN, bool OUT_BF16, bool PARTIAL>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M, int64_t N, Cuts cuts,
+    int tiles_m, int tiles_n, int group_m)
+{
+    typedef MfmaShape<INSTR> S;
+    constexpr int BK = 64, CPR = BK / kChunk;  // 8 chunks of 16 B per tile row
+    constexpr int NW = WM * WN, NT = 64 * NW;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / S::M, TN = WTN / S::N;
+    constexpr int A_CH = BM * CPR, B_CH = BN * CPR;
+    constexpr int A_PER_T = A_CH / NT, B_PER_T = B_CH / NT;
+    static_assert(A_CH % NT == 0 && B_CH % NT == 0, "tile must split evenly over the waves");
+    static_assert(WTM % S::M == 0 && WTN % S::N == 0, "wave tile must hold whole MFMA blocks");
+
+    __shared__ u32x4 lds_a[2][A_CH];
+    __shared__ u32x4 lds_b[2][B_CH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int split = blockIdx.y;
+    const int64_t k_begin = cuts.c[split];
+    const int64_t k_end = cuts.c[split + 1];
+    const int n_full = (int)((k_end - k_begin) / BK);
+    const int n_turns = (int)((k_end - k_begin + BK - 1) / BK);
+
+    // per-lane source rows and logical chunks (fixed for the whole k walk)
+    const uint16_t* a_src[A_PER_T];
+    const uint16_t* b_src[B_PER_T];
+    int a_kc[A_PER_T], b_kc[B_PER_T];
+#pragma unroll
+    for (int i = 0; i < A_PER_T; i++) {
+        const int c = i * NT + wave * 64 + lane;  // LDS slot this lane fills
+        const int row = c / CPR;
+        a_kc[i] = (c % CPR) ^ (row & 7);
+        int64_t gm = m0 + row;
+        gm = gm < M ? gm : M - 1;
+        a_src[i] = A + gm * lda + a_kc[i] * kChunk;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; i++) {
+        const int c = i * NT + wave * 64 + lane;
+        const int row = c / CPR;
+        b_kc[i] = (c % CPR) ^ (row & 7);
+        int64_t gn = n0 + row;
+        gn = gn < N ? gn : N - 1;
+        b_src[i] = B + gn * ldb + b_kc[i] * kChunk;
+    }
+
+    typename S::acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < S::ACC; e++) acc[i][j][e] = 0.0f;
+
+    auto issue = [&](int turn, int stage) {
+        const int64_t kb = k_begin + (int64_t)turn * BK;
+        if (turn < n_full) {
+#pragma unroll
+            for (int i = 0; i < A_PER_T; i++)
+                lds_copy16(a_src[i] + kb, &lds_a[stage][i * NT + wave * 64]);
+#pragma unroll
+            for (int i = 0; i < B_PER_T; i++)
+                lds_copy16(b_src[i] + kb, &lds_b[stage][i * NT + wave * 64]);
+        } else {  // the short last turn: zero-filled through registers
+#pragma unroll
+            for (int i = 0; i < A_PER_T; i++) {
+                const int c = i * NT + wave * 64 + lane;
+                const int64_t gm = m0 + c / CPR;
+                lds_a[stage][c] = load_chunk(A + (gm < M ? gm : M - 1) * lda, true, kb + a_kc[i] * kChunk, k_end);
+            }
+#pragma unroll
+            for (int i = 0; i < B_PER_T; i++) {
+                const int c = i * NT + wave * 64 + lane;
+                const int64_t gn = n0 + c / CPR;
+                lds_b[stage][c] = load_chunk(B + (gn < N ? gn : N - 1) * ldb, true, kb + b_kc[i] * kChunk, k_end);
+            }
+        }
+    };
+    auto compute = [&](int stage) {
+        const int r_in = lane % S::M;
+        const int kc_in = lane / S::M;
+#pragma unroll
+        for (int ks = 0; ks < BK / S::K; ks++) {
+            bf16x8 a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int row = wm * WTM + i * S::M + r_in;
+                a[i] = __builtin_bit_cast(bf16x8, lds_a[stage][lds_slot<BK>(row, ks * (S::K / kChunk) + kc_in)]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const int row = wn * WTN + j * S::N + r_in;
+                b[j] = __builtin_bit_cast(bf16x8, lds_b[stage][lds_slot<BK>(row, ks * (S::K / kChunk) + kc_in)]);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) acc[i][j] = mfma<INSTR>(a[i], b[j], acc[i][j]);
+        }
+    };
+
+    if (n_turns > 0) issue(0, 0);
+    for (int t = 0; t < n_turns; t++) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's copies have landed
+        __syncthreads();                      // ... and every lane's; stage (t+1)&1 is free
+        if (t + 1 < n_turns) issue(t + 1, (t + 1) & 1);
+        compute(t & 1);
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int e = 0; e < S::ACC; e++) {
+                int rm, cn;
+                if constexpr (S::M == 32) {
+                    rm = 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+                    cn = lane % 32;
+                } else {
+                    rm = 4 * (lane / 16) + e;
+                    cn = lane % 16;
+                }
+                const int64_t gm = m0 + wm * WTM + i * S::M + rm;
+                const int64_t gn = n0 + wn * WTN + j * S::N + cn;
+                if (gm < M && gn < N) {
+                    const float v = acc[i][j][e];
+                    if constexpr (PARTIAL)
+                        ws[((int64_t)split * M + gm) * N + gn] = v;
+                    else if constexpr (OUT_BF16)
+                        ((uint16_t*)C)[gm * ldc + gn] = bf16_rne(v);
+                    else
+                        ((float*)C)[gm * ldc + gn] = v;
+                }
+            }
+}
+
 // Balanced tree over v[0..n), neighbours first, an odd last element carried
 // up unchanged.  With n a compile-time constant the loops unroll and v stays
 // in registers.
@@ -270,24 +453,55 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(const float* __rest
         ((float*)C)[m * ldc + n] = r;
 }
 
-template <int INSTR, int BM, int BN, int BK, int WM, int WN>
-hipError_t launch_tile(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
-                       const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws,
-                       hipStream_t stream)
-{
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.S);
-    dim3 block(64 * WM * WN);
-    if (p.S > 1)
-        hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, true>), grid, block, 0,
-                           stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
-    else if (p.out_bf16)
-        hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, true, false>), grid, block, 0,
-                           stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
-    else
-        hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, false>), grid, block, 0,
-                           stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
-    return hipGetLastError();
-}
+// One launcher per staging path (a kernel launched from one branch of an
+// `if constexpr` does not get its host stub emitted, so the two paths are two
+// specialisations).
+template <int DIRECT>
+struct TileLauncher;
+
+template <>
+struct TileLauncher<1> {
+    template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+    static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
+    {
+        static_assert(BK == 64, "the direct path stages k tiles of 64");
+        const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+        const int group_m = p.group_m > 0 ? p.group_m : 8;
+        dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.S), block(64 * WM * WN);
+        if (p.S > 1)
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, true>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        else if (p.out_bf16)
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, true, false>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        else
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, false>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        return hipGetLastError();
+    }
+};
+
+template <>
+struct TileLauncher<0> {
+    template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+    static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
+    {
+        dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.S);
+        dim3 block(64 * WM * WN);
+        if (p.S > 1)
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, true>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+        else if (p.out_bf16)
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, true, false>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+        else
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, false>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+        return hipGetLastError();
+    }
+};
 
 template <bool OUT_BF16>
 hipError_t launch_combine(int S, int64_t M, int64_t N, const float* ws, void* C, int64_t ldc,
@@ -317,23 +531,35 @@ hipError_t launch_combine(int S, int64_t M, int64_t N, const float* ws, void* C,
     return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace gemm_impl
 
-// The tile shapes compiled in: (instruction, BM, BN, BK, waves_m, waves_n).
+using namespace gemm_impl;
+
+// The tile shapes compiled in: (instruction, BM, BN, BK, waves_m, waves_n,
+// direct-to-LDS staging).
 #define BG_GEMM_TILES(X)                                            \
-    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2)                \
-    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2)                  \
-    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 64, 1, 2)                  \
-    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 64, 1, 1)                  \
-    X(BG_MFMA_F32_16X16X32_BF16, 128, 128, 64, 2, 2)                \
-    X(BG_MFMA_F32_16X16X32_BF16, 64, 64, 64, 2, 2)                  \
-    X(BG_MFMA_F32_16X16X32_BF16, 32, 32, 64, 1, 1)                  \
-    X(BG_MFMA_F32_16X16X32_BF16, 16, 32, 64, 1, 2)
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 2, 1)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 4, 1)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 64, 2, 2, 1)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 256, 64, 2, 2, 1)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 1)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 0)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2, 0)               \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 64, 1, 2, 0)               \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 64, 1, 1, 0)               \
+    X(BG_MFMA_F32_16X16X32_BF16, 256, 256, 64, 2, 2, 1)             \
+    X(BG_MFMA_F32_16X16X32_BF16, 256, 128, 64, 2, 2, 1)             \
+    X(BG_MFMA_F32_16X16X32_BF16, 128, 128, 64, 2, 2, 0)             \
+    X(BG_MFMA_F32_16X16X32_BF16, 64, 64, 64, 2, 2, 0)               \
+    X(BG_MFMA_F32_16X16X32_BF16, 32, 32, 64, 1, 1, 0)               \
+    X(BG_MFMA_F32_16X16X32_BF16, 16, 32, 64, 1, 2, 0)
 
-bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n)
+bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct)
 {
-#define BG_HAS(I, BM_, BN_, BK_, WM_, WN_) \
-    if (mfma == I && bm == BM_ && bn == BN_ && bk == BK_ && waves_m == WM_ && waves_n == WN_) return true;
+#define BG_HAS(I, BM_, BN_, BK_, WM_, WN_, D_)                                                      \
+    if (mfma == I && bm == BM_ && bn == BN_ && bk == BK_ && waves_m == WM_ && waves_n == WN_ &&      \
+        direct == D_)                                                                                \
+        return true;
     BG_GEMM_TILES(BG_HAS)
 #undef BG_HAS
     return false;
@@ -346,11 +572,11 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, 
     (void)K;
     hipError_t err = hipErrorInvalidValue;
     bool found = false;
-#define BG_LAUNCH(I, BM_, BN_, BK_, WM_, WN_)                                                           \
+#define BG_LAUNCH(I, BM_, BN_, BK_, WM_, WN_, D_)                                                       \
     if (!found && p.mfma == I && p.bm == BM_ && p.bn == BN_ && p.bk == BK_ && p.waves_m == WM_ &&      \
-        p.waves_n == WN_) {                                                                              \
+        p.waves_n == WN_ && p.direct == D_) {                                                           \
         found = true;                                                                                    \
-        err = launch_tile<I, BM_, BN_, BK_, WM_, WN_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream);    \
+        err = TileLauncher<D_>::template run<I, BM_, BN_, BK_, WM_, WN_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream); \
     }
     BG_GEMM_TILES(BG_LAUNCH)
 #undef BG_LAUNCH

@@ -40,6 +40,8 @@ struct GemmPlan {
     bool out_bf16;   // rounding point target
     int bm, bn, bk;  // schedule
     int waves_m, waves_n;
+    int direct;      // 1: operand tiles copied global -> LDS directly
+    int group_m;     // tile rows per group of the workgroup walk
 };
 
 hipError_t launch_probe(int mfma, int64_t n_cases, const void* A, const void* B, const void* C,
@@ -50,6 +52,6 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K,
                             void* C, int64_t ldc, float* ws, hipStream_t stream);
 
 // which tile shapes the GEMM kernel is instantiated for
-bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n);
+bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct);
 
 }  // namespace bg

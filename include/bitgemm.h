@@ -91,14 +91,16 @@ typedef enum { BG_ROUND_AFTER_COMBINE_RNE = 0 } bg_rounding_point;
 typedef enum { BG_EPI_NONE = 0, BG_EPI_W8A8_POW2 = 1 } bg_epilogue;
 
 /* Speed knobs.  They are NOT part of the order: any value returns the same
- * bits ([T] 3.2.2: BLOCK_M/N/K are speed knobs; appendix E).  0 = let the
- * library choose for the shape. */
+ * bits ([T] 3.2.2: BLOCK_M/N/K are speed knobs; appendix E).  bm..waves_n all
+ * 0 = let the library choose the tile and load path for the shape; a
+ * combination that is not compiled in is BG_E_UNSUPPORTED. */
 typedef struct {
     int32_t bm, bn, bk;       /* output tile and k-tile                    */
     int32_t waves_m, waves_n; /* wave grid inside a workgroup              */
-    int32_t lds_stages;       /* LDS buffers (1 or 2)                      */
-    int32_t grid_swizzle;     /* tile-to-workgroup mapping                 */
-    int32_t combine_block;    /* threads per workgroup of the combine      */
+    int32_t load_path;        /* 0: global -> VGPR -> LDS; 1: global -> LDS */
+    int32_t group_m;          /* tile rows per group of the workgroup walk
+                                 (0 = 8)                                   */
+    int32_t combine_block;    /* reserved                                  */
 } bg_gemm_schedule;
 
 /* GEMM descriptor ([T] 3.2.2 and 4).  Every field before `sched` is an order

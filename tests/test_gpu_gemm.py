@@ -13,11 +13,18 @@ pytestmark = pytest.mark.gpu
 
 INSTRS = ["F32_32X32X16_BF16", "F32_16X16X32_BF16"]
 SCHEDULES = {
-    "F32_32X32X16_BF16": [dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2),
+    "F32_32X32X16_BF16": [dict(bm=256, bn=256, bk=64, waves_m=2, waves_n=2, load_path=1),
+                          dict(bm=256, bn=256, bk=64, waves_m=2, waves_n=4, load_path=1),
+                          dict(bm=256, bn=128, bk=64, waves_m=2, waves_n=2, load_path=1),
+                          dict(bm=128, bn=256, bk=64, waves_m=2, waves_n=2, load_path=1),
+                          dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2, load_path=1, group_m=3),
+                          dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2, load_path=0),
                           dict(bm=64, bn=64, bk=64, waves_m=2, waves_n=2),
                           dict(bm=32, bn=64, bk=64, waves_m=1, waves_n=2),
                           dict(bm=32, bn=32, bk=64, waves_m=1, waves_n=1)],
-    "F32_16X16X32_BF16": [dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2),
+    "F32_16X16X32_BF16": [dict(bm=256, bn=256, bk=64, waves_m=2, waves_n=2, load_path=1),
+                          dict(bm=256, bn=128, bk=64, waves_m=2, waves_n=2, load_path=1),
+                          dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2),
                           dict(bm=64, bn=64, bk=64, waves_m=2, waves_n=2),
                           dict(bm=32, bn=32, bk=64, waves_m=1, waves_n=1),
                           dict(bm=16, bn=32, bk=64, waves_m=1, waves_n=2)],
@@ -136,8 +143,9 @@ def test_spread_parity_ragged(instr):
     A = synth.bf16_spread(41, (150, 712), -25, 25)
     B = synth.bf16_spread(42, (200, 712), -25, 25)  # N = 200: ldc a multiple of 8
     for S in (1, 3):
-        print_case("spread_parity", instr, S)
         spec = {"mfma": instr, "split_k": S, "cut_unit": 64}
-        got = run_gemm(spec, A, B)
         ref = oracle.gemm_bf16(oracle_desc(spec, instr), A, B)
-        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+        for sched in [None] + SCHEDULES[instr]:
+            print_case("spread_parity", instr, S, sched)
+            got = run_gemm(dict(spec, schedule=sched) if sched else spec, A, B)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), sched
