@@ -350,19 +350,79 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
     return fail(BG_E_UNSUPPORTED, "W8A8 path not built yet");
 }
 
+// Validate a reduce descriptor and fill the plan; BG_OK or a refusal.
+static bg_status reduce_plan(const bg_reduce_desc* d, int64_t rows, int64_t cols, bg::ReducePlan& p,
+                             int64_t& n_blocks)
+{
+    if (!d) return fail(BG_E_INVALID, "descriptor is NULL");
+    if (d->version != 1) return fail(BG_E_INVALID, "descriptor version must be 1");
+    if (d->in_type != BG_FP32 && d->in_type != BG_BF16) return fail(BG_E_INVALID, "in_type must be fp32 or bf16");
+    if (d->acc_type != BG_FP32 || d->out_type != BG_FP32) return fail(BG_E_INVALID, "accumulation and output are fp32");
+    if (d->op < BG_RED_SUM || d->op > BG_RED_SUM_AND_SUMSQ) return fail(BG_E_INVALID, "unknown op");
+    if (d->axis != BG_AXIS_ROW && d->axis != BG_AXIS_COL) return fail(BG_E_INVALID, "unknown axis");
+    if (d->leaf_order != BG_LEAF_SEQUENTIAL_NO_SEED) return fail(BG_E_INVALID, "unknown leaf_order");
+    if (d->sq_fma != BG_SQ_FUSED && d->sq_fma != BG_SQ_UNFUSED) return fail(BG_E_INVALID, "unknown sq_fma");
+    if (d->tree != BG_TREE_BALANCED) return fail(BG_E_INVALID, "unknown tree");
+    if (d->odd_rule != BG_ODD_CARRY_LAST) return fail(BG_E_INVALID, "unknown odd_rule");
+    if (d->leaf_len != 32) return fail(BG_E_UNSUPPORTED, "only leaves of 32 elements are built");
+    if (rows < 0 || cols < 0) return fail(BG_E_INVALID, "negative size");
+    p.axis = (int)d->axis;
+    p.bf16 = d->in_type == BG_BF16;
+    p.fused = d->sq_fma == BG_SQ_FUSED;
+    if (p.axis == BG_AXIS_ROW) {
+        n_blocks = bg::reduce_row_blocks(cols);
+        if (n_blocks > 64) return fail(BG_E_UNSUPPORTED, "a row longer than 64 * 8192 elements is not built");
+    } else {
+        p.leaves_per_wg = d->sched.leaves_per_wg ? d->sched.leaves_per_wg : 8;
+        if (p.leaves_per_wg != 4 && p.leaves_per_wg != 8 && p.leaves_per_wg != 16 && p.leaves_per_wg != 32)
+            return fail(BG_E_UNSUPPORTED, "leaves_per_wg must be 4, 8, 16 or 32");
+        const int cpw = d->sched.cols_per_wg ? d->sched.cols_per_wg : 256;
+        p.cols_per_lane = cpw / 64;
+        if (cpw % 64 || (p.cols_per_lane != 4 && (p.cols_per_lane != 8 || !p.bf16)))
+            return fail(BG_E_UNSUPPORTED, "cols_per_wg must be 256 (or 512 for bf16 input)");
+        n_blocks = bg::reduce_col_blocks(rows, p.leaves_per_wg);
+        if (n_blocks > 64) return fail(BG_E_UNSUPPORTED, "too many leaf blocks: raise leaves_per_wg");
+    }
+    return BG_OK;
+}
+
 bg_status bg_reduce_workspace_bytes(const bg_reduce_desc* d, int64_t rows, int64_t cols, size_t* bytes)
 {
-    (void)d, (void)rows, (void)cols;
-    if (bytes) *bytes = 0;
-    return fail(BG_E_UNSUPPORTED, "reductions not built yet");
+    if (!bytes) return fail(BG_E_INVALID, "NULL argument");
+    bg::ReducePlan p{};
+    int64_t nb = 0;
+    bg_status st = reduce_plan(d, rows, cols, p, nb);
+    if (st != BG_OK) return st;
+    const int64_t n_out = p.axis == BG_AXIS_ROW ? rows : cols;
+    *bytes = nb > 1 ? (size_t)n_out * (size_t)nb * 2 * sizeof(float) : 0;
+    return BG_OK;
 }
 
 bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols, const void* X, int64_t ldx,
                          float* out_sum, float* out_sumsq, void* ws, size_t ws_bytes, hipStream_t stream)
 {
-    (void)d, (void)rows, (void)cols, (void)X, (void)ldx, (void)out_sum, (void)out_sumsq, (void)ws;
-    (void)ws_bytes, (void)stream;
-    return fail(BG_E_UNSUPPORTED, "reductions not built yet");
+    bg::ReducePlan p{};
+    int64_t nb = 0;
+    bg_status st = reduce_plan(d, rows, cols, p, nb);
+    if (st != BG_OK) return st;
+    if (!(d->op & BG_RED_SUM)) out_sum = nullptr;
+    if (!(d->op & BG_RED_SUMSQ)) out_sumsq = nullptr;
+    if (ldx < cols) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (rows == 0 || cols == 0) return BG_OK;
+    if (!X) return fail(BG_E_INVALID, "NULL tensor");
+    if ((d->op & BG_RED_SUM) && !out_sum) return fail(BG_E_INVALID, "op asks for the sum but out_sum is NULL");
+    if ((d->op & BG_RED_SUMSQ) && !out_sumsq) return fail(BG_E_INVALID, "op asks for sumsq but out_sumsq is NULL");
+    if (!aligned16(X) || ldx % 8) return fail(BG_E_ALIGN, "X must be 16-byte aligned with ldx a multiple of 8");
+    if (((uintptr_t)out_sum & 3u) || ((uintptr_t)out_sumsq & 3u)) return fail(BG_E_ALIGN, "outputs must be 4-byte aligned");
+    const int64_t n_out = p.axis == BG_AXIS_ROW ? rows : cols;
+    const size_t need = nb > 1 ? (size_t)n_out * (size_t)nb * 2 * sizeof(float) : 0;
+    if (need && (!ws || ws_bytes < need)) return fail(BG_E_WORKSPACE, "this shape needs a workspace");
+    if (p.axis == BG_AXIS_ROW && rows > 0x7fffffff) return fail(BG_E_UNSUPPORTED, "too many rows");
+    st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_reduce(p, rows, cols, X, ldx, out_sum, out_sumsq, (float*)ws, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
 }
 
 bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
@@ -376,9 +436,20 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
 bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, int64_t cols, const void* X,
                                int64_t ldx, float* out_sum, float* out_sumsq, hipStream_t stream)
 {
-    (void)axis, (void)in_type, (void)rows, (void)cols, (void)X, (void)ldx, (void)out_sum, (void)out_sumsq;
-    (void)stream;
-    return fail(BG_E_UNSUPPORTED, "free-order twin not built yet");
+    if (axis != BG_AXIS_ROW && axis != BG_AXIS_COL) return fail(BG_E_INVALID, "unknown axis");
+    if (in_type != BG_FP32 && in_type != BG_BF16) return fail(BG_E_INVALID, "in_type must be fp32 or bf16");
+    if (rows < 0 || cols < 0 || ldx < cols) return fail(BG_E_INVALID, "bad sizes");
+    if (rows == 0 || cols == 0) return BG_OK;
+    if (!X || !aligned16(X) || ldx % 8) return fail(BG_E_ALIGN, "X must be 16-byte aligned with ldx a multiple of 8");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    int dev = 0, n_cu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    hipError_t e = bg::launch_reduce_free((int)axis, in_type == BG_BF16, rows, cols, X, ldx, out_sum, out_sumsq,
+                                          n_cu, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
 }
 
 bg_status bg_probe_mfma(uint32_t mfma, int64_t n_cases, const void* A, const void* B, const void* C, void* D,

@@ -51,6 +51,21 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                             void* C, int64_t ldc, float* ws, hipStream_t stream);
 
+struct ReducePlan {
+    int axis;          // BG_AXIS_ROW | BG_AXIS_COL
+    bool bf16;         // input type
+    bool fused;        // q = fma(x, x, q)
+    int leaves_per_wg; // column axis: leaves one workgroup folds (4, 8, 16, 32)
+    int cols_per_lane; // column axis, bf16 input: 4 or 8
+};
+
+int64_t reduce_row_blocks(int64_t cols);
+int64_t reduce_col_blocks(int64_t rows, int lpw);
+hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const void* X, int64_t ldx,
+                         float* out_sum, float* out_sq, float* ws, hipStream_t stream);
+hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, const void* X, int64_t ldx,
+                              float* out_sum, float* out_sq, int n_cu, hipStream_t stream);
+
 // which tile shapes the GEMM kernel is instantiated for
 bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct);
 
