@@ -13,9 +13,12 @@ The same JSON line also carries:
                 stream) against the dense bf16 MFMA peak;
   cpu_baseline  the oracle timed on a bounded sample of the same outputs on
                 the host cores;
+  free_order    the free-order twin of the same GEMM (split-K by CU count,
+                fp32 atomics) and the time ratio fixed / free;
   extra         the other workloads (smaller batches, the split-K sweep, the
-                small split-K GEMM), each parity-sampled and timed the same
-                way, and the free-order twin where it is built.
+                small split-K GEMM, W8A8, the row and column reductions),
+                each parity-checked and timed the same way, with its
+                free-order twin where one exists.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -32,6 +35,7 @@ METRIC = ("order-fixed bf16 GEMM TFLOP/s (bit-exact vs oracle), % MFMA peak, "
           "cost vs free order")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0       # MI355X published dense int8 MFMA peak
 
 
 def log(*a):
@@ -130,6 +134,115 @@ def cpu_baseline(g, budget_s=12.0):
             "sample": f"{done} outputs of the M=4000 N=9728 K=2560 GEMM, {t_total:.1f} s"}
 
 
+def free_twin_us(g, args, torch, split_k=0):
+    dF = torch.empty((g.M, g.N), dtype=torch.float32, device="cuda")
+    t, _ = time_steps(lambda: g.bg.bench_gemm_bf16_free(g.dA, g.dB, dF, split_k), args.steps, args.warmup, torch)
+    return t * 1e3
+
+
+def gemm_extras(X, W, args, torch, bg, synth):
+    """Smaller batches of the batch-invariance sweep, the split-K sweep and the
+    small split-K GEMM, each parity-sampled, with the free-order twin."""
+    out = {}
+    for M in (1, 8, 64, 512):
+        g = Gemm(f"gemm_bf16 M={M}", X[:M].copy(), W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"},
+                 torch, bg)
+        p = g.parity(128)
+        t, _ = time_steps(g.run, args.steps, args.warmup, torch)
+        free = free_twin_us(g, args, torch)
+        out[f"batch_sweep_M{M}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(g.flops() / t / 1e9, 2),
+                                    "GB/s": round(g.bytes() / t / 1e6, 1), "free_us": round(free, 2),
+                                    "fixed_over_free_time": round(t * 1e3 / free, 3), "parity": p}
+        log(f"bench: M={M}: {t * 1e3:.2f} us (free {free:.2f} us)")
+    A4, W4 = synth.gemm_splitk_sweep()
+    free = None
+    for S in (1, 2, 4, 8, 16):
+        g = Gemm(f"splitk S={S}", A4, W4, {"mfma": "F32_32X32X16_BF16", "split_k": S, "out_type": "fp32"},
+                 torch, bg)
+        p = g.parity(128)
+        t, _ = time_steps(g.run, args.steps, args.warmup, torch)
+        if free is None:
+            free = free_twin_us(g, args, torch)
+        out[f"splitk_S{S}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(g.flops() / t / 1e9, 2),
+                               "GB/s": round(g.bytes() / t / 1e6, 1), "free_us": round(free, 2),
+                               "fixed_over_free_time": round(t * 1e3 / free, 3), "parity": p}
+        log(f"bench: split-K S={S}: {t * 1e3:.2f} us (free {free:.2f} us)")
+    A1, B1 = synth.gemm_small()
+    g = Gemm("small", A1, B1, {"mfma": "F32_32X32X16_BF16", "split_k": 2, "cut_rule": "EXPLICIT",
+                               "cuts": [0, 256, 512], "out_type": "fp32"}, torch, bg)
+    p = g.parity(256)
+    t, _ = time_steps(g.run, args.steps, args.warmup, torch)
+    out["small_32x64x512_S2"] = {"us": round(t * 1e3, 2), "parity": p}
+    return out
+
+
+def w8a8_extra(args, torch, bg, synth):
+    """W8A8 1024 x 6144 x 2048 with the power-of-two epilogue, checked in full
+    against the oracle (int32 and bf16 bits)."""
+    import numpy as np
+    import oracle
+    a_q, w_q, a_s, w_s = synth.w8a8_input()
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    d = bg.gemm_desc(dict(mfma="I32_32X32X32_I8", a_type="int8", b_type="int8", acc_type="int32",
+                          out_type="bf16", epilogue="W8A8_POW2"))
+    dA, dW = torch.from_numpy(a_q).cuda(), torch.from_numpy(w_q).cuda()
+    sa, sw = torch.from_numpy(a_s).cuda(), torch.from_numpy(w_s).cuda()
+    dY = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dacc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY, dacc)
+    torch.cuda.synchronize()
+    Yo, acco = oracle.w8a8_pow2(a_q, w_q, a_s, w_s)
+    par = {"checked": int(M * N), "acc_mismatches": int(np.sum(dacc.cpu().numpy() != acco)),
+           "y_mismatches": int(np.sum(dY.cpu().numpy().view(np.uint16) != Yo))}
+    t, _ = time_steps(lambda: bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY), args.steps, args.warmup, torch)
+    ops = 2.0 * M * N * K
+    byts = M * K + N * K + 4 * (M + N) + 2 * M * N
+    log(f"bench: W8A8: {t * 1e3:.2f} us")
+    return {"w8a8_1024x6144x2048": {"us": round(t * 1e3, 2), "TOP/s": round(ops / t / 1e9, 2),
+                                    "frac_int8_peak": round(ops / t / 1e9 / PEAK_INT8_TOPS, 4),
+                                    "GB/s": round(byts / t / 1e6, 1), "parity": par}}
+
+
+def reduce_extras(args, torch, bg, synth):
+    """The row reduction (fp32 16384 x 8192, sum and sum of squares from one
+    read) and the column sum (bf16 8192 x 4096), against HBM bandwidth, with
+    their free-order twins; sampled rows / columns checked against the oracle."""
+    import numpy as np
+    import oracle
+    out = {}
+    cases = [("row", "fp32", synth.reduce_rows_input(), "sum_and_sumsq", 4),
+             ("col", "bf16", synth.reduce_cols_input(), "sum", 2)]
+    for axis, in_type, Xh, op, elt in cases:
+        rows, cols = Xh.shape
+        d = bg.reduce_desc(dict(in_type=in_type, op=op, axis=axis))
+        dX = torch.from_numpy(Xh.view(np.int16) if in_type == "bf16" else Xh).cuda()
+        n_out = rows if axis == "row" else cols
+        s = torch.empty(n_out, dtype=torch.float32, device="cuda")
+        q = torch.empty(n_out, dtype=torch.float32, device="cuda") if op == "sum_and_sumsq" else None
+        nws = bg.reduce_workspace_bytes(d, rows, cols)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        bg.reduce_tree(d, dX, s, q, ws)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(7)
+        idx = np.sort(rng.choice(n_out, 64, replace=False))
+        sub = Xh[idx] if axis == "row" else Xh[:, idx]
+        rs, rq = oracle.reduce(sub, axis, in_type=in_type)
+        bad = int(np.sum(s.cpu().numpy()[idx].view(np.uint32) != rs.view(np.uint32)))
+        if q is not None:
+            bad += int(np.sum(q.cpu().numpy()[idx].view(np.uint32) != rq.view(np.uint32)))
+        t, _ = time_steps(lambda: bg.reduce_tree(d, dX, s, q, ws), args.steps, args.warmup, torch)
+        tf, _ = time_steps(lambda: bg.bench_reduce_free(axis, in_type, dX, s, q), args.steps, args.warmup, torch)
+        byts = rows * cols * elt + 4 * n_out * (2 if q is not None else 1)
+        gbs = byts / t / 1e6
+        out[f"reduce_{axis}_{in_type}_{rows}x{cols}"] = {
+            "us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "free_us": round(tf * 1e3, 2), "fixed_over_free_time": round(t / tf, 3),
+            "parity": {"sampled_outputs": 64, "mismatches": bad}}
+        log(f"bench: reduce {axis}: {t * 1e3:.2f} us, {gbs:.0f} GB/s (free {tf * 1e3:.2f} us)")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,31 +296,19 @@ def main():
     }
     del wall
 
+    # the free-order twin of the headline (fp32 out; split-K by CU count)
+    dF = torch.empty((head.M, head.N), dtype=torch.float32, device="cuda")
+    ms_free, _ = time_steps(lambda: bg.bench_gemm_bf16_free(head.dA, head.dB, dF), args.steps, args.warmup, torch)
+    line["free_order"] = {"ms": round(ms_free, 5), "TFLOP/s": round(head.flops() / (ms_free * 1e-3) / 1e12, 3),
+                          "fixed_over_free_time": round(ms / ms_free, 4),
+                          "note": "free twin writes fp32 (4 B/output) where the fixed path writes bf16"}
+    log(f"bench: free-order twin {ms_free:.4f} ms")
+
     extra = {}
     if not args.no_extra:
-        for M in (1, 8, 64, 512):
-            g = Gemm(f"gemm_bf16 M={M}", X[:M].copy(), W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"},
-                     torch, bg)
-            p = g.parity(128)
-            t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-            extra[f"batch_sweep_M{M}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(g.flops() / t / 1e9, 2),
-                                          "GB/s": round(g.bytes() / t / 1e6, 1), "parity": p}
-            log(f"bench: M={M}: {t * 1e3:.2f} us")
-        A4, W4 = synth.gemm_splitk_sweep()
-        for S in (1, 2, 4, 8, 16):
-            g = Gemm(f"splitk S={S}", A4, W4, {"mfma": "F32_32X32X16_BF16", "split_k": S, "out_type": "fp32"},
-                     torch, bg)
-            p = g.parity(128)
-            t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-            extra[f"splitk_S{S}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(g.flops() / t / 1e9, 2),
-                                     "GB/s": round(g.bytes() / t / 1e6, 1), "parity": p}
-            log(f"bench: split-K S={S}: {t * 1e3:.2f} us")
-        A1, B1 = synth.gemm_small()
-        g = Gemm("small", A1, B1, {"mfma": "F32_32X32X16_BF16", "split_k": 2, "cut_rule": "EXPLICIT",
-                                   "cuts": [0, 256, 512], "out_type": "fp32"}, torch, bg)
-        p = g.parity(256)
-        t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-        extra["small_32x64x512_S2"] = {"us": round(t * 1e3, 2), "parity": p}
+        extra.update(gemm_extras(X, W, args, torch, bg, synth))
+        extra.update(w8a8_extra(args, torch, bg, synth))
+        extra.update(reduce_extras(args, torch, bg, synth))
     if extra:
         line["extra"] = extra
 

@@ -345,9 +345,42 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
                             const float* w_scale, void* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
                             hipStream_t stream)
 {
-    (void)d, (void)M, (void)N, (void)K, (void)A, (void)lda, (void)W, (void)ldw, (void)a_scale;
-    (void)w_scale, (void)Y, (void)ldy, (void)acc_out, (void)ld_acc, (void)stream;
-    return fail(BG_E_UNSUPPORTED, "W8A8 path not built yet");
+    bg_status st = check_common_order(d);
+    if (st != BG_OK) return st;
+    if (d->a_type != BG_INT8 || d->b_type != BG_INT8) return fail(BG_E_INVALID, "W8A8 takes int8 operands");
+    if (d->acc_type != BG_INT32) return fail(BG_E_INVALID, "W8A8 accumulates in int32");
+    if (d->out_type != BG_BF16) return fail(BG_E_INVALID, "W8A8 writes bf16");
+    if (d->mfma != BG_MFMA_I32_32X32X32_I8 && d->mfma != BG_MFMA_I32_16X16X64_I8)
+        return fail(BG_E_INVALID, "mfma must be an int8 instruction");
+    if (d->epilogue != BG_EPI_W8A8_POW2) return fail(BG_E_INVALID, "epilogue must be W8A8_POW2");
+    if (d->split_k != 1) return fail(BG_E_UNSUPPORTED, "W8A8 is built with split_k = 1");
+    if (M < 0 || N < 0 || K < 1) return fail(BG_E_INVALID, "bad sizes");
+    if (K > 131071) return fail(BG_E_UNSUPPORTED, "K > 131071 could leave the exact int32 range");
+    if (lda < K || ldw < K || ldy < N || (acc_out && ld_acc < N))
+        return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    bg::W8A8Plan p{};
+    p.mfma = (int)d->mfma;
+    const bg_gemm_schedule& s = d->sched;
+    p.group_m = s.group_m;
+    if (s.bm || s.bn || s.waves_m || s.waves_n) {
+        if (!bg::w8a8_has_tile(p.mfma, s.bm, s.bn, s.waves_m, s.waves_n))
+            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, waves) is not compiled in for W8A8");
+        p.bm = s.bm, p.bn = s.bn, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
+    } else {
+        const bool big = M >= 128 && N >= 128 && ((M + 127) / 128) * ((N + 127) / 128) >= 128;
+        p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
+    }
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !W || !a_scale || !w_scale || !Y) return fail(BG_E_INVALID, "NULL tensor");
+    if (!aligned16(A) || !aligned16(W) || lda % 16 || ldw % 16 || !aligned16(Y) || ldy % 8 ||
+        ((uintptr_t)a_scale & 3u) || ((uintptr_t)w_scale & 3u) || (acc_out && (!aligned16(acc_out) || ld_acc % 4)))
+        return fail(BG_E_ALIGN, "pointers must be aligned and leading dimensions multiples of 16 (int8) / 8 / 4");
+    st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_w8a8(p, M, N, K, A, lda, W, ldw, a_scale, w_scale, (uint16_t*)Y, ldy, acc_out,
+                                   ld_acc, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
 }
 
 // Validate a reduce descriptor and fill the plan; BG_OK or a refusal.
@@ -428,9 +461,41 @@ bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols, co
 bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                                   int64_t ldb, float* C, int64_t ldc, int32_t split_k, hipStream_t stream)
 {
-    (void)M, (void)N, (void)K, (void)A, (void)lda, (void)B, (void)ldb, (void)C, (void)ldc, (void)split_k;
-    (void)stream;
-    return fail(BG_E_UNSUPPORTED, "free-order twin not built yet");
+    if (M < 0 || N < 0 || K < 1) return fail(BG_E_INVALID, "bad sizes");
+    if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (split_k > BG_MAX_SPLIT) return fail(BG_E_INVALID, "split_k must be at most 64");
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 8 || ldb % 8 || ldc % 8)
+        return fail(BG_E_ALIGN, "pointers must be 16-byte aligned and leading dimensions multiples of 8");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    bg::GemmPlan p{};
+    p.mfma = BG_MFMA_F32_32X32X16_BF16;
+    p.out_bf16 = false;
+    choose_gemm_tile(p, M, N);
+    int S = split_k;
+    if (S <= 0) {  // enough workgroups for two per CU, each split at least 256 deep
+        int dev = 0, n_cu = 256;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+        S = 1;
+        while (S < BG_MAX_SPLIT && tiles * S < 2 * n_cu && K / (2 * S) >= 256) S *= 2;
+    }
+    const int64_t span = (K / (64 * (int64_t)S)) * 64;
+    if (S > 1 && span == 0) return fail(BG_E_INVALID, "K too small for that many splits");
+    p.S = S;
+    for (int s = 0; s < S; s++) p.cuts.c[s] = s * span;
+    p.cuts.c[S] = K;
+    p.atomic = S > 1;
+    hipError_t e = hipSuccess;
+    if (p.atomic) e = bg::launch_zero_rows(C, M, N, ldc, stream);
+    if (e == hipSuccess)
+        e = bg::launch_gemm_bf16(p, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, nullptr,
+                                 stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
 }
 
 bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, int64_t cols, const void* X,

@@ -76,7 +76,7 @@ __device__ __forceinline__ int lds_slot(int row, int kc)
     return row * CPR + (kc ^ (row & MASK));
 }
 
-template <int INSTR, int BM, int BN, int BK, int WM, int WN, bool OUT_BF16, bool PARTIAL>
+template <int INSTR, int BM, int BN, int BK, int WM, int WN, bool OUT_BF16, int PARTIAL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M, int64_t N, Cuts cuts)
@@ -203,8 +203,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
                 const int64_t gn = n0 + wn * WTN + j * S::N + cn;
                 if (gm < M && gn < N) {
                     const float v = acc[i][j][e];
-                    if constexpr (PARTIAL)
+                    if constexpr (PARTIAL == 1)
                         ws[((int64_t)split * M + gm) * N + gn] = v;
+                    else if constexpr (PARTIAL == 2)  // free-order twin only
+                        unsafeAtomicAdd(&((float*)C)[gm * ldc + gn], v);
                     else if constexpr (OUT_BF16)
                         ((uint16_t*)C)[gm * ldc + gn] = bf16_rne(v);
                     else
@@ -249,7 +251,7 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int gro
 // a clamped row: those results are never stored.  A turn that would run past
 // the split's k_end is staged through registers with zero fill instead, so a
 // short last turn is zero-padded exactly as in the register path.
-template <int INSTR, int BM, int BN, int WM, int WN, bool OUT_BF16, bool PARTIAL>
+template <int INSTR, int BM, int BN, int WM, int WN, bool OUT_BF16, int PARTIAL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M, int64_t N, Cuts cuts,
@@ -386,8 +388,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
                 const int64_t gn = n0 + wn * WTN + j * S::N + cn;
                 if (gm < M && gn < N) {
                     const float v = acc[i][j][e];
-                    if constexpr (PARTIAL)
+                    if constexpr (PARTIAL == 1)
                         ws[((int64_t)split * M + gm) * N + gn] = v;
+                    else if constexpr (PARTIAL == 2)  // free-order twin only
+                        unsafeAtomicAdd(&((float*)C)[gm * ldc + gn], v);
                     else if constexpr (OUT_BF16)
                         ((uint16_t*)C)[gm * ldc + gn] = bf16_rne(v);
                     else
@@ -469,14 +473,17 @@ struct TileLauncher<1> {
         const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
         const int group_m = p.group_m > 0 ? p.group_m : 8;
         dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.S), block(64 * WM * WN);
-        if (p.S > 1)
-            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, true>), grid, block, 0,
+        if (p.atomic)
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, 2>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        else if (p.S > 1)
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, 1>), grid, block, 0,
                                stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
         else if (p.out_bf16)
-            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, true, false>), grid, block, 0,
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, true, 0>), grid, block, 0,
                                stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
         else
-            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, false>), grid, block, 0,
+            hipLaunchKernelGGL((gemm_bf16_direct_kernel<INSTR, BM, BN, WM, WN, false, 0>), grid, block, 0,
                                stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
         return hipGetLastError();
     }
@@ -490,14 +497,17 @@ struct TileLauncher<0> {
     {
         dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.S);
         dim3 block(64 * WM * WN);
-        if (p.S > 1)
-            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, true>), grid, block, 0,
+        if (p.atomic)
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, 2>), grid, block, 0,
+                               stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
+        else if (p.S > 1)
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, 1>), grid, block, 0,
                                stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
         else if (p.out_bf16)
-            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, true, false>), grid, block, 0,
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, true, 0>), grid, block, 0,
                                stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
         else
-            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, false>), grid, block, 0,
+            hipLaunchKernelGGL((gemm_bf16_kernel<INSTR, BM, BN, BK, WM, WN, false, 0>), grid, block, 0,
                                stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts);
         return hipGetLastError();
     }
@@ -531,9 +541,27 @@ hipError_t launch_combine(int S, int64_t M, int64_t N, const float* ws, void* C,
     return hipGetLastError();
 }
 
+// C[m][0..N) = 0 for every row, with the row stride ldc (a kernel rather
+// than a memset so that the pitch is honoured).
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ C, int64_t M, int64_t N, int64_t ldc)
+{
+    const int64_t total = M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256)
+        C[(i / N) * ldc + i % N] = 0.0f;
+}
+
 }  // namespace gemm_impl
 
 using namespace gemm_impl;
+
+hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream)
+{
+    const int64_t total = M * N;
+    int64_t blocks = (total + 255) / 256;
+    blocks = blocks < 4096 ? blocks : 4096;
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, M, N, ldc);
+    return hipGetLastError();
+}
 
 // The tile shapes compiled in: (instruction, BM, BN, BK, waves_m, waves_n,
 // direct-to-LDS staging).
@@ -581,7 +609,7 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, 
     BG_GEMM_TILES(BG_LAUNCH)
 #undef BG_LAUNCH
     if (!found || err != hipSuccess) return found ? err : hipErrorInvalidValue;
-    if (p.S > 1) {
+    if (p.S > 1 && !p.atomic) {
         if (p.out_bf16) return launch_combine<true>(p.S, M, N, ws, C, ldc, stream);
         return launch_combine<false>(p.S, M, N, ws, C, ldc, stream);
     }

@@ -42,6 +42,7 @@ struct GemmPlan {
     int waves_m, waves_n;
     int direct;      // 1: operand tiles copied global -> LDS directly
     int group_m;     // tile rows per group of the workgroup walk
+    bool atomic;     // free-order twin: splits added into a zeroed fp32 C with atomics
 };
 
 hipError_t launch_probe(int mfma, int64_t n_cases, const void* A, const void* B, const void* C,
@@ -50,6 +51,16 @@ hipError_t launch_probe(int mfma, int64_t n_cases, const void* A, const void* B,
 hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                             void* C, int64_t ldc, float* ws, hipStream_t stream);
+
+struct W8A8Plan {
+    int mfma;  // BG_MFMA_I32_32X32X32_I8 | BG_MFMA_I32_16X16X64_I8
+    int bm, bn, waves_m, waves_n, group_m;
+};
+
+bool w8a8_has_tile(int mfma, int bm, int bn, int waves_m, int waves_n);
+hipError_t launch_w8a8(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                       const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
+                       int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream);
 
 struct ReducePlan {
     int axis;          // BG_AXIS_ROW | BG_AXIS_COL
@@ -67,6 +78,7 @@ hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, c
                               float* out_sum, float* out_sq, int n_cu, hipStream_t stream);
 
 // which tile shapes the GEMM kernel is instantiated for
+hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
 bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct);
 
 }  // namespace bg

@@ -98,3 +98,31 @@ def test_refusals_before_any_launch(bg):
     assert _call_gemm(bg, bg.gemm_desc({}), lda=513) == 4     # BG_E_ALIGN
     assert _call_gemm(bg, bg.gemm_desc({}), ptr=0x1004) == 4
     assert _call_gemm(bg, bg.gemm_desc({}), M=0) == 0          # nothing to do
+
+
+def _call_w8a8(bg, d, M=64, N=64, K=256, lda=256, ldw=256, ldy=64, ptr=0x10000, acc=0):
+    return bg.lib().bg_gemm_w8a8_pow2(C.byref(d), M, N, K, ptr, lda, ptr, ldw, ptr, ptr, ptr, ldy,
+                                      acc or None, 64, None)
+
+
+def test_w8a8_refusals_before_any_launch(bg):
+    base = dict(mfma="I32_32X32X32_I8", a_type="int8", b_type="int8", acc_type="int32", out_type="bf16",
+                epilogue="W8A8_POW2")
+    cases = [
+        (dict(base, mfma="F32_32X32X16_BF16"), {}, 1),
+        (dict(base, epilogue="NONE"), {}, 1),
+        (dict(base, acc_type="fp32"), {}, 1),
+        (dict(base, a_type="bf16"), {}, 1),
+        (dict(base, split_k=2), {}, 2),
+        (dict(base, schedule=dict(bm=96, bn=96, waves_m=2, waves_n=2)), {}, 2),
+        (base, dict(K=131072, lda=131072, ldw=131072), 2),   # beyond the exact int32 range
+        (base, dict(K=0), 1),
+        (base, dict(lda=100), 1),                            # lda < K
+        (base, dict(lda=264), 4),                            # not a multiple of 16
+        (base, dict(ldy=68), 4),                             # not a multiple of 8
+        (base, dict(ptr=0x10008), 4),
+        (base, dict(M=0), 0),
+    ]
+    for spec, args, want in cases:
+        st = _call_w8a8(bg, bg.gemm_desc(spec), **args)
+        assert st == want, (spec, args, st, bg.lib().bg_last_error())

@@ -149,3 +149,30 @@ def test_spread_parity_ragged(instr):
             print_case("spread_parity", instr, S, sched)
             got = run_gemm(dict(spec, schedule=sched) if sched else spec, A, B)
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), sched
+
+
+# ---------------------------------------------------------------------------
+# the free-order twin (bench only): no bitwise contract, but it must compute
+# the same product
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,split_k", [(1, 0), (8, 0), (64, 0), (200, 0), (64, 1), (64, 4)])
+def test_free_twin_computes_the_product(M, split_k):
+    import torch
+    import fixed_order_fp_amd as bg
+    X, W = synth.gemm_batch_sweep(M=M)
+    W = W[:1024]
+    N, K = W.shape
+    print_case("free twin", M, N, K, split_k)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    bg.bench_gemm_bf16_free(to_dev_u16(X), to_dev_u16(W), dC, split_k)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy().astype(np.float64)
+    a = synth.bf16_bits_to_f32(X).astype(np.float64)
+    b = synth.bf16_bits_to_f32(W).astype(np.float64)
+    exact = a @ b.T
+    scale = np.abs(a) @ np.abs(b).T
+    # fp32 accumulation over K terms plus at most 64 split partials
+    assert np.all(np.abs(got - exact) <= (K / 8 + 64) * 2.0 ** -23 * scale + 1e-30)
+    if split_k == 1:
+        fixed = run_gemm({"mfma": "F32_32X32X16_BF16"}, X, W, out="fp32")
+        assert np.array_equal(fixed.view(np.uint32), dC.cpu().numpy().view(np.uint32))
