@@ -13,13 +13,16 @@
 // on the number of compute units, and nothing uses atomics.
 //
 // Row axis: a workgroup of 4 waves owns 256 leaves (8192 elements) of one
-// row.  Each wave copies its 64 leaves with coalesced global_load_lds loads
-// (16 B per lane, consecutive lanes on consecutive addresses) into LDS; each
-// lane then reads its own leaf back, rotating its chunk order by its lane
-// index so that the 16-byte reads of a wave spread over the banks.
-// Column axis: lanes map to adjacent columns (coalesced rows), each lane
-// folds its columns' leaves row by row; a workgroup covers an aligned run of
-// leaves with its waves, combined through LDS.
+// row; each lane loads its own leaf (128 B of fp32 or 64 B of bf16) with
+// 16-byte vector loads -- consecutive lanes read consecutive 128 B lines, so a
+// wave's loads cover whole lines with nothing to stage or transpose -- and
+// folds it in registers.  The 64 leaves of a wave are combined with DPP
+// row shifts (offsets 1, 2, 4, 8, the right node added to the left one in
+// its own lane) and the four row roots read back as (r0 + r1) + (r2 + r3).
+// Column axis: a lane covers 16 adjacent bytes of a row (8 bf16 or 4 fp32
+// columns), a wave folds one leaf (32 rows) at a time with all of the leaf's
+// row loads in flight, and the waves of a workgroup hold consecutive leaves,
+// combined through LDS.
 #include <type_traits>
 
 #include "bg_internal.h"
@@ -29,11 +32,6 @@ namespace bg {
 namespace reduce_impl {
 
 constexpr int kLeaf = 32;
-
-__device__ __forceinline__ void lds_copy16(const void* src, u32x4* lds_dst)
-{
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
-}
 
 // The count-up tree over one wave's 64 nodes (lane l holds node l of this
 // level run); n_valid = how many of the 64 exist.  Lane 0 ends with the root.
@@ -47,16 +45,84 @@ __device__ __forceinline__ float wave_tree(float v, int lane, int n_valid)
     return v;
 }
 
-// Balanced tree over up to 8 workgroup-level nodes held in LDS (node i
-// covering 2^level_base leaves each), n_valid of them present.
-__device__ __forceinline__ float small_tree(float* v, int n)
+// The same count-up tree for a wave whose 64 nodes all exist, with DPP row
+// shifts: after the step of offset d, lane l with l = -1 mod 2d holds the node
+// covering lanes (l - 2d, l], computed as left + right.  Offsets 16 and 32
+// cross DPP rows; they are taken from the four row roots (lanes 15, 31, 47,
+// 63) read into scalars.  Every lane returns the root.
+__device__ __forceinline__ float wave_tree_full(float v)
 {
-    while (n > 1) {
-        int w = 0;
-        for (int i = 0; i + 1 < n; i += 2) v[w++] = v[i] + v[i + 1];
-        if (n & 1) v[w++] = v[n - 1];
-        n = w;
+    const int lane = threadIdx.x & 63;
+    float o;
+    o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));  // row_shr:1
+    if ((lane & 1) == 1) v = o + v;
+    o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));  // row_shr:2
+    if ((lane & 3) == 3) v = o + v;
+    o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));  // row_shr:4
+    if ((lane & 7) == 7) v = o + v;
+    o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));  // row_shr:8
+    if ((lane & 15) == 15) v = o + v;
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// element i of 8 bf16 packed in a u32x4 (little endian: even elements in the
+// low halves)
+__device__ __forceinline__ float bf16_lane(const u32x4& v, int i)
+{
+    const uint32_t w = v[i / 2];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+
+template <bool FUSED>
+__device__ __forceinline__ void fold_step(float x, float& s, float& q)
+{
+    s = s + x;
+    if constexpr (FUSED) q = __builtin_fmaf(x, x, q);
+    else {
+        const float xx = x * x;
+        q = q + xx;
     }
+}
+
+// Fold one whole leaf (32 elements at p, 16-byte aligned) in index order.
+template <typename T, bool FUSED>
+__device__ __forceinline__ void fold_leaf_vec(const T* p, float& s, float& q)
+{
+    if constexpr (std::is_same<T, float>::value) {
+        u32x4 c[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) c[i] = *(const u32x4*)(p + 4 * i);
+        s = __uint_as_float(c[0][0]);
+        q = s * s;
+#pragma unroll
+        for (int i = 1; i < kLeaf; i++) fold_step<FUSED>(__uint_as_float(c[i / 4][i % 4]), s, q);
+    } else {
+        u32x4 c[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) c[i] = *(const u32x4*)(p + 8 * i);
+        s = bf16_lane(c[0], 0);
+        q = s * s;
+#pragma unroll
+        for (int i = 1; i < kLeaf; i++) fold_step<FUSED>(bf16_lane(c[i / 8], i % 8), s, q);
+    }
+}
+
+// Balanced tree over v[0..n), n <= N, in place: at stride d the node at i
+// (a multiple of 2d) absorbs its right neighbour i + d when that node exists
+// (i + d < n), which is the neighbours-first pairing with an odd last node
+// carried up unchanged.  N is a compile-time bound so v stays in registers.
+template <int N>
+__device__ __forceinline__ float tree_upto(float* v, int n)
+{
+#pragma unroll
+    for (int d = 1; d < N; d <<= 1)
+#pragma unroll
+        for (int i = 0; i + d < N; i += 2 * d)
+            if (i + d < n) v[i] = v[i] + v[i + d];
     return v[0];
 }
 
@@ -84,15 +150,13 @@ __device__ __forceinline__ void fold_leaf(const float* x, int n, float& s, float
 }
 
 // ---- row axis ---------------------------------------------------------------
-// One workgroup: row `row`, leaf block `blk` (256 leaves).  fp32 input with a
-// full block on the fast path (direct copies to LDS); anything else (bf16, a
-// short block, an unaligned row) folds straight from global memory.
+// One workgroup: row `row`, leaf block `blk` (256 leaves).  A full block takes
+// the vector path; a short block folds element by element.
 template <typename T, bool FUSED>
 __global__ __launch_bounds__(256) void reduce_row_kernel(const T* __restrict__ X, int64_t ldx, int64_t cols,
                                                          float* __restrict__ out_sum, float* __restrict__ out_sq,
                                                          float* __restrict__ ws, int n_blocks)
 {
-    __shared__ u32x4 stage[4 * 64 * 8];  // 4 waves x 64 leaves x 128 B (fp32)
     __shared__ float roots[2][4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -105,37 +169,26 @@ __global__ __launch_bounds__(256) void reduce_row_kernel(const T* __restrict__ X
     const int my_leaf = wave * 64 + lane;  // within the block
 
     float s = 0.0f, q = 0.0f;
-    const bool full = std::is_same<T, float>::value && (leaf0 + 256) * kLeaf <= cols;
+    // the whole block present and every leaf 16-byte aligned (X 16-byte
+    // aligned, ldx a multiple of 8, leaves of 32 elements)
+    const bool full = (leaf0 + 256) * kLeaf <= cols;
     if (full) {
-        // coalesced copy of this wave's 64 leaves (8 KB) into LDS
-        const float* src = (const float*)xr + (leaf0 + wave * 64) * kLeaf;
-#pragma unroll
-        for (int c = 0; c < 8; c++) lds_copy16(src + (c * 64 + lane) * 4, &stage[(wave * 8 + c) * 64]);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float x[kLeaf];
-        const u32x4* mine = &stage[(wave * 64 + lane) * 8];
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-            const int cc = (c + lane) & 7;  // rotated chunk order: spreads the banks
-            const u32x4 v = mine[cc];
-#pragma unroll
-            for (int j = 0; j < 4; j++) x[cc * 4 + j] = __uint_as_float(v[j]);
+        fold_leaf_vec<T, FUSED>(xr + (leaf0 + my_leaf) * kLeaf, s, q);
+        s = wave_tree_full(s);
+        q = wave_tree_full(q);
+    } else {
+        if (my_leaf < n_valid) {
+            const int64_t e0 = (leaf0 + my_leaf) * kLeaf;
+            const int n = (int)((cols - e0) < kLeaf ? (cols - e0) : kLeaf);
+            float x[kLeaf];
+            for (int i = 0; i < n; i++) x[i] = load_elem<T>(xr + e0 + i);
+            fold_leaf<FUSED>(x, n, s, q);
         }
-        fold_leaf<FUSED>(x, kLeaf, s, q);
-    } else if (my_leaf < n_valid) {
-        const int64_t e0 = (leaf0 + my_leaf) * kLeaf;
-        const int n = (int)((cols - e0) < kLeaf ? (cols - e0) : kLeaf);
-        float x[kLeaf];
-        for (int i = 0; i < n; i++) x[i] = load_elem<T>(xr + e0 + i);
-        fold_leaf<FUSED>(x, n, s, q);
+        const int wave_valid = n_valid - wave * 64;
+        s = wave_tree(s, lane, wave_valid);
+        q = wave_tree(q, lane, wave_valid);
     }
-
-    // wave level: this wave's nodes are leaves [64 wave, 64 wave + 64)
-    const int wave_valid = n_valid - wave * 64;
-    s = wave_tree(s, lane, wave_valid);
-    q = wave_tree(q, lane, wave_valid);
+    // this wave's root (leaves [64 wave, 64 wave + 64)) is in lane 0
     if (lane == 0) {
         roots[0][wave] = s;
         roots[1][wave] = q;
@@ -144,8 +197,9 @@ __global__ __launch_bounds__(256) void reduce_row_kernel(const T* __restrict__ X
     if (threadIdx.x == 0) {
         const int n_waves = (n_valid + 63) / 64;
         float vs[4], vq[4];
-        for (int w = 0; w < n_waves; w++) vs[w] = roots[0][w], vq[w] = roots[1][w];
-        const float rs = small_tree(vs, n_waves), rq = small_tree(vq, n_waves);
+#pragma unroll
+        for (int w = 0; w < 4; w++) vs[w] = roots[0][w], vq[w] = roots[1][w];
+        const float rs = tree_upto<4>(vs, n_waves), rq = tree_upto<4>(vq, n_waves);
         if (n_blocks == 1) {
             if (out_sum) out_sum[row] = rs;
             if (out_sq) out_sq[row] = rq;
@@ -156,34 +210,76 @@ __global__ __launch_bounds__(256) void reduce_row_kernel(const T* __restrict__ X
     }
 }
 
-// Upper tree levels over the block roots of one output.
+// Upper tree levels over the block roots of one output (n_blocks <= NB).
+template <int NB>
 __global__ __launch_bounds__(256) void reduce_blocks_kernel(const float* __restrict__ ws, int64_t n_out,
                                                             int n_blocks, int64_t stride_out, int64_t stride_blk,
                                                             float* __restrict__ out_sum, float* __restrict__ out_sq)
 {
     const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= n_out) return;
-    float vs[64], vq[64];  // n_blocks <= 64 (checked by the host)
-    for (int b = 0; b < n_blocks; b++) {
-        vs[b] = ws[(o * stride_out + b * stride_blk) * 2];
-        vq[b] = ws[(o * stride_out + b * stride_blk) * 2 + 1];
+    float vs[NB], vq[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        vs[b] = b < n_blocks ? ws[(o * stride_out + b * stride_blk) * 2] : 0.0f;
+        vq[b] = b < n_blocks ? ws[(o * stride_out + b * stride_blk) * 2 + 1] : 0.0f;
     }
-    const float rs = small_tree(vs, n_blocks), rq = small_tree(vq, n_blocks);
+    const float rs = tree_upto<NB>(vs, n_blocks), rq = tree_upto<NB>(vq, n_blocks);
     if (out_sum) out_sum[o] = rs;
     if (out_sq) out_sq[o] = rq;
 }
 
+hipError_t launch_blocks(const float* ws, int64_t n_out, int nb, int64_t stride_out, int64_t stride_blk,
+                         float* out_sum, float* out_sq, hipStream_t stream)
+{
+    dim3 grid((unsigned)((n_out + 255) / 256)), block(256);
+    if (nb <= 4)
+        hipLaunchKernelGGL(reduce_blocks_kernel<4>, grid, block, 0, stream, ws, n_out, nb, stride_out, stride_blk,
+                           out_sum, out_sq);
+    else if (nb <= 16)
+        hipLaunchKernelGGL(reduce_blocks_kernel<16>, grid, block, 0, stream, ws, n_out, nb, stride_out, stride_blk,
+                           out_sum, out_sq);
+    else
+        hipLaunchKernelGGL(reduce_blocks_kernel<64>, grid, block, 0, stream, ws, n_out, nb, stride_out, stride_blk,
+                           out_sum, out_sq);
+    return hipGetLastError();
+}
+
 // ---- column axis ------------------------------------------------------------
-// A workgroup covers CPL * 64 adjacent columns and LPW leaves (LPW * 32 rows)
-// starting at leaf block `blk`; wave w folds leaves [w LPW/4, (w+1) LPW/4)
-// of that run, one after the other, pairing them as they complete.
-template <typename T, int CPL, int LPW, bool FUSED>
+// A workgroup of 4 waves covers 64 * CPL adjacent columns (CPL * sizeof(T) =
+// 16 or 8 bytes per lane) and 4 * LPWAVE consecutive leaves starting at leaf
+// block `blk`; wave w folds leaves [w LPWAVE, (w+1) LPWAVE) of that run one
+// after the other and pairs them into its node; the four wave nodes are then
+// paired through LDS.
+template <typename T, int CPL>
+__device__ __forceinline__ void load_row_vec(const T* p, float* x)
+{
+    if constexpr (std::is_same<T, float>::value) {
+        static_assert(CPL == 4, "fp32 rows are read 16 bytes per lane");
+        const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+        for (int c = 0; c < 4; c++) x[c] = __uint_as_float(v[c]);
+    } else if constexpr (CPL == 8) {
+        const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+        for (int c = 0; c < 8; c++) x[c] = bf16_lane(v, c);
+    } else {
+        static_assert(CPL == 4, "bf16 rows are read 16 or 8 bytes per lane");
+        const uint2 v = *(const uint2*)p;
+        x[0] = __uint_as_float(v.x << 16);
+        x[1] = __uint_as_float(v.x & 0xffff0000u);
+        x[2] = __uint_as_float(v.y << 16);
+        x[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+}
+
+template <typename T, int CPL, int LPWAVE, bool FUSED>
 __global__ __launch_bounds__(256) void reduce_col_kernel(const T* __restrict__ X, int64_t ldx, int64_t rows,
                                                          int64_t cols, float* __restrict__ ws,
                                                          float* __restrict__ out_sum, float* __restrict__ out_sq,
                                                          int n_blocks)
 {
-    constexpr int LPWAVE = LPW / 4;  // leaves per wave (a power of two)
+    constexpr int LPW = 4 * LPWAVE;
     __shared__ float part[2][4][64 * CPL];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -191,6 +287,7 @@ __global__ __launch_bounds__(256) void reduce_col_kernel(const T* __restrict__ X
     const int blk = blockIdx.y;
     const int64_t n_leaf = (rows + kLeaf - 1) / kLeaf;
     const int64_t wleaf0 = (int64_t)blk * LPW + wave * LPWAVE;  // this wave's first leaf
+    const bool vec = col0 + CPL <= cols;
 
     float ls[LPWAVE][CPL], lq[LPWAVE][CPL];
     int n_mine = 0;  // leaves of this wave that exist
@@ -202,56 +299,35 @@ __global__ __launch_bounds__(256) void reduce_col_kernel(const T* __restrict__ X
         const int64_t r0 = leaf * kLeaf;
         const int n = (int)((rows - r0) < kLeaf ? (rows - r0) : kLeaf);
         float s[CPL], q[CPL];
-        auto fold_rows = [&](int nr) {
-        for (int i = 0; i < nr; i++) {
-            const T* p = X + (r0 + i) * ldx + col0;
-            float x[CPL];
-            if (col0 + CPL <= cols) {
-                if constexpr (std::is_same<T, float>::value) {
-                    const u32x4 v = *(const u32x4*)p;  // CPL == 4 for fp32
+        if (n == kLeaf && vec) {
+            // the whole leaf: 32 independent row loads, folded in row order
+            float x[kLeaf][CPL];
 #pragma unroll
-                    for (int c = 0; c < CPL; c++) x[c] = __uint_as_float(v[c]);
-                } else {
-                    if constexpr (CPL == 8) {
-                        const u32x4 v = *(const u32x4*)p;
-#pragma unroll
-                        for (int c = 0; c < 4; c++) {
-                            x[2 * c] = __uint_as_float(v[c] << 16);
-                            x[2 * c + 1] = __uint_as_float(v[c] & 0xffff0000u);
-                        }
-                    } else {
-                        const uint2 v = *(const uint2*)p;
-                        x[0] = __uint_as_float(v.x << 16);
-                        x[1] = __uint_as_float(v.x & 0xffff0000u);
-                        x[2] = __uint_as_float(v.y << 16);
-                        x[3] = __uint_as_float(v.y & 0xffff0000u);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int c = 0; c < CPL; c++) x[c] = (col0 + c < cols) ? load_elem<T>(p + c) : 0.0f;
-            }
+            for (int i = 0; i < kLeaf; i++) load_row_vec<T, CPL>(X + (r0 + i) * ldx + col0, x[i]);
 #pragma unroll
             for (int c = 0; c < CPL; c++) {
-                if (i == 0) {
-                    s[c] = x[c];
-                    q[c] = x[c] * x[c];
-                } else {
-                    s[c] = s[c] + x[c];
-                    if constexpr (FUSED) q[c] = __builtin_fmaf(x[c], x[c], q[c]);
-                    else {
-                        const float xx = x[c] * x[c];
-                        q[c] = q[c] + xx;
+                s[c] = x[0][c];
+                q[c] = x[0][c] * x[0][c];
+            }
+#pragma unroll
+            for (int i = 1; i < kLeaf; i++)
+#pragma unroll
+                for (int c = 0; c < CPL; c++) fold_step<FUSED>(x[i][c], s[c], q[c]);
+        } else {
+            // a short leaf or the ragged right edge, element by element
+            for (int i = 0; i < n; i++) {
+                const T* p = X + (r0 + i) * ldx + col0;
+#pragma unroll
+                for (int c = 0; c < CPL; c++) {
+                    const float x = (col0 + c < cols) ? load_elem<T>(p + c) : 0.0f;
+                    if (i == 0) {
+                        s[c] = x;
+                        q[c] = x * x;
+                    } else {
+                        fold_step<FUSED>(x, s[c], q[c]);
                     }
                 }
             }
-        }
-        };
-        if (n == kLeaf) {
-#pragma unroll
-            for (int h = 0; h < 1; h++) fold_rows(kLeaf);
-        } else {
-            fold_rows(n);
         }
 #pragma unroll
         for (int c = 0; c < CPL; c++) ls[l][c] = s[c], lq[l][c] = q[c];
@@ -261,9 +337,10 @@ __global__ __launch_bounds__(256) void reduce_col_kernel(const T* __restrict__ X
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
         float vs[LPWAVE], vq[LPWAVE];
-        for (int l = 0; l < n_mine; l++) vs[l] = ls[l][c], vq[l] = lq[l][c];
-        ws_[c] = n_mine ? small_tree(vs, n_mine) : 0.0f;
-        wq_[c] = n_mine ? small_tree(vq, n_mine) : 0.0f;
+#pragma unroll
+        for (int l = 0; l < LPWAVE; l++) vs[l] = ls[l][c], vq[l] = lq[l][c];
+        ws_[c] = n_mine ? tree_upto<LPWAVE>(vs, n_mine) : 0.0f;
+        wq_[c] = n_mine ? tree_upto<LPWAVE>(vq, n_mine) : 0.0f;
     }
 #pragma unroll
     for (int c = 0; c < CPL; c++) {
@@ -273,13 +350,15 @@ __global__ __launch_bounds__(256) void reduce_col_kernel(const T* __restrict__ X
     __syncthreads();
     // the workgroup's waves -> one node; waves with no leaf do not exist
     const int64_t blk_leaf0 = (int64_t)blk * LPW;
-    const int n_waves = (int)(((n_leaf - blk_leaf0) + LPWAVE - 1) / LPWAVE < 4 ? ((n_leaf - blk_leaf0) + LPWAVE - 1) / LPWAVE : 4);
+    const int64_t left = (n_leaf - blk_leaf0 + LPWAVE - 1) / LPWAVE;
+    const int n_waves = (int)(left < 4 ? left : 4);
     for (int idx = threadIdx.x; idx < 64 * CPL; idx += 256) {
         const int64_t col = (int64_t)blockIdx.x * 64 * CPL + idx;
         if (col >= cols) continue;
         float vs[4], vq[4];
-        for (int w = 0; w < n_waves; w++) vs[w] = part[0][w][idx], vq[w] = part[1][w][idx];
-        const float rs = small_tree(vs, n_waves), rq = small_tree(vq, n_waves);
+#pragma unroll
+        for (int w = 0; w < 4; w++) vs[w] = part[0][w][idx], vq[w] = part[1][w][idx];
+        const float rs = tree_upto<4>(vs, n_waves), rq = tree_upto<4>(vq, n_waves);
         if (n_blocks == 1) {
             if (out_sum) out_sum[col] = rs;
             if (out_sq) out_sq[col] = rq;
@@ -386,10 +465,7 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
 #undef BG_ROW
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || nb == 1) return e;
-        dim3 g2((unsigned)((rows + 255) / 256));
-        hipLaunchKernelGGL(reduce_blocks_kernel, g2, dim3(256), 0, stream, ws, rows, nb, (int64_t)nb, (int64_t)1,
-                           out_sum, out_sq);
-        return hipGetLastError();
+        return launch_blocks(ws, rows, nb, (int64_t)nb, (int64_t)1, out_sum, out_sq, stream);
     }
     const int cpl = p.bf16 ? p.cols_per_lane : 4;
     const int lpw = p.leaves_per_wg;
@@ -397,12 +473,12 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
     dim3 grid((unsigned)((cols + 64 * cpl - 1) / (64 * cpl)), (unsigned)nb), block(256);
     bool done = false;
 #define BG_COL(T, C, L, F)                                                                                       \
-    if (!done && cpl == C && lpw == L && p.fused == F) {                                                         \
+    if (!done && cpl == C && lpw == 4 * L && p.fused == F) {                                                     \
         hipLaunchKernelGGL((reduce_col_kernel<T, C, L, F>), grid, block, 0, stream, (const T*)X, ldx, rows, cols, ws, \
                            out_sum, out_sq, nb);                                                                 \
         done = true;                                                                                             \
     }
-#define BG_COL_L(T, C, F) BG_COL(T, C, 4, F) BG_COL(T, C, 8, F) BG_COL(T, C, 16, F) BG_COL(T, C, 32, F)
+#define BG_COL_L(T, C, F) BG_COL(T, C, 1, F) BG_COL(T, C, 2, F) BG_COL(T, C, 4, F) BG_COL(T, C, 8, F)
     if (p.bf16) {
         BG_COL_L(uint16_t, 4, true) BG_COL_L(uint16_t, 4, false) BG_COL_L(uint16_t, 8, true) BG_COL_L(uint16_t, 8, false)
     } else {
@@ -413,10 +489,7 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
     if (!done) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nb == 1) return e;
-    dim3 g2((unsigned)((cols + 255) / 256));
-    hipLaunchKernelGGL(reduce_blocks_kernel, g2, dim3(256), 0, stream, ws, cols, nb, (int64_t)1, cols, out_sum,
-                       out_sq);
-    return hipGetLastError();
+    return launch_blocks(ws, cols, nb, (int64_t)1, cols, out_sum, out_sq, stream);
 }
 
 hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, const void* X, int64_t ldx,

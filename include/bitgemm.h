@@ -139,8 +139,10 @@ typedef enum { BG_SQ_FUSED = 0, BG_SQ_UNFUSED = 1 } bg_sq_fma;
 typedef enum { BG_TREE_BALANCED = 0 } bg_tree;
 
 typedef struct {
-    int32_t leaves_per_wg;  /* column axis: leaves one workgroup folds (power of 2) */
-    int32_t cols_per_wg;    /* column axis: columns one workgroup covers       */
+    int32_t leaves_per_wg;  /* column axis: leaves one workgroup folds: 4, 8, 16
+                               or 32 (0: the fewest keeping <= 64 block roots) */
+    int32_t cols_per_wg;    /* column axis: columns one workgroup covers: 256,
+                               or 512 for bf16 (0: 16 bytes per lane)          */
     int32_t reserved0, reserved1;
 } bg_reduce_schedule;
 
