@@ -18,9 +18,13 @@ The same JSON line also carries:
   extra         the other workloads (smaller batches, the split-K sweep, the
                 small split-K GEMM, W8A8, the row and column reductions),
                 each parity-checked and timed the same way, with its
-                free-order twin where one exists.
+                free-order twin where one exists; "graph_us" is the same
+                call captured K times in one HIP graph and replayed, which
+                takes host launch cost off the clock for the short kernels
+                (rates are quoted on it).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-extra]
+       [--only-headline] [--copy-calibration]
 """
 import argparse
 import json
@@ -109,6 +113,31 @@ def time_steps(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def graph_time(fn, reps, torch, replays=5):
+    """Per-call time of `fn` with `reps` calls captured in one HIP graph and
+    replayed, so that host launch cost is off the clock (for the short
+    kernels, where it would otherwise dominate)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the plan caches outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * reps)
+
+
 def cpu_baseline(g, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the headline GEMM's
     outputs, on every host core it is given."""
@@ -135,9 +164,11 @@ def cpu_baseline(g, budget_s=12.0):
 
 
 def free_twin_us(g, args, torch, split_k=0):
+    """(eager us, graph us) of the free-order twin of GEMM workload g."""
     dF = torch.empty((g.M, g.N), dtype=torch.float32, device="cuda")
-    t, _ = time_steps(lambda: g.bg.bench_gemm_bf16_free(g.dA, g.dB, dF, split_k), args.steps, args.warmup, torch)
-    return t * 1e3
+    fn = lambda: g.bg.bench_gemm_bf16_free(g.dA, g.dB, dF, split_k)  # noqa: E731
+    t, _ = time_steps(fn, args.steps, args.warmup, torch)
+    return t * 1e3, graph_time(fn, args.steps, torch) * 1e3
 
 
 def gemm_extras(X, W, args, torch, bg, synth):
@@ -149,11 +180,14 @@ def gemm_extras(X, W, args, torch, bg, synth):
                  torch, bg)
         p = g.parity(128)
         t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-        free = free_twin_us(g, args, torch)
-        out[f"batch_sweep_M{M}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(g.flops() / t / 1e9, 2),
-                                    "GB/s": round(g.bytes() / t / 1e6, 1), "free_us": round(free, 2),
-                                    "fixed_over_free_time": round(t * 1e3 / free, 3), "parity": p}
-        log(f"bench: M={M}: {t * 1e3:.2f} us (free {free:.2f} us)")
+        tg = graph_time(g.run, args.steps, torch)
+        free, free_g = free_twin_us(g, args, torch)
+        out[f"batch_sweep_M{M}"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
+                                    "TFLOP/s": round(g.flops() / tg / 1e9, 2),
+                                    "GB/s": round(g.bytes() / tg / 1e6, 1), "free_us": round(free, 2),
+                                    "free_graph_us": round(free_g, 2),
+                                    "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p}
+        log(f"bench: M={M}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A4, W4 = synth.gemm_splitk_sweep()
     free = None
     for S in (1, 2, 4, 8, 16):
@@ -161,18 +195,22 @@ def gemm_extras(X, W, args, torch, bg, synth):
                  torch, bg)
         p = g.parity(128)
         t, _ = time_steps(g.run, args.steps, args.warmup, torch)
+        tg = graph_time(g.run, args.steps, torch)
         if free is None:
-            free = free_twin_us(g, args, torch)
-        out[f"splitk_S{S}"] = {"us": round(t * 1e3, 2), "TFLOP/s": round(g.flops() / t / 1e9, 2),
-                               "GB/s": round(g.bytes() / t / 1e6, 1), "free_us": round(free, 2),
-                               "fixed_over_free_time": round(t * 1e3 / free, 3), "parity": p}
-        log(f"bench: split-K S={S}: {t * 1e3:.2f} us (free {free:.2f} us)")
+            free, free_g = free_twin_us(g, args, torch)
+        out[f"splitk_S{S}"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
+                               "TFLOP/s": round(g.flops() / tg / 1e9, 2),
+                               "GB/s": round(g.bytes() / tg / 1e6, 1), "free_us": round(free, 2),
+                               "free_graph_us": round(free_g, 2),
+                               "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p}
+        log(f"bench: split-K S={S}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A1, B1 = synth.gemm_small()
     g = Gemm("small", A1, B1, {"mfma": "F32_32X32X16_BF16", "split_k": 2, "cut_rule": "EXPLICIT",
                                "cuts": [0, 256, 512], "out_type": "fp32"}, torch, bg)
     p = g.parity(256)
     t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-    out["small_32x64x512_S2"] = {"us": round(t * 1e3, 2), "parity": p}
+    tg = graph_time(g.run, args.steps, torch)
+    out["small_32x64x512_S2"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2), "parity": p}
     return out
 
 
@@ -195,13 +233,16 @@ def w8a8_extra(args, torch, bg, synth):
     Yo, acco = oracle.w8a8_pow2(a_q, w_q, a_s, w_s)
     par = {"checked": int(M * N), "acc_mismatches": int(np.sum(dacc.cpu().numpy() != acco)),
            "y_mismatches": int(np.sum(dY.cpu().numpy().view(np.uint16) != Yo))}
-    t, _ = time_steps(lambda: bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY), args.steps, args.warmup, torch)
+    fn = lambda: bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY)  # noqa: E731
+    t, _ = time_steps(fn, args.steps, args.warmup, torch)
+    tg = graph_time(fn, args.steps, torch)
     ops = 2.0 * M * N * K
     byts = M * K + N * K + 4 * (M + N) + 2 * M * N
-    log(f"bench: W8A8: {t * 1e3:.2f} us")
-    return {"w8a8_1024x6144x2048": {"us": round(t * 1e3, 2), "TOP/s": round(ops / t / 1e9, 2),
-                                    "frac_int8_peak": round(ops / t / 1e9 / PEAK_INT8_TOPS, 4),
-                                    "GB/s": round(byts / t / 1e6, 1), "parity": par}}
+    log(f"bench: W8A8: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us")
+    return {"w8a8_1024x6144x2048": {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
+                                    "TOP/s": round(ops / tg / 1e9, 2),
+                                    "frac_int8_peak": round(ops / tg / 1e9 / PEAK_INT8_TOPS, 4),
+                                    "GB/s": round(byts / tg / 1e6, 1), "parity": par}}
 
 
 def reduce_extras(args, torch, bg, synth):
@@ -231,15 +272,21 @@ def reduce_extras(args, torch, bg, synth):
         bad = int(np.sum(s.cpu().numpy()[idx].view(np.uint32) != rs.view(np.uint32)))
         if q is not None:
             bad += int(np.sum(q.cpu().numpy()[idx].view(np.uint32) != rq.view(np.uint32)))
-        t, _ = time_steps(lambda: bg.reduce_tree(d, dX, s, q, ws), args.steps, args.warmup, torch)
-        tf, _ = time_steps(lambda: bg.bench_reduce_free(axis, in_type, dX, s, q), args.steps, args.warmup, torch)
+        fn = lambda: bg.reduce_tree(d, dX, s, q, ws)  # noqa: E731
+        ffn = lambda: bg.bench_reduce_free(axis, in_type, dX, s, q)  # noqa: E731
+        t, _ = time_steps(fn, args.steps, args.warmup, torch)
+        tg = graph_time(fn, args.steps, torch)
+        tf, _ = time_steps(ffn, args.steps, args.warmup, torch)
+        tfg = graph_time(ffn, args.steps, torch)
         byts = rows * cols * elt + 4 * n_out * (2 if q is not None else 1)
-        gbs = byts / t / 1e6
+        gbs = byts / tg / 1e6
         out[f"reduce_{axis}_{in_type}_{rows}x{cols}"] = {
-            "us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-            "free_us": round(tf * 1e3, 2), "fixed_over_free_time": round(t / tf, 3),
+            "us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "free_us": round(tf * 1e3, 2),
+            "free_graph_us": round(tfg * 1e3, 2), "fixed_over_free_time": round(tg / tfg, 3),
             "parity": {"sampled_outputs": 64, "mismatches": bad}}
-        log(f"bench: reduce {axis}: {t * 1e3:.2f} us, {gbs:.0f} GB/s (free {tf * 1e3:.2f} us)")
+        log(f"bench: reduce {axis}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us, {gbs:.0f} GB/s "
+            f"(free {tf * 1e3:.2f} / {tfg * 1e3:.2f} us)")
     return out
 
 
@@ -250,6 +297,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline GEMM only (for counter runs): no twins, extras or CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
@@ -295,6 +346,19 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
     del wall
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: ran 3 plain copies of 1 GiB")
+        del src, dst
+    if args.only_headline:
+        line["config"]["note"] = "headline only (counter run)"
+        print(json.dumps(line), flush=True)
+        return
 
     # the free-order twin of the headline (fp32 out; split-K by CU count)
     dF = torch.empty((head.M, head.N), dtype=torch.float32, device="cuda")

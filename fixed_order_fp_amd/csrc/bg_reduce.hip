@@ -504,13 +504,14 @@ hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, c
                                ldx, cols, out_sum, out_sq);
         return hipGetLastError();
     }
-    // zero the outputs with a kernel-free memset, then one strip per CU-sized slot
+    // zero the outputs (a fill kernel, so the sequence can be graph-captured),
+    // then one strip per CU-sized slot
     if (out_sum) {
-        hipError_t e = hipMemsetAsync(out_sum, 0, cols * sizeof(float), stream);
+        hipError_t e = launch_zero_rows(out_sum, 1, cols, cols, stream);
         if (e != hipSuccess) return e;
     }
     if (out_sq) {
-        hipError_t e = hipMemsetAsync(out_sq, 0, cols * sizeof(float), stream);
+        hipError_t e = launch_zero_rows(out_sq, 1, cols, cols, stream);
         if (e != hipSuccess) return e;
     }
     const int64_t col_wgs = (cols + 511) / 512;
