@@ -25,6 +25,7 @@ The same JSON line also carries:
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-extra]
        [--only-headline] [--copy-calibration]
+       python bench.py --summarize-trace <rocprofv3 kernel_trace.csv>
 """
 import argparse
 import json
@@ -190,10 +191,19 @@ def gemm_extras(X, W, args, torch, bg, synth):
         log(f"bench: M={M}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A4, W4 = synth.gemm_splitk_sweep()
     free = None
+    base = None
     for S in (1, 2, 4, 8, 16):
         g = Gemm(f"splitk S={S}", A4, W4, {"mfma": "F32_32X32X16_BF16", "split_k": S, "out_type": "fp32"},
                  torch, bg)
         p = g.parity(128)
+        # how many outputs this split count changes against S = 1 (fp32 bits,
+        # and after a bf16 rounding of both)
+        cur = g.dC.clone()
+        if base is None:
+            base = cur
+        diff32 = int((cur.view(torch.int32) != base.view(torch.int32)).sum().item())
+        diff16 = int((cur.to(torch.bfloat16).view(torch.int16) != base.to(torch.bfloat16).view(torch.int16))
+                     .sum().item())
         t, _ = time_steps(g.run, args.steps, args.warmup, torch)
         tg = graph_time(g.run, args.steps, torch)
         if free is None:
@@ -202,7 +212,9 @@ def gemm_extras(X, W, args, torch, bg, synth):
                                "TFLOP/s": round(g.flops() / tg / 1e9, 2),
                                "GB/s": round(g.bytes() / tg / 1e6, 1), "free_us": round(free, 2),
                                "free_graph_us": round(free_g, 2),
-                               "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p}
+                               "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p,
+                               "outputs_differing_from_S1": {"fp32": diff32, "after_bf16_rounding": diff16,
+                                                             "of": int(g.M * g.N)}}
         log(f"bench: split-K S={S}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A1, B1 = synth.gemm_small()
     g = Gemm("small", A1, B1, {"mfma": "F32_32X32X16_BF16", "split_k": 2, "cut_rule": "EXPLICIT",
@@ -290,7 +302,58 @@ def reduce_extras(args, torch, bg, synth):
     return out
 
 
+def summarize_trace(path):
+    """Markdown table of a rocprofv3 kernel-trace CSV grouped by kernel and grid
+    size (one workload per grid), so a kernel that serves several workloads
+    gets one row per workload."""
+    import csv
+    import statistics
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            grid = r.get("Grid_Size") or r.get("Grid_Size_X")
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            groups.setdefault((r["Kernel_Name"], grid, r.get("Workgroup_Size_X", "")), []).append(dur)
+    print("| kernel | grid (threads) | block | calls | mean us | median us | min us |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name.split("(")[0].replace("void ", "")
+        print(f"| `{short}` | {grid} | {wg} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | "
+              f"{statistics.median(v) / 1e3:.2f} | {min(v) / 1e3:.2f} |")
+
+
+def kernel_source_digest():
+    """sha256 of the GEMM kernel source: stored counter readings apply only to
+    the kernel they were taken on."""
+    import hashlib
+    with open(os.path.join(ROOT, "fixed_order_fp_amd", "csrc", "bg_gemm_bf16.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic():
+    """HBM-side bytes per launch of the headline GEMM from the committed
+    counter summary, scaled by the copy-kernel calibration; None when the
+    kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_4000x9728x2560_counters.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("    ") and ":" in line:
+                k, v = line.strip().split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024
+    write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]) * 1024
+    return round(fetch + write)
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -343,7 +406,8 @@ def main():
                    "out": "bf16"},
         "parity": par,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic()},
     }
     del wall
 
