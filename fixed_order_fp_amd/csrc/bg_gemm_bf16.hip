@@ -17,6 +17,8 @@
 // the MFMA operand reads, 16 B per lane down 32 rows, hit distinct banks),
 // double-buffered with one barrier per turn; MFMA operands are read from LDS
 // in the placement of the instruction (lane half h holds k 8h..8h+7).
+#include <type_traits>
+
 #include "bg_internal.h"
 
 namespace bg {
@@ -400,6 +402,310 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
             }
 }
 
+// ---- the pipelined kernel for large M x N --------------------------------
+//
+// The same order as the kernels above; only the schedule differs.
+//  * k tiles of 32 (4 chunks of 16 B per row, swizzled by (row >> 2) & 3 so
+//    the operand reads of 16 consecutive rows hit 16 distinct bank groups),
+//    NS stages in LDS, turn t+NS-1 copied while turn t is multiplied;
+//  * one barrier per turn, placed before the turn's last k-step: the MFMAs
+//    of the step before it are still queued while waves meet there, and the
+//    first operands of the next turn are read right after it;
+//  * MFMA operands swapped (the B fragment is the instruction's first operand,
+//    so the instruction computes the transposed 32x32 block): every product
+//    and every k group is the same, and each lane ends up holding 4
+//    consecutive columns of one row of C;
+//  * bf16 output is staged through LDS and written row by row, 16 bytes per
+//    lane with consecutive lanes on consecutive addresses.
+//
+// 16 bytes from global memory into LDS at byte address lds_addr + 16 * lane
+// (global_load_lds_dwordx4; M0 holds the LDS address and is restored).  It is
+// issued as inline assembly so that the compiler, which cannot place an LDS
+// DMA among its LDS reads, does not drain every read before each MFMA; the
+// copies are waited for with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_addr)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait until at most `newer` turns of LOADS copies each are outstanding
+template <int LOADS, int MAXN>
+__device__ __forceinline__ void wait_turns(int newer)
+{
+    if constexpr (MAXN >= 3) { if (newer >= 3) { wait_vmcnt<3 * LOADS>(); return; } }
+    if constexpr (MAXN >= 2) { if (newer >= 2) { wait_vmcnt<2 * LOADS>(); return; } }
+    if constexpr (MAXN >= 1) { if (newer >= 1) { wait_vmcnt<1 * LOADS>(); return; } }
+    wait_vmcnt<0>();
+}
+
+// Staged bf16 C rows hold CHR 16-byte chunks; chunk ch of row m is stored at
+// position ch ^ (m & mask) inside its row (within the leading power of two of
+// chunks, and within the trailing eight), so that the writes of 16
+// consecutive rows to one column chunk land in distinct bank groups.
+template <int CHR>
+__device__ __forceinline__ int c_swizzle(int ch, int m)
+{
+    static_assert(CHR == 16 || CHR == 32 || CHR == 40, "staged row widths: 128, 256 or 320 columns");
+    if constexpr (CHR == 40) return ch < 32 ? ch ^ (m & 31) : ch ^ (m & 7);
+    else return ch ^ (m & (CHR - 1));
+}
+
+// LDS the pipelined kernel uses, and the waves per SIMD that leaves room for
+template <int BM, int BN, int NS, int OUT>
+struct PipeLds {
+    static constexpr int STAGE_BYTES = (BM + BN) * 64;  // k tile of 32 bf16 per row
+    static constexpr int PIPE = NS * STAGE_BYTES, EPI = OUT == 1 ? BM * BN * 2 : 0;
+    static constexpr int BYTES = PIPE > EPI ? PIPE : EPI;
+    static constexpr int WG_PER_CU = (160 * 1024) / BYTES;
+};
+template <int BM, int BN, int WM, int WN, int NS, int OUT>
+struct PipeOcc {
+    static constexpr int W = PipeLds<BM, BN, NS, OUT>::WG_PER_CU * WM * WN / 4;
+    static constexpr int WAVES_PER_EU = W < 1 ? 1 : W;
+};
+
+// OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace
+template <int BM, int BN, int WM, int WN, int NS, int OUT>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
+    PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU)))
+void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+                           int64_t ldb, void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M,
+                           int64_t N, Cuts cuts, int tiles_m, int tiles_n, int group_m)
+{
+    constexpr int BK = 32, CPR = BK / kChunk, KS = BK / 16;
+    constexpr int NW = WM * WN, NT = 64 * NW;
+    constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+    constexpr int A_CH = BM * CPR, B_CH = BN * CPR;
+    constexpr int STAGE = A_CH + B_CH;  // 16-byte chunks per stage
+    // a stage is copied in slots of 64 chunks (one instruction per wave); slot
+    // s goes to wave s % NW in round s / NW, so waves below SLOTS % NW make
+    // one copy more per tile than the others
+    constexpr int SLOTS = STAGE / 64, ROUNDS = (SLOTS + NW - 1) / NW, EXTRA = SLOTS % NW;
+    constexpr int LOADS_HI = ROUNDS, LOADS_LO = EXTRA ? ROUNDS - 1 : ROUNDS;
+    constexpr int CHR = BN / 8;  // 16-byte chunks per staged bf16 C row
+    constexpr int LDS_BYTES = PipeLds<BM, BN, NS, OUT>::BYTES;
+    static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "tile rows must fill whole copy slots");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole MFMA blocks");
+    static_assert(NS >= 3 && LOADS_HI * (NS - 2) < 64, "stages: three at least, waits within vmcnt");
+    static_assert(KS == 2, "two k-steps per turn: the fragment buffers alternate within a turn");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
+    __shared__ u32x4 lds[LDS_BYTES / 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int split = blockIdx.y;
+    const int64_t k_begin = cuts.c[split];
+    const int64_t k_end = cuts.c[split + 1];
+    const int n_full = (int)((k_end - k_begin) / BK);
+    const int n_turns = (int)((k_end - k_begin + BK - 1) / BK);
+    const bool hi = EXTRA == 0 || wave < EXTRA;  // this wave copies ROUNDS slots
+
+    // the chunk this lane copies in round r: stage chunk c = 64 s + lane (A
+    // rows first, then B rows), global (row, logical chunk kc) under the swizzle
+    const uint16_t* src[ROUNDS];
+    int kcs[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; r++) {
+        const int s = r * NW + wave;
+        const int c = (s < SLOTS ? s : 0) * 64 + lane;
+        const bool is_a = c < A_CH;
+        const int row = is_a ? c / CPR : (c - A_CH) / CPR;
+        kcs[r] = (c % CPR) ^ ((row >> 2) & 3);
+        int64_t g = (is_a ? m0 : n0) + row;
+        const int64_t lim = is_a ? M : N;
+        g = g < lim ? g : lim - 1;  // rows past M or N read a clamped row: never stored
+        src[r] = (is_a ? A + g * lda : B + g * ldb) + k_begin + kcs[r] * kChunk;
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)lds);
+
+    // copy k tile `turn` into its stage; the short last tile (k_end not a
+    // multiple of 32 past k_begin) goes through registers with zeros past
+    // k_end (cut points are multiples of 8, so a chunk is all in or all out)
+    auto issue = [&](int turn) {
+        const int st = turn % NS;
+        const int64_t kb = (int64_t)turn * BK;
+#pragma unroll
+        for (int r = 0; r < ROUNDS; r++) {
+            const int s = r * NW + wave;
+            if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS) {
+                if (turn < n_full) {
+                    dma16(src[r] + kb, lds_base + (uint32_t)(st * STAGE + s * 64) * 16u);
+                } else {
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (k_begin + kb + kcs[r] * kChunk < k_end) v = *(const u32x4*)(src[r] + kb);
+                    lds[st * STAGE + s * 64 + lane] = v;
+                }
+            }
+        }
+    };
+    // copied turns after turn `after` that may still be in flight once turns
+    // up to `last` have been issued (the short tile is synchronous)
+    auto dma_newer = [&](int after, int last) {
+        const int l = last < n_full - 1 ? last : n_full - 1;
+        return l > after ? l - after : 0;
+    };
+    // wait until at most `newer` turns of this wave's copies are outstanding
+    auto wait_newer = [&](int newer, auto max_tag) {
+        constexpr int MAXN = decltype(max_tag)::value;
+        if (hi) wait_turns<LOADS_HI, MAXN>(newer);
+        else wait_turns<LOADS_LO, MAXN>(newer);
+    };
+
+    // operand fragment offsets (in chunks) for the two k-steps of a turn; the
+    // 32-row blocks of a wave add multiples of 32 rows, which keep the swizzle
+    const int r_in = lane & 31, h = lane >> 5;
+    int a_off[KS], b_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        a_off[ks] = (wm * WTM + r_in) * CPR + ((2 * ks + h) ^ ((r_in >> 2) & 3));
+        b_off[ks] = A_CH + (wn * WTN + r_in) * CPR + ((2 * ks + h) ^ ((r_in >> 2) & 3));
+    }
+    auto rd = [&](int turn, int ks, bf16x8* a, bf16x8* b) {
+        const u32x4* base = lds + (turn % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < TM; i++) a[i] = __builtin_bit_cast(bf16x8, base[a_off[ks] + i * 32 * CPR]);
+#pragma unroll
+        for (int j = 0; j < TN; j++) b[j] = __builtin_bit_cast(bf16x8, base[b_off[ks] + j * 32 * CPR]);
+    };
+
+    f32x16 acc[TN][TM];  // block (j, i): rows n of C^T = columns n of C
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[j][i][e] = 0.0f;
+    auto mm = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+    };
+
+    // prologue: tiles 0 .. NS-2 in flight, tile 0 landed and visible
+#pragma unroll
+    for (int s = 0; s < NS - 1; s++)
+        if (s < n_turns) issue(s);
+    wait_newer(dma_newer(0, NS - 2), std::integral_constant<int, NS - 2>{});
+    __syncthreads();
+
+    bf16x8 xa[2][TM], xb[2][TN];
+    rd(0, 0, xa[0], xb[0]);
+    // FULL: tiles t+1 .. t+NS-1 are all whole, so every wait and copy is
+    // unconditional and the loop body has no branch (the compiler can then
+    // count LDS reads across the back edge)
+    auto turn = [&](int t, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        // k-step 0: read the operands of k-step 1, multiply k-step 0
+        rd(t, 1, xa[1], xb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(xa[0], xb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        // tile t+1 must have landed in every wave's share before its first read
+        if constexpr (FULL) {
+            if (hi) wait_vmcnt<LOADS_HI * (NS - 3)>();
+            else wait_vmcnt<LOADS_LO * (NS - 3)>();
+        } else {
+            const int last = t + NS - 2 < n_turns - 1 ? t + NS - 2 : n_turns - 1;
+            wait_newer(dma_newer(t + 1, last), std::integral_constant<int, NS - 3>{});
+        }
+        __builtin_amdgcn_s_barrier();
+        // every wave is past its reads of tile t-1: its stage takes tile t+NS-1
+        if constexpr (FULL) {
+            issue(t + NS - 1);
+        } else {
+            if (t + NS - 1 < n_turns) issue(t + NS - 1);
+        }
+        rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
+        __builtin_amdgcn_sched_barrier(0);
+        mm(xa[1], xb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    const int n_steady = n_full - (NS - 1);
+    int t = 0;
+    for (; t < n_steady; t++) turn(t, std::true_type{});
+    for (; t < n_turns; t++) turn(t, std::false_type{});
+
+    // epilogue.  Block (j, i), element e of lane l: row m = wm*WTM + 32i + l%32,
+    // columns n = wn*WTN + 32j + 8(e/4) + 4(l/32) + (0..3) for e%4 = 0..3.
+    if constexpr (OUT == 1) {
+        __syncthreads();  // every wave is done with the operand stages
+        unsigned char* cl = (unsigned char*)lds;
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int m = wm * WTM + i * 32 + r_in;
+                    const int n = wn * WTN + j * 32 + 8 * q;  // chunk n/8; lane half h takes bytes 8h..8h+7
+                    uint2 w;
+                    w.x = bf16x2_rne(acc[j][i][4 * q + 0], acc[j][i][4 * q + 1]);
+                    w.y = bf16x2_rne(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
+                    *(uint2*)(cl + m * (BN * 2) + c_swizzle<CHR>(n / 8, m) * 16 + h * 8) = w;
+                }
+        __syncthreads();
+        uint16_t* Cb = (uint16_t*)C;
+        for (int c = tid; c < BM * CHR; c += NT) {
+            const int row = c / CHR, ch = c % CHR;
+            const int64_t gm = m0 + row, gn = n0 + ch * 8;
+            if (gm >= M || gn >= N) continue;
+            const u32x4 v = *(const u32x4*)(cl + row * (BN * 2) + c_swizzle<CHR>(ch, row) * 16);
+            if (gn + 8 <= N) {
+                *(u32x4*)(Cb + gm * ldc + gn) = v;
+            } else {
+                for (int u = 0; u < 8 && gn + u < N; u++)
+                    Cb[gm * ldc + gn + u] = (uint16_t)(v[u / 2] >> (16 * (u % 2)));
+            }
+        }
+    } else {
+        float* out = OUT == 2 ? ws + (int64_t)split * M * N : (float*)C;
+        const int64_t ld = OUT == 2 ? N : ldc;
+        const bool vec_ok = (ld % 4) == 0;
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int64_t gm = m0 + wm * WTM + i * 32 + r_in;
+                    const int64_t gn = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
+                    if (gm >= M || gn >= N) continue;
+                    float* p = out + gm * ld + gn;
+                    if (vec_ok && gn + 4 <= N) {
+                        f32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+                        *(f32x4*)p = v;
+                    } else {
+                        for (int u = 0; u < 4 && gn + u < N; u++) p[u] = acc[j][i][4 * q + u];
+                    }
+                }
+    }
+}
+
 // Balanced tree over v[0..n), neighbours first, an odd last element carried
 // up unchanged.  With n a compile-time constant the loops unroll and v stays
 // in registers.
@@ -490,6 +796,30 @@ struct TileLauncher<1> {
 };
 
 template <>
+struct TileLauncher<2> {
+    template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+    static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
+    {
+        static_assert(INSTR == BG_MFMA_F32_32X32X16_BF16 && BK == 32, "the pipelined path: 32x32x16, k tiles of 32");
+        if (p.atomic) return hipErrorInvalidValue;  // the free-order twin uses the other paths
+        const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+        const int group_m = p.group_m > 0 ? p.group_m : 8;
+        dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.S), block(64 * WM * WN);
+        if (p.S > 1)
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, 4, 2>), grid, block, 0, stream, A, lda, B, ldb,
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        else if (p.out_bf16)
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, 4, 1>), grid, block, 0, stream, A, lda, B, ldb,
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        else
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, 4, 0>), grid, block, 0, stream, A, lda, B, ldb,
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        return hipGetLastError();
+    }
+};
+
+template <>
 struct TileLauncher<0> {
     template <int INSTR, int BM, int BN, int BK, int WM, int WN>
     static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
@@ -564,8 +894,14 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
 }
 
 // The tile shapes compiled in: (instruction, BM, BN, BK, waves_m, waves_n,
-// direct-to-LDS staging).
+// load path: 0 registers, 1 direct-to-LDS, 2 pipelined direct-to-LDS).
 #define BG_GEMM_TILES(X)                                            \
+    X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 32, 2, 4, 2)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 32, 4, 2, 2)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 2, 2)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 4, 2)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 32, 2, 2, 2)             \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2)             \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 2, 1)             \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 4, 1)             \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 64, 2, 2, 1)             \
