@@ -34,7 +34,7 @@ STATUS = {0: "BG_OK", 1: "BG_E_INVALID", 2: "BG_E_UNSUPPORTED", 3: "BG_E_WORKSPA
 class GemmSchedule(C.Structure):
     _fields_ = [("bm", C.c_int32), ("bn", C.c_int32), ("bk", C.c_int32),
                 ("waves_m", C.c_int32), ("waves_n", C.c_int32), ("load_path", C.c_int32),
-                ("group_m", C.c_int32), ("combine_block", C.c_int32)]
+                ("group_m", C.c_int32), ("stages", C.c_int32)]
 
 
 class GemmDesc(C.Structure):

@@ -129,19 +129,54 @@ bg_status check_common_order(const bg_gemm_desc* d)
     return BG_OK;
 }
 
-// Speed only: a tile shape for the problem (measured on MI355X: the 128x128
-// direct-to-LDS tile, two workgroups per CU, leads from M = 64 up; below
-// that 64x64 register-staged tiles give the most workgroups).
+// Speed only: a tile shape for the problem (every shape gives the same bits).
+// Chosen from measurements on MI355X: large outputs take the pipelined
+// 320x256 / 256x320 tiles (8 waves, two rounds of workgroups at the headline
+// size); smaller outputs take smaller pipelined tiles with deeper LDS
+// pipelines, since each workgroup's walk over K is then bound by copy
+// latency rather than by the MFMA rate.  Needs p.S and p.cuts set.
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
 {
-    auto set = [&](int bm, int bn, int wm, int wn, int direct) {
-        p.bm = bm, p.bn = bn, p.bk = 64, p.waves_m = wm, p.waves_n = wn, p.direct = direct;
+    auto set = [&](int bm, int bn, int bk, int wm, int wn, int direct, int stages) {
+        p.bm = bm, p.bn = bn, p.bk = bk, p.waves_m = wm, p.waves_n = wn, p.direct = direct, p.stages = stages;
     };
-    const bool i32 = p.mfma == BG_MFMA_F32_32X32X16_BF16;
-    if (M > 32 && N >= 128 && (M >= 128 || i32)) set(128, 128, 2, 2, i32 ? 1 : 0);
-    else if (M > 16 || i32) set(64, 64, 2, 2, 0);
-    else set(32, 32, 1, 1, 0);
-    (void)N;
+    if (p.mfma != BG_MFMA_F32_32X32X16_BF16) {
+        if (M > 32 && N >= 128 && M >= 128) set(128, 128, 64, 2, 2, 0, 0);
+        else if (M > 16) set(64, 64, 64, 2, 2, 0, 0);
+        else set(32, 32, 64, 1, 1, 0, 0);
+        return;
+    }
+    const int64_t n_cu = 256;
+    // fraction of the last round of workgroups that is busy, weighted in
+    auto quant = [&](int64_t bm, int64_t bn, int per_cu) {
+        const int64_t wgs = ceil_div(M, bm) * ceil_div(N, bn) * p.S;
+        const int64_t slots = n_cu * per_cu;
+        return (double)(M * N) / (double)(ceil_div(wgs, slots) * slots * bm * bn) * p.S;
+    };
+    if (ceil_div(M, 256) * ceil_div(N, 256) * p.S >= 384) {
+        if (quant(320, 256, 1) >= quant(256, 320, 1)) set(320, 256, 32, 2, 4, 2, 4);
+        else set(256, 320, 32, 4, 2, 2, 4);
+        return;
+    }
+    if (M <= 64) {
+        set(64, 64, 32, 2, 2, 2, 8);
+        return;
+    }
+    // deep splits: the largest tile that still gives ~150 workgroups;
+    // shallow splits: small tiles (their prologue and epilogue weigh less)
+    auto wgs = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn) * p.S; };
+    const int64_t turns = p.cuts.c[1] / 32;
+    if (turns >= 64) {
+        if (wgs(256, 128) >= 150) set(256, 128, 32, 2, 2, 2, 4);
+        else if (wgs(128, 128) >= 150) set(128, 128, 32, 2, 2, 2, 5);
+        else if (wgs(128, 64) >= 150) set(128, 64, 32, 2, 2, 2, 8);
+        else set(64, 64, 32, 2, 2, 2, 8);
+        return;
+    }
+    if (wgs(64, 64) <= 2048) set(64, 64, 32, 2, 2, 2, 8);
+    else set(128, 64, 32, 2, 2, 2, 4);
 }
 
 }  // namespace
@@ -325,10 +360,11 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
     const bg_gemm_schedule& s = d->sched;
     p.group_m = s.group_m;
     if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
-        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path))
-            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path) is not compiled in");
+        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path, s.stages))
+            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path, stages) is not compiled in");
         p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
         p.direct = s.load_path;
+        p.stages = s.stages;
     } else {
         choose_gemm_tile(p, M, N);
     }
@@ -480,21 +516,25 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     bg::GemmPlan p{};
     p.mfma = BG_MFMA_F32_32X32X16_BF16;
     p.out_bf16 = false;
+    p.S = 1;
+    p.cuts.c[0] = 0;
+    p.cuts.c[1] = K;
     choose_gemm_tile(p, M, N);
     int S = split_k;
-    if (S <= 0) {  // enough workgroups for two per CU, each split at least 256 deep
+    if (S <= 0) {  // at least one workgroup per CU, each split at least 256 deep
         int dev = 0, n_cu = 256;
         if (hipGetDevice(&dev) == hipSuccess)
             (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
         const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
         S = 1;
-        while (S < BG_MAX_SPLIT && tiles * S < 2 * n_cu && K / (2 * S) >= 256) S *= 2;
+        while (S < BG_MAX_SPLIT && tiles * S < n_cu && K / (2 * S) >= 256) S *= 2;
     }
     const int64_t span = (K / (64 * (int64_t)S)) * 64;
     if (S > 1 && span == 0) return fail(BG_E_INVALID, "K too small for that many splits");
     p.S = S;
     for (int s = 0; s < S; s++) p.cuts.c[s] = s * span;
     p.cuts.c[S] = K;
+    if (S > 1) choose_gemm_tile(p, M, N);  // the tile for the split grid
     p.atomic = S > 1;
     hipError_t e = hipSuccess;
     if (p.atomic) e = bg::launch_zero_rows(C, M, N, ldc, stream);

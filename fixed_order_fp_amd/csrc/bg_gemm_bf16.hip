@@ -446,13 +446,19 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // wait until at most `newer` turns of LOADS copies each are outstanding
+// (newer <= MAXN; a larger value waits for more than needed, never less)
 template <int LOADS, int MAXN>
 __device__ __forceinline__ void wait_turns(int newer)
 {
-    if constexpr (MAXN >= 3) { if (newer >= 3) { wait_vmcnt<3 * LOADS>(); return; } }
-    if constexpr (MAXN >= 2) { if (newer >= 2) { wait_vmcnt<2 * LOADS>(); return; } }
-    if constexpr (MAXN >= 1) { if (newer >= 1) { wait_vmcnt<1 * LOADS>(); return; } }
-    wait_vmcnt<0>();
+    if constexpr (MAXN >= 1) {
+        if (newer >= MAXN) {
+            wait_vmcnt<MAXN * LOADS>();
+            return;
+        }
+        wait_turns<LOADS, MAXN - 1>(newer);
+    } else {
+        wait_vmcnt<0>();
+    }
 }
 
 // Staged bf16 C rows hold CHR 16-byte chunks; chunk ch of row m is stored at
@@ -462,7 +468,8 @@ __device__ __forceinline__ void wait_turns(int newer)
 template <int CHR>
 __device__ __forceinline__ int c_swizzle(int ch, int m)
 {
-    static_assert(CHR == 16 || CHR == 32 || CHR == 40, "staged row widths: 128, 256 or 320 columns");
+    static_assert(CHR == 4 || CHR == 8 || CHR == 16 || CHR == 32 || CHR == 40,
+                  "staged row widths: 32, 64, 128, 256 or 320 columns");
     if constexpr (CHR == 40) return ch < 32 ? ch ^ (m & 31) : ch ^ (m & 7);
     else return ch ^ (m & (CHR - 1));
 }
@@ -481,7 +488,8 @@ struct PipeOcc {
     static constexpr int WAVES_PER_EU = W < 1 ? 1 : W;
 };
 
-// OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace
+// OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32
+// split partial added into C with atomics (the free-order twin only)
 template <int BM, int BN, int WM, int WN, int NS, int OUT>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
     PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU)))
@@ -696,7 +704,9 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
                     const int64_t gn = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
                     if (gm >= M || gn >= N) continue;
                     float* p = out + gm * ld + gn;
-                    if (vec_ok && gn + 4 <= N) {
+                    if constexpr (OUT == 3) {
+                        for (int u = 0; u < 4 && gn + u < N; u++) unsafeAtomicAdd(p + u, acc[j][i][4 * q + u]);
+                    } else if (vec_ok && gn + 4 <= N) {
                         f32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
                         *(f32x4*)p = v;
                     } else {
@@ -771,7 +781,7 @@ struct TileLauncher;
 
 template <>
 struct TileLauncher<1> {
-    template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+    template <int INSTR, int BM, int BN, int BK, int WM, int WN, int NS>
     static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                           const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
     {
@@ -797,23 +807,27 @@ struct TileLauncher<1> {
 
 template <>
 struct TileLauncher<2> {
-    template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+    template <int INSTR, int BM, int BN, int BK, int WM, int WN, int NS>
     static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                           const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
     {
         static_assert(INSTR == BG_MFMA_F32_32X32X16_BF16 && BK == 32, "the pipelined path: 32x32x16, k tiles of 32");
-        if (p.atomic) return hipErrorInvalidValue;  // the free-order twin uses the other paths
         const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-        const int group_m = p.group_m > 0 ? p.group_m : 8;
+        // default walk: down whole tile columns (each XCD's run of tiles then
+        // shares B panels and streams A; measured best on MI355X)
+        const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
         dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.S), block(64 * WM * WN);
-        if (p.S > 1)
-            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, 4, 2>), grid, block, 0, stream, A, lda, B, ldb,
+        if (p.atomic)  // free-order twin only
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 3>), grid, block, 0, stream, A, lda, B, ldb,
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+        else if (p.S > 1)
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, stream, A, lda, B, ldb,
                                C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
         else if (p.out_bf16)
-            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, 4, 1>), grid, block, 0, stream, A, lda, B, ldb,
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, stream, A, lda, B, ldb,
                                C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
         else
-            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, 4, 0>), grid, block, 0, stream, A, lda, B, ldb,
+            hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, stream, A, lda, B, ldb,
                                C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
         return hipGetLastError();
     }
@@ -821,7 +835,7 @@ struct TileLauncher<2> {
 
 template <>
 struct TileLauncher<0> {
-    template <int INSTR, int BM, int BN, int BK, int WM, int WN>
+    template <int INSTR, int BM, int BN, int BK, int WM, int WN, int NS>
     static hipError_t run(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                           const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
     {
@@ -894,35 +908,56 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
 }
 
 // The tile shapes compiled in: (instruction, BM, BN, BK, waves_m, waves_n,
-// load path: 0 registers, 1 direct-to-LDS, 2 pipelined direct-to-LDS).
+// load path: 0 registers, 1 direct-to-LDS, 2 pipelined direct-to-LDS, LDS
+// stages of the pipelined path; the other paths double-buffer).  The first
+// entry of a shape is its default stage count.
 #define BG_GEMM_TILES(X)                                            \
-    X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 32, 2, 4, 2)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 32, 4, 2, 2)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 2, 2)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 4, 2)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 32, 2, 2, 2)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 2, 1)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 4, 1)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 64, 2, 2, 1)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 128, 256, 64, 2, 2, 1)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 1)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 0)             \
-    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2, 0)               \
-    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 64, 1, 2, 0)               \
-    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 64, 1, 1, 0)               \
-    X(BG_MFMA_F32_16X16X32_BF16, 256, 256, 64, 2, 2, 1)             \
-    X(BG_MFMA_F32_16X16X32_BF16, 256, 128, 64, 2, 2, 1)             \
-    X(BG_MFMA_F32_16X16X32_BF16, 128, 128, 64, 2, 2, 0)             \
-    X(BG_MFMA_F32_16X16X32_BF16, 64, 64, 64, 2, 2, 0)               \
-    X(BG_MFMA_F32_16X16X32_BF16, 32, 32, 64, 1, 1, 0)               \
-    X(BG_MFMA_F32_16X16X32_BF16, 16, 32, 64, 1, 2, 0)
+    X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 32, 2, 4, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 32, 4, 2, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 2, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 4, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 32, 2, 2, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 32, 2, 2, 2, 6)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2, 5)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2, 8)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 64, 32, 2, 2, 2, 4)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 64, 32, 2, 2, 2, 8)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 128, 32, 2, 2, 2, 4)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 128, 32, 2, 2, 2, 8)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 32, 2, 2, 2, 4)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 32, 2, 2, 2, 8)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 32, 2, 2, 2, 12)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 128, 32, 1, 4, 2, 4)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 128, 32, 1, 4, 2, 8)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 32, 1, 2, 2, 4)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 32, 1, 2, 2, 8)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 32, 1, 2, 2, 12)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 32, 1, 1, 2, 4)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 32, 1, 1, 2, 8)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 32, 1, 1, 2, 16)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 2, 1, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 4, 1, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 64, 2, 2, 1, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 256, 64, 2, 2, 1, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 1, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 0, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2, 0, 2)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 64, 1, 2, 0, 2)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 32, 64, 1, 1, 0, 2)            \
+    X(BG_MFMA_F32_16X16X32_BF16, 256, 256, 64, 2, 2, 1, 2)          \
+    X(BG_MFMA_F32_16X16X32_BF16, 256, 128, 64, 2, 2, 1, 2)          \
+    X(BG_MFMA_F32_16X16X32_BF16, 128, 128, 64, 2, 2, 0, 2)          \
+    X(BG_MFMA_F32_16X16X32_BF16, 64, 64, 64, 2, 2, 0, 2)            \
+    X(BG_MFMA_F32_16X16X32_BF16, 32, 32, 64, 1, 1, 0, 2)            \
+    X(BG_MFMA_F32_16X16X32_BF16, 16, 32, 64, 1, 2, 0, 2)
 
-bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct)
+// stages == 0 takes the first compiled entry of the shape
+bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct, int stages)
 {
-#define BG_HAS(I, BM_, BN_, BK_, WM_, WN_, D_)                                                      \
+#define BG_HAS(I, BM_, BN_, BK_, WM_, WN_, D_, NS_)                                                 \
     if (mfma == I && bm == BM_ && bn == BN_ && bk == BK_ && waves_m == WM_ && waves_n == WN_ &&      \
-        direct == D_)                                                                                \
+        direct == D_ && (stages == 0 || stages == NS_))                                              \
         return true;
     BG_GEMM_TILES(BG_HAS)
 #undef BG_HAS
@@ -936,11 +971,11 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, 
     (void)K;
     hipError_t err = hipErrorInvalidValue;
     bool found = false;
-#define BG_LAUNCH(I, BM_, BN_, BK_, WM_, WN_, D_)                                                       \
+#define BG_LAUNCH(I, BM_, BN_, BK_, WM_, WN_, D_, NS_)                                                  \
     if (!found && p.mfma == I && p.bm == BM_ && p.bn == BN_ && p.bk == BK_ && p.waves_m == WM_ &&      \
-        p.waves_n == WN_ && p.direct == D_) {                                                           \
+        p.waves_n == WN_ && p.direct == D_ && (p.stages == 0 || p.stages == NS_)) {                    \
         found = true;                                                                                    \
-        err = TileLauncher<D_>::template run<I, BM_, BN_, BK_, WM_, WN_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream); \
+        err = TileLauncher<D_>::template run<I, BM_, BN_, BK_, WM_, WN_, NS_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream); \
     }
     BG_GEMM_TILES(BG_LAUNCH)
 #undef BG_LAUNCH

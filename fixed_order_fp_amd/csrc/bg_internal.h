@@ -55,7 +55,8 @@ struct GemmPlan {
     bool out_bf16;   // rounding point target
     int bm, bn, bk;  // schedule
     int waves_m, waves_n;
-    int direct;      // 1: operand tiles copied global -> LDS directly
+    int direct;      // 1: operand tiles copied global -> LDS directly; 2: pipelined
+    int stages;      // k tiles in LDS (pipelined path)
     int group_m;     // tile rows per group of the workgroup walk
     bool atomic;     // free-order twin: splits added into a zeroed fp32 C with atomics
 };
@@ -94,6 +95,6 @@ hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, c
 
 // which tile shapes the GEMM kernel is instantiated for
 hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
-bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct);
+bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct, int stages);
 
 }  // namespace bg

@@ -97,10 +97,13 @@ typedef enum { BG_EPI_NONE = 0, BG_EPI_W8A8_POW2 = 1 } bg_epilogue;
 typedef struct {
     int32_t bm, bn, bk;       /* output tile and k-tile                    */
     int32_t waves_m, waves_n; /* wave grid inside a workgroup              */
-    int32_t load_path;        /* 0: global -> VGPR -> LDS; 1: global -> LDS */
+    int32_t load_path;        /* 0: global -> VGPR -> LDS; 1: global -> LDS;
+                                 2: global -> LDS, multi-stage pipeline (k
+                                 tiles of 32; 32x32x16 instruction only)   */
     int32_t group_m;          /* tile rows per group of the workgroup walk
-                                 (0 = 8)                                   */
-    int32_t combine_block;    /* reserved                                  */
+                                 (0 = 8, or every tile row for path 2)     */
+    int32_t stages;           /* k tiles held in LDS by path 2 (0 = the
+                                 tile's default)                           */
 } bg_gemm_schedule;
 
 /* GEMM descriptor ([T] 3.2.2 and 4).  Every field before `sched` is an order

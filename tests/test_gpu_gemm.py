@@ -19,6 +19,15 @@ SCHEDULES = {
                           dict(bm=256, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2, group_m=3),
                           dict(bm=256, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
                           dict(bm=128, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
+                          dict(bm=128, bn=64, bk=32, waves_m=2, waves_n=2, load_path=2),
+                          dict(bm=64, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
+                          dict(bm=64, bn=64, bk=32, waves_m=2, waves_n=2, load_path=2),
+                          dict(bm=32, bn=128, bk=32, waves_m=1, waves_n=4, load_path=2),
+                          dict(bm=32, bn=64, bk=32, waves_m=1, waves_n=2, load_path=2),
+                          dict(bm=32, bn=32, bk=32, waves_m=1, waves_n=1, load_path=2, group_m=2),
+                          dict(bm=32, bn=32, bk=32, waves_m=1, waves_n=1, load_path=2, stages=16),
+                          dict(bm=64, bn=64, bk=32, waves_m=2, waves_n=2, load_path=2, stages=12),
+                          dict(bm=128, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2, stages=8),
                           dict(bm=256, bn=256, bk=64, waves_m=2, waves_n=2, load_path=1),
                           dict(bm=256, bn=256, bk=64, waves_m=2, waves_n=4, load_path=1),
                           dict(bm=256, bn=128, bk=64, waves_m=2, waves_n=2, load_path=1),
