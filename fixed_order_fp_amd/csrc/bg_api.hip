@@ -399,12 +399,21 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
     const bg_gemm_schedule& s = d->sched;
     p.group_m = s.group_m;
     if (s.bm || s.bn || s.waves_m || s.waves_n) {
-        if (!bg::w8a8_has_tile(p.mfma, s.bm, s.bn, s.waves_m, s.waves_n))
-            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, waves) is not compiled in for W8A8");
+        const int path = s.load_path ? s.load_path : 1;
+        if (!bg::w8a8_has_tile(p.mfma, s.bm, s.bn, s.waves_m, s.waves_n, path, s.stages))
+            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, waves, load_path, stages) is not compiled in for W8A8");
         p.bm = s.bm, p.bn = s.bn, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
+        p.path = path, p.stages = s.stages;
+    } else if (p.mfma == BG_MFMA_I32_32X32X32_I8) {
+        // speed only: the pipelined kernel; 128x128 tiles where they give a
+        // workgroup per CU, otherwise deep-pipelined small tiles
+        const bool big = ((M + 127) / 128) * ((N + 127) / 128) >= 192;
+        p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
+        p.path = 2, p.stages = big ? 4 : 8;
     } else {
         const bool big = M >= 128 && N >= 128 && ((M + 127) / 128) * ((N + 127) / 128) >= 128;
         p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
+        p.path = 1, p.stages = 0;
     }
     if (M == 0 || N == 0) return BG_OK;
     if (!A || !W || !a_scale || !w_scale || !Y) return fail(BG_E_INVALID, "NULL tensor");

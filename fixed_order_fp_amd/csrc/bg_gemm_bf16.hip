@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "bg_internal.h"
+#include "bg_pipe.h"
 
 namespace bg {
 
@@ -225,25 +226,6 @@ __device__ __forceinline__ void lds_copy16(const void* src, u32x4* lds_dst)
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs in turn, so
-// consecutive ids land on different L2s; renumber them so that each XCD gets
-// one contiguous run of tiles, then walk that run GROUP_M tile-rows at a time
-// (column-major inside a group) so that neighbours share A rows and B columns.
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int group_m, int& tm, int& tn)
-{
-    const int T = tiles_m * tiles_n;
-    const int q = T / 8, r = T % 8;
-    const int x = b % 8, j = b / 8;
-    const int bb = x * q + (x < r ? x : r) + j;  // a bijection on [0, T)
-    const int per_group = group_m * tiles_n;
-    const int g = bb / per_group;
-    const int first_m = g * group_m;
-    const int gsize = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int in = bb - g * per_group;
-    tm = first_m + in % gsize;
-    tn = in / gsize;
-}
-
 // The same order as gemm_bf16_kernel, with the operand tiles copied from
 // global memory straight into LDS (global_load_lds_dwordx4: lane i of a wave
 // writes the 16 bytes it loads to LDS base + 16 i), so no VGPRs and no LDS
@@ -417,76 +399,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 //    consecutive columns of one row of C;
 //  * bf16 output is staged through LDS and written row by row, 16 bytes per
 //    lane with consecutive lanes on consecutive addresses.
-//
-// 16 bytes from global memory into LDS at byte address lds_addr + 16 * lane
-// (global_load_lds_dwordx4; M0 holds the LDS address and is restored).  It is
-// issued as inline assembly so that the compiler, which cannot place an LDS
-// DMA among its LDS reads, does not drain every read before each MFMA; the
-// copies are waited for with explicit vmcnt waits.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr)
-{
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(src), "s"(lds_addr)
-        : "memory");
-}
-
-// s_waitcnt vmcnt(N), other counters untouched
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// wait until at most `newer` turns of LOADS copies each are outstanding
-// (newer <= MAXN; a larger value waits for more than needed, never less)
-template <int LOADS, int MAXN>
-__device__ __forceinline__ void wait_turns(int newer)
-{
-    if constexpr (MAXN >= 1) {
-        if (newer >= MAXN) {
-            wait_vmcnt<MAXN * LOADS>();
-            return;
-        }
-        wait_turns<LOADS, MAXN - 1>(newer);
-    } else {
-        wait_vmcnt<0>();
-    }
-}
-
-// Staged bf16 C rows hold CHR 16-byte chunks; chunk ch of row m is stored at
-// position ch ^ (m & mask) inside its row (within the leading power of two of
-// chunks, and within the trailing eight), so that the writes of 16
-// consecutive rows to one column chunk land in distinct bank groups.
-template <int CHR>
-__device__ __forceinline__ int c_swizzle(int ch, int m)
-{
-    static_assert(CHR == 4 || CHR == 8 || CHR == 16 || CHR == 32 || CHR == 40,
-                  "staged row widths: 32, 64, 128, 256 or 320 columns");
-    if constexpr (CHR == 40) return ch < 32 ? ch ^ (m & 31) : ch ^ (m & 7);
-    else return ch ^ (m & (CHR - 1));
-}
-
-// LDS the pipelined kernel uses, and the waves per SIMD that leaves room for
-template <int BM, int BN, int NS, int OUT>
-struct PipeLds {
-    static constexpr int STAGE_BYTES = (BM + BN) * 64;  // k tile of 32 bf16 per row
-    static constexpr int PIPE = NS * STAGE_BYTES, EPI = OUT == 1 ? BM * BN * 2 : 0;
-    static constexpr int BYTES = PIPE > EPI ? PIPE : EPI;
-    static constexpr int WG_PER_CU = (160 * 1024) / BYTES;
-};
-template <int BM, int BN, int WM, int WN, int NS, int OUT>
-struct PipeOcc {
-    static constexpr int W = PipeLds<BM, BN, NS, OUT>::WG_PER_CU * WM * WN / 4;
-    static constexpr int WAVES_PER_EU = W < 1 ? 1 : W;
-};
+// The copies bypass the compiler (see dma16) and are waited for explicitly.
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32
 // split partial added into C with atomics (the free-order twin only)

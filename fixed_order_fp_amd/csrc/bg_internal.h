@@ -71,9 +71,11 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K,
 struct W8A8Plan {
     int mfma;  // BG_MFMA_I32_32X32X32_I8 | BG_MFMA_I32_16X16X64_I8
     int bm, bn, waves_m, waves_n, group_m;
+    int path;    // 1: direct-to-LDS double buffer; 2: pipelined (32x32x32 only)
+    int stages;  // k tiles in LDS (pipelined path; 0 = the tile's default)
 };
 
-bool w8a8_has_tile(int mfma, int bm, int bn, int waves_m, int waves_n);
+bool w8a8_has_tile(int mfma, int bm, int bn, int waves_m, int waves_n, int path, int stages);
 hipError_t launch_w8a8(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
                        const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
                        int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream);

@@ -8,11 +8,15 @@
 // No multiply-add is fused (built with -ffp-contract=off; the epilogue has no
 // add at all).
 //
-// Data path as in the bf16 direct kernel: 128-byte k tiles (128 int8) of A
-// and W copied global -> LDS with global_load_lds_dwordx4 under a row-XOR
-// swizzle, double-buffered; v_mfma_i32_32x32x32_i8 or v_mfma_i32_16x16x64_i8
+// Two data paths: the pipelined kernel (the default for the 32x32x32
+// instruction; see w8a8_pipe_kernel) and a double-buffered one: 128-byte k
+// tiles (128 int8) of A and W copied global -> LDS with global_load_lds_dwordx4
+// under a row-XOR swizzle; v_mfma_i32_32x32x32_i8 or v_mfma_i32_16x16x64_i8
 // with one 16-byte chunk per lane per instruction.
+#include <type_traits>
+
 #include "bg_internal.h"
+#include "bg_pipe.h"
 
 namespace bg {
 
@@ -62,21 +66,6 @@ __device__ __forceinline__ u32x4 load_chunk_i8(const int8_t* row_ptr, int64_t k,
         if (k + j < k_end) w[j / 4] |= (uint32_t)(uint8_t)row_ptr[k + j] << (8 * (j % 4));
     v[0] = w[0], v[1] = w[1], v[2] = w[2], v[3] = w[3];
     return v;
-}
-
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int group_m, int& tm, int& tn)
-{
-    const int T = tiles_m * tiles_n;
-    const int q = T / 8, r = T % 8;
-    const int x = b % 8, j = b / 8;
-    const int bb = x * q + (x < r ? x : r) + j;
-    const int per_group = group_m * tiles_n;
-    const int g = bb / per_group;
-    const int first_m = g * group_m;
-    const int gsize = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
-    const int in = bb - g * per_group;
-    tm = first_m + in % gsize;
-    tn = in / gsize;
 }
 
 template <int INSTR, int BM, int BN, int WM, int WN, bool ACC_OUT>
@@ -207,6 +196,228 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
             }
 }
 
+// The pipelined W8A8 kernel: the bf16 pipelined kernel's schedule (NS
+// stages of 64-byte k tiles copied straight to LDS, one barrier per turn
+// placed before the last k-step, MFMA operands swapped so that a lane holds 4
+// consecutive columns of one row) on v_mfma_i32_32x32x32_i8, whose int32 sum
+// is exact in any order.  The epilogue applies the fixed order above to 4
+// columns at a time and stages the bf16 tile in LDS for row-contiguous
+// 16-byte stores.  A short last k tile (K not a multiple of 64) is copied
+// through registers with zeros past K.
+template <int BM, int BN, int WM, int WN, int NS, bool ACC_OUT>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
+    PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU)))
+void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* __restrict__ W, int64_t ldw,
+                      const float* __restrict__ a_scale, const float* __restrict__ w_scale,
+                      uint16_t* __restrict__ Y, int64_t ldy, int32_t* __restrict__ acc_out, int64_t ld_acc,
+                      int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, int group_m)
+{
+    constexpr int PK = 64, PCPR = PK / kChunk, KS = PK / 32;  // k tile, chunks per row, k-steps
+    constexpr int NW = WM * WN, NT = 64 * NW;
+    constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+    constexpr int A_CH = BM * PCPR, B_CH = BN * PCPR;
+    constexpr int STAGE = A_CH + B_CH;
+    constexpr int SLOTS = STAGE / 64, ROUNDS = (SLOTS + NW - 1) / NW, EXTRA = SLOTS % NW;
+    constexpr int LOADS_HI = ROUNDS, LOADS_LO = EXTRA ? ROUNDS - 1 : ROUNDS;
+    constexpr int CHR = BN / 8;
+    constexpr int LDS_BYTES = PipeLds<BM, BN, NS, 1>::BYTES;
+    static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "tile rows must fill whole copy slots");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole MFMA blocks");
+    static_assert(NS >= 3 && LOADS_HI * (NS - 2) < 64, "stages: three at least, waits within vmcnt");
+    static_assert(KS == 2, "two k-steps per turn");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
+    __shared__ u32x4 lds[LDS_BYTES / 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int n_full = (int)(K / PK);
+    const int n_turns = (int)((K + PK - 1) / PK);
+    const bool hi = EXTRA == 0 || wave < EXTRA;
+
+    const int8_t* rows[ROUNDS];
+    int kcs[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; r++) {
+        const int s = r * NW + wave;
+        const int c = (s < SLOTS ? s : 0) * 64 + lane;
+        const bool is_a = c < A_CH;
+        const int row = is_a ? c / PCPR : (c - A_CH) / PCPR;
+        kcs[r] = (c % PCPR) ^ ((row >> 2) & 3);
+        int64_t g = (is_a ? m0 : n0) + row;
+        const int64_t lim = is_a ? M : N;
+        g = g < lim ? g : lim - 1;  // rows past M or N read a clamped row: never stored
+        rows[r] = is_a ? A + g * lda : W + g * ldw;
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)lds);
+
+    auto issue = [&](int turn) {
+        const int st = turn % NS;
+        const int64_t kb = (int64_t)turn * PK;
+#pragma unroll
+        for (int r = 0; r < ROUNDS; r++) {
+            const int s = r * NW + wave;
+            if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS) {
+                const int64_t k = kb + kcs[r] * kChunk;
+                if (turn < n_full)
+                    dma16(rows[r] + k, lds_base + (uint32_t)(st * STAGE + s * 64) * 16u);
+                else
+                    lds[st * STAGE + s * 64 + lane] = load_chunk_i8(rows[r], k, K);
+            }
+        }
+    };
+    auto dma_newer = [&](int after, int last) {
+        const int l = last < n_full - 1 ? last : n_full - 1;
+        return l > after ? l - after : 0;
+    };
+    auto wait_newer = [&](int newer, auto max_tag) {
+        constexpr int MAXN = decltype(max_tag)::value;
+        if (hi) wait_turns<LOADS_HI, MAXN>(newer);
+        else wait_turns<LOADS_LO, MAXN>(newer);
+    };
+
+    const int r_in = lane & 31, h = lane >> 5;
+    int a_off[KS], b_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        a_off[ks] = (wm * WTM + r_in) * PCPR + ((2 * ks + h) ^ ((r_in >> 2) & 3));
+        b_off[ks] = A_CH + (wn * WTN + r_in) * PCPR + ((2 * ks + h) ^ ((r_in >> 2) & 3));
+    }
+    auto rd = [&](int turn, int ks, i32x4* a, i32x4* b) {
+        const u32x4* base = lds + (turn % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < TM; i++) a[i] = __builtin_bit_cast(i32x4, base[a_off[ks] + i * 32 * PCPR]);
+#pragma unroll
+        for (int j = 0; j < TN; j++) b[j] = __builtin_bit_cast(i32x4, base[b_off[ks] + j * 32 * PCPR]);
+    };
+    i32x16 acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[j][i][e] = 0;
+    auto mm = [&](const i32x4* a, const i32x4* b) {
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j][i], 0, 0, 0);
+    };
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; s++)
+        if (s < n_turns) issue(s);
+    wait_newer(dma_newer(0, NS - 2), std::integral_constant<int, NS - 2>{});
+    __syncthreads();
+
+    i32x4 xa[2][TM], xb[2][TN];
+    rd(0, 0, xa[0], xb[0]);
+    auto turn = [&](int t, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        rd(t, 1, xa[1], xb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(xa[0], xb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FULL) {
+            if (hi) wait_vmcnt<LOADS_HI * (NS - 3)>();
+            else wait_vmcnt<LOADS_LO * (NS - 3)>();
+        } else {
+            const int last = t + NS - 2 < n_turns - 1 ? t + NS - 2 : n_turns - 1;
+            wait_newer(dma_newer(t + 1, last), std::integral_constant<int, NS - 3>{});
+        }
+        __builtin_amdgcn_s_barrier();
+        if constexpr (FULL) {
+            issue(t + NS - 1);
+        } else {
+            if (t + NS - 1 < n_turns) issue(t + NS - 1);
+        }
+        rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
+        __builtin_amdgcn_sched_barrier(0);
+        mm(xa[1], xb[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    const int n_steady = n_full - (NS - 1);
+    int t = 0;
+    for (; t < n_steady; t++) turn(t, std::true_type{});
+    for (; t < n_turns; t++) turn(t, std::false_type{});
+
+    // epilogue: block (j, i), element 4q+u of lane l is row m = wm*WTM + 32i +
+    // l%32, column n = wn*WTN + 32j + 8q + 4(l/32) + u
+    __syncthreads();  // every wave is done with the operand stages
+    unsigned char* cl = (unsigned char*)lds;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const int m = wm * WTM + i * 32 + r_in;
+        const int64_t gm = m0 + m;
+        const float as = a_scale[gm < M ? gm : M - 1];
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int n = wn * WTN + j * 32 + 8 * q;  // chunk n/8; lane half h takes bytes 8h..8h+7
+                const int64_t gn = n0 + n + 4 * h;
+                float y[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const float ws = w_scale[gn + u < N ? gn + u : N - 1];
+                    const float f = (float)acc[j][i][4 * q + u];  // v_cvt_f32_i32: round to nearest even
+                    const float tt = f * ws;                       // exact: a power of two
+                    y[u] = tt * as;                                // the one rounding
+                }
+                uint2 w;
+                w.x = bf16x2_rne(y[0], y[1]);
+                w.y = bf16x2_rne(y[2], y[3]);
+                *(uint2*)(cl + m * (BN * 2) + c_swizzle<CHR>(n / 8, m) * 16 + h * 8) = w;
+                if constexpr (ACC_OUT) {
+                    if (gm < M && gn < N) {
+                        int32_t* pa = acc_out + gm * ld_acc + gn;
+                        if (gn + 4 <= N) {
+                            i32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+                            *(i32x4*)pa = v;
+                        } else {
+                            for (int u = 0; u < 4 && gn + u < N; u++) pa[u] = acc[j][i][4 * q + u];
+                        }
+                    }
+                }
+            }
+    }
+    __syncthreads();
+    for (int c = tid; c < BM * CHR; c += NT) {
+        const int row = c / CHR, ch = c % CHR;
+        const int64_t gm = m0 + row, gn = n0 + ch * 8;
+        if (gm >= M || gn >= N) continue;
+        const u32x4 v = *(const u32x4*)(cl + row * (BN * 2) + c_swizzle<CHR>(ch, row) * 16);
+        if (gn + 8 <= N) {
+            *(u32x4*)(Y + gm * ldy + gn) = v;
+        } else {
+            for (int u = 0; u < 8 && gn + u < N; u++) Y[gm * ldy + gn + u] = (uint16_t)(v[u / 2] >> (16 * (u % 2)));
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_pipe(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                       const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
+                       int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream)
+{
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
+    dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
+    if (acc_out)
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, true>), grid, block, 0, stream, A, lda, W, ldw,
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+    else
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, false>), grid, block, 0, stream, A, lda, W, ldw,
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
 template <int INSTR, int BM, int BN, int WM, int WN>
 hipError_t launch(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
                   const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y, int64_t ldy,
@@ -228,30 +439,70 @@ hipError_t launch(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8
 
 using namespace w8a8_impl;
 
-#define BG_W8A8_TILES(X)                       \
-    X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2) \
-    X(BG_MFMA_I32_32X32X32_I8, 256, 128, 2, 2) \
-    X(BG_MFMA_I32_32X32X32_I8, 64, 64, 2, 2)   \
-    X(BG_MFMA_I32_16X16X64_I8, 128, 128, 2, 2) \
-    X(BG_MFMA_I32_16X16X64_I8, 64, 64, 2, 2)
+// (instruction, BM, BN, waves_m, waves_n, load path: 1 direct-to-LDS double
+// buffer, 2 pipelined, LDS stages of the pipelined path)
+#define BG_W8A8_TILES(X)                             \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 4) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 5) \
+    X(BG_MFMA_I32_32X32X32_I8, 256, 256, 2, 4, 2, 4) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 64, 2, 2, 2, 8)  \
+    X(BG_MFMA_I32_32X32X32_I8, 64, 64, 2, 2, 2, 8)   \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 1, 2) \
+    X(BG_MFMA_I32_32X32X32_I8, 256, 128, 2, 2, 1, 2) \
+    X(BG_MFMA_I32_32X32X32_I8, 64, 64, 2, 2, 1, 2)   \
+    X(BG_MFMA_I32_16X16X64_I8, 128, 128, 2, 2, 1, 2) \
+    X(BG_MFMA_I32_16X16X64_I8, 64, 64, 2, 2, 1, 2)
 
-bool w8a8_has_tile(int mfma, int bm, int bn, int waves_m, int waves_n)
+// stages == 0 takes the first compiled entry of the shape and path
+bool w8a8_has_tile(int mfma, int bm, int bn, int waves_m, int waves_n, int path, int stages)
 {
-#define BG_HAS(I, BM_, BN_, WM_, WN_) \
-    if (mfma == I && bm == BM_ && bn == BN_ && waves_m == WM_ && waves_n == WN_) return true;
+#define BG_HAS(I, BM_, BN_, WM_, WN_, P_, NS_)                                                                  \
+    if (mfma == I && bm == BM_ && bn == BN_ && waves_m == WM_ && waves_n == WN_ && path == P_ &&                  \
+        (stages == 0 || stages == NS_))                                                                          \
+        return true;
     BG_W8A8_TILES(BG_HAS)
 #undef BG_HAS
     return false;
 }
 
+// one launcher per load path (a kernel launched only from a discarded branch
+// would not get its host stub)
+template <int P>
+struct W8A8Launcher;
+template <>
+struct W8A8Launcher<1> {
+    template <int I, int BM, int BN, int WM, int WN, int NS>
+    static hipError_t run(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                          const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
+                          int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream)
+    {
+        return launch<I, BM, BN, WM, WN>(p, M, N, K, A, lda, W, ldw, a_scale, w_scale, Y, ldy, acc_out, ld_acc,
+                                         stream);
+    }
+};
+template <>
+struct W8A8Launcher<2> {
+    template <int I, int BM, int BN, int WM, int WN, int NS>
+    static hipError_t run(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                          const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
+                          int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream)
+    {
+        static_assert(I == BG_MFMA_I32_32X32X32_I8, "the pipelined path runs the 32x32x32 instruction");
+        return launch_pipe<BM, BN, WM, WN, NS>(p, M, N, K, A, lda, W, ldw, a_scale, w_scale, Y, ldy, acc_out,
+                                               ld_acc, stream);
+    }
+};
+
 hipError_t launch_w8a8(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
                        const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
                        int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream)
 {
-#define BG_LAUNCH(I, BM_, BN_, WM_, WN_)                                                                          \
-    if (p.mfma == I && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_)                          \
-        return launch<I, BM_, BN_, WM_, WN_>(p, M, N, K, A, lda, W, ldw, a_scale, w_scale, Y, ldy, acc_out, ld_acc, \
-                                             stream);
+#define BG_LAUNCH(I, BM_, BN_, WM_, WN_, P_, NS_)                                                              \
+    if (p.mfma == I && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_ && p.path == P_ &&   \
+        (p.stages == 0 || p.stages == NS_))                                                                    \
+        return W8A8Launcher<P_>::template run<I, BM_, BN_, WM_, WN_, NS_>(p, M, N, K, A, lda, W, ldw, a_scale, \
+                                                                         w_scale, Y, ldy, acc_out, ld_acc,     \
+                                                                         stream);
     BG_W8A8_TILES(BG_LAUNCH)
 #undef BG_LAUNCH
     return hipErrorInvalidValue;

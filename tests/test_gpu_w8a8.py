@@ -13,8 +13,15 @@ from gpu_util import from_dev_u16, print_case, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-TILES = [("I32_32X32X32_I8", 128, 128), ("I32_32X32X32_I8", 256, 128), ("I32_32X32X32_I8", 64, 64),
-         ("I32_16X16X64_I8", 128, 128), ("I32_16X16X64_I8", 64, 64)]
+# (instruction, bm, bn, waves_m, waves_n, load path, stages): path 2 is the
+# pipelined kernel, path 1 the double-buffered one
+TILES = [("I32_32X32X32_I8", 128, 128, 2, 2, 2, 4), ("I32_32X32X32_I8", 128, 128, 2, 2, 2, 5),
+         ("I32_32X32X32_I8", 256, 256, 2, 4, 2, 4), ("I32_32X32X32_I8", 128, 64, 2, 2, 2, 8),
+         ("I32_32X32X32_I8", 64, 64, 2, 2, 2, 8),
+         ("I32_32X32X32_I8", 128, 128, 2, 2, 1, 0), ("I32_32X32X32_I8", 256, 128, 2, 2, 1, 0),
+         ("I32_32X32X32_I8", 64, 64, 2, 2, 1, 0),
+         ("I32_16X16X64_I8", 128, 128, 2, 2, 1, 0), ("I32_16X16X64_I8", 64, 64, 2, 2, 1, 0)]
+TILE_IDS = [f"{t[0][4:13]}-{t[1]}x{t[2]}-w{t[3]}x{t[4]}-p{t[5]}-s{t[6]}" for t in TILES]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -33,7 +40,8 @@ def run_w8a8(a_q, w_q, a_scale, w_scale, instr="I32_32X32X32_I8", tile=None, wan
     import fixed_order_fp_amd as bg
     M, K = a_q.shape
     N = w_q.shape[0]
-    sched = {} if tile is None else dict(bm=tile[0], bn=tile[1], waves_m=2, waves_n=2)
+    sched = {} if tile is None else dict(bm=tile[0], bn=tile[1], waves_m=tile[2], waves_n=tile[3],
+                                         load_path=tile[4], stages=tile[5])
     d = bg.gemm_desc(dict(mfma=instr, a_type="int8", b_type="int8", acc_type="int32", out_type="bf16",
                           epilogue="W8A8_POW2", split_k=1, schedule=sched))
     kp = _pad(K, 16)
@@ -79,22 +87,23 @@ def test_full_workload_default_schedule():
     check(a_q, w_q, a_s, w_s)
 
 
-@pytest.mark.parametrize("instr,bm,bn", TILES)
-def test_full_workload_every_tile(instr, bm, bn):
+@pytest.mark.parametrize("tile", TILES, ids=TILE_IDS)
+def test_full_workload_every_tile(tile):
     a_q, w_q, a_s, w_s = synth.w8a8_input()
-    print_case("w8a8 full tile", instr, bm, bn)
-    check(a_q, w_q, a_s, w_s, instr=instr, tile=(bm, bn), want_acc=False)
+    print_case("w8a8 full tile", tile)
+    check(a_q, w_q, a_s, w_s, instr=tile[0], tile=tile[1:], want_acc=False)
 
 
-@pytest.mark.parametrize("instr,bm,bn", TILES)
+@pytest.mark.parametrize("tile", TILES, ids=TILE_IDS)
 @pytest.mark.parametrize("M,N,K", [(200, 136, 2128), (1, 8, 16), (37, 300, 1), (130, 129, 333), (257, 64, 4100)])
-def test_ragged(instr, bm, bn, M, N, K):
+def test_ragged(tile, M, N, K):
+    instr = tile[0]
     a_q, _ = synth.quantize_per_token(synth.f32_normal(1100 + K, (M, K)))
     w_q = synth.int8_uniform(2100 + K, (N, K))
     w_s = synth.pow2_scales(3100 + K, N)
     _, a_s = synth.quantize_per_token(synth.f32_normal(1100 + K, (M, K)))
-    print_case("w8a8 ragged", instr, bm, bn, M, N, K)
-    check(a_q, w_q, a_s, w_s, instr=instr, tile=(bm, bn))
+    print_case("w8a8 ragged", tile, M, N, K)
+    check(a_q, w_q, a_s, w_s, instr=instr, tile=tile[1:])
 
 
 def test_extreme_operands_max_k():
@@ -106,9 +115,10 @@ def test_extreme_operands_max_k():
     a_s = np.full(M, 1.0 / 127, dtype=np.float32)
     w_s = synth.pow2_scales(3200, N)
     print_case("w8a8 extreme", M, N, K)
-    Y, acc = run_w8a8(a_q, w_q, a_s, w_s, tile=(64, 64))
-    assert (acc == K * 16384).all()
-    check(a_q, w_q, a_s, w_s, tile=(64, 64))
+    for tile in ((64, 64, 2, 2, 1, 0), (64, 64, 2, 2, 2, 8), (128, 128, 2, 2, 2, 4)):
+        Y, acc = run_w8a8(a_q, w_q, a_s, w_s, tile=tile)
+        assert (acc == K * 16384).all(), tile
+        check(a_q, w_q, a_s, w_s, tile=tile)
 
 
 def test_zero_rows_and_signed_extremes():
@@ -127,9 +137,9 @@ def test_zero_rows_and_signed_extremes():
     a_s = np.ldexp(rng.random(M).astype(np.float32) + 0.5, -7).astype(np.float32)
     a_s[0] = 1.0
     w_s = synth.pow2_scales(3300, N)
-    for instr, bm, bn in TILES:
-        print_case("w8a8 extremes", instr, bm, bn)
-        check(a_q, w_q, a_s, w_s, instr=instr, tile=(bm, bn))
+    for tile in TILES:
+        print_case("w8a8 extremes", tile)
+        check(a_q, w_q, a_s, w_s, instr=tile[0], tile=tile[1:])
 
 
 def test_batch_invariance():
