@@ -450,6 +450,11 @@ static bg_status reduce_plan(const bg_reduce_desc* d, int64_t rows, int64_t cols
     if (p.axis == BG_AXIS_ROW) {
         n_blocks = bg::reduce_row_blocks(cols);
         if (n_blocks > 64) return fail(BG_E_UNSUPPORTED, "a row longer than 64 * 8192 elements is not built");
+    } else if (d->sched.leaves_per_wg == 256) {
+        // one pass, a workgroup per column strip over every row (rows <= 8192)
+        if ((rows + 31) / 32 > 256) return fail(BG_E_UNSUPPORTED, "the one-pass column path holds 256 leaves");
+        p.col_full = true;
+        n_blocks = 1;
     } else {
         // speed only (any aligned run of leaves is an exact subtree): the
         // fewest leaves per workgroup that keep the block roots within 64
@@ -461,7 +466,7 @@ static bg_status reduce_plan(const bg_reduce_desc* d, int64_t rows, int64_t cols
         p.leaves_per_wg = lpw;
         if (p.leaves_per_wg != 4 && p.leaves_per_wg != 8 && p.leaves_per_wg != 16 && p.leaves_per_wg != 32)
             return fail(BG_E_UNSUPPORTED, "leaves_per_wg must be 4, 8, 16 or 32");
-        const int cpw = d->sched.cols_per_wg ? d->sched.cols_per_wg : (p.bf16 ? 512 : 256);
+        const int cpw = d->sched.cols_per_wg ? d->sched.cols_per_wg : 256;
         p.cols_per_lane = cpw / 64;
         if (cpw % 64 || (p.cols_per_lane != 4 && (p.cols_per_lane != 8 || !p.bf16)))
             return fail(BG_E_UNSUPPORTED, "cols_per_wg must be 256 (or 512 for bf16 input)");

@@ -86,6 +86,7 @@ struct ReducePlan {
     bool fused;        // q = fma(x, x, q)
     int leaves_per_wg; // column axis: leaves one workgroup folds (4, 8, 16, 32)
     int cols_per_lane; // column axis, bf16 input: 4 or 8
+    bool col_full;     // column axis: one pass, a workgroup per strip over every row
 };
 
 int64_t reduce_row_blocks(int64_t cols);

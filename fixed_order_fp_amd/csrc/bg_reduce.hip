@@ -219,10 +219,13 @@ __global__ __launch_bounds__(256) void reduce_blocks_kernel(const float* __restr
     const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= n_out) return;
     float vs[NB], vq[NB];
+    // every load is issued (past the last block it re-reads a valid one, never
+    // used) so that all of them are in flight at once
 #pragma unroll
     for (int b = 0; b < NB; b++) {
-        vs[b] = b < n_blocks ? ws[(o * stride_out + b * stride_blk) * 2] : 0.0f;
-        vq[b] = b < n_blocks ? ws[(o * stride_out + b * stride_blk) * 2 + 1] : 0.0f;
+        const int64_t blk = b < n_blocks ? b : n_blocks - 1;
+        vs[b] = ws[(o * stride_out + blk * stride_blk) * 2];
+        vq[b] = ws[(o * stride_out + blk * stride_blk) * 2 + 1];
     }
     const float rs = tree_upto<NB>(vs, n_blocks), rq = tree_upto<NB>(vq, n_blocks);
     if (out_sum) out_sum[o] = rs;
@@ -242,6 +245,68 @@ hipError_t launch_blocks(const float* ws, int64_t n_out, int nb, int64_t stride_
     else
         hipLaunchKernelGGL(reduce_blocks_kernel<64>, grid, block, 0, stream, ws, n_out, nb, stride_out, stride_blk,
                            out_sum, out_sq);
+    return hipGetLastError();
+}
+
+// Upper tree levels of the column axis: roots ws[blk][col] (sum, sumsq
+// interleaved).  A workgroup of 4 waves takes 64 adjacent columns; wave p
+// folds the aligned run of block roots [p NBP, (p+1) NBP) of each column (an
+// exact subtree: one load per block covers 64 adjacent columns), and the four
+// run roots are paired through LDS as the tree's top two levels.
+template <int NBP>
+__global__ __launch_bounds__(256) void reduce_col_blocks_kernel(const float* __restrict__ ws, int64_t cols,
+                                                                int n_blocks, float* __restrict__ out_sum,
+                                                                float* __restrict__ out_sq)
+{
+    __shared__ float part[2][4][64];
+    const int lane = threadIdx.x & 63;
+    const int p = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+    const int first = p * NBP;
+    const int n = n_blocks - first < NBP ? (n_blocks - first > 0 ? n_blocks - first : 0) : NBP;
+    float vs[NBP], vq[NBP];
+    // every load is issued (past the last block or column it re-reads a valid
+    // one, never used) so that all of them are in flight at once
+    const int64_t c = col < cols ? col : cols - 1;
+#pragma unroll
+    for (int b = 0; b < NBP; b++) vs[b] = 0.0f, vq[b] = 0.0f;
+    if (out_sum) {
+#pragma unroll
+        for (int b = 0; b < NBP; b++) {
+            const int blk = first + b < n_blocks ? first + b : n_blocks - 1;
+            vs[b] = ws[(c + (int64_t)blk * cols) * 2];
+        }
+    }
+    if (out_sq) {
+#pragma unroll
+        for (int b = 0; b < NBP; b++) {
+            const int blk = first + b < n_blocks ? first + b : n_blocks - 1;
+            vq[b] = ws[(c + (int64_t)blk * cols) * 2 + 1];
+        }
+    }
+    part[0][p][lane] = n ? tree_upto<NBP>(vs, n) : 0.0f;
+    part[1][p][lane] = n ? tree_upto<NBP>(vq, n) : 0.0f;
+    __syncthreads();
+    if (p == 0 && col < cols) {
+        const int n_parts = (n_blocks + NBP - 1) / NBP;
+        float rs[4], rq[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) rs[k] = part[0][k][lane], rq[k] = part[1][k][lane];
+        if (out_sum) out_sum[col] = tree_upto<4>(rs, n_parts);
+        if (out_sq) out_sq[col] = tree_upto<4>(rq, n_parts);
+    }
+}
+
+hipError_t launch_col_blocks(const float* ws, int64_t cols, int nb, float* out_sum, float* out_sq,
+                             hipStream_t stream)
+{
+    dim3 grid((unsigned)((cols + 63) / 64)), block(256);
+    if (nb <= 4)
+        hipLaunchKernelGGL(reduce_col_blocks_kernel<1>, grid, block, 0, stream, ws, cols, nb, out_sum, out_sq);
+    else if (nb <= 16)
+        hipLaunchKernelGGL(reduce_col_blocks_kernel<4>, grid, block, 0, stream, ws, cols, nb, out_sum, out_sq);
+    else
+        hipLaunchKernelGGL(reduce_col_blocks_kernel<16>, grid, block, 0, stream, ws, cols, nb, out_sum, out_sq);
     return hipGetLastError();
 }
 
@@ -369,6 +434,155 @@ __global__ __launch_bounds__(256) void reduce_col_kernel(const T* __restrict__ X
     }
 }
 
+// ---- column axis, one pass ----------------------------------------------------
+// For up to 256 leaves per column (rows <= 8192) one workgroup owns a strip
+// of 4 * CPL adjacent columns over every row, so no workspace and no second
+// kernel are needed.  A lane covers 16 bytes of a row (CPL columns); the 4
+// lanes of a quad cover the strip, and quad k of wave w folds the LPQ leaves
+// starting at leaf LPQ (16 w + k), each in row order with its 32 rows loaded at
+// once (one 64-byte row segment per quad per load instruction); a quad's two
+// leaves are its node of tree level 1.  The tree then runs as shuffles at
+// lane distances 4, 8, 16, 32 and through LDS over the wave nodes.  LPQ = 2
+// for bf16 (8 columns per lane: 512 threads, a leaf's rows fit in registers),
+// 1 for fp32 (1024 threads).  The two strips that share a 128-byte line are
+// handed to workgroups on one XCD (workgroup b runs on XCD b % 8), so one L2
+// fetches the line for both.
+template <typename T, bool FUSED>
+struct ColFull {
+    static constexpr int CPL = 16 / (int)sizeof(T);
+    static constexpr int SW = 4 * CPL;              // strip width in columns
+    static constexpr int LPQ = CPL == 8 ? 2 : 1;    // leaves per quad
+    static constexpr int NW = 16 / LPQ;             // waves: 16 * LPQ * NW = 256 leaves
+    static constexpr int NT = 64 * NW;
+};
+
+template <typename T, int CPL, bool FUSED>
+__device__ __forceinline__ void fold_leaf_rows(const T* base, int64_t ldx, int n, int64_t col0, int64_t cols,
+                                               float* s, float* q)
+{
+    if (n == kLeaf && col0 + CPL <= cols) {
+        // the leaf's 32 row pieces stay packed (16 bytes each) until folded
+        u32x4 raw[kLeaf];
+#pragma unroll
+        for (int i = 0; i < kLeaf; i++) raw[i] = *(const u32x4*)(base + i * ldx);
+        auto elem = [&](int i, int c) {
+            if constexpr (std::is_same<T, float>::value) return __uint_as_float(raw[i][c]);
+            else return bf16_lane(raw[i], c);
+        };
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+            s[c] = elem(0, c);
+            q[c] = s[c] * s[c];
+        }
+#pragma unroll
+        for (int i = 1; i < kLeaf; i++)
+#pragma unroll
+            for (int c = 0; c < CPL; c++) fold_step<FUSED>(elem(i, c), s[c], q[c]);
+    } else {
+        // a short leaf or the ragged right edge, element by element
+        for (int i = 0; i < n; i++) {
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                const float xe = (col0 + c < cols) ? load_elem<T>(base + i * ldx + c) : 0.0f;
+                if (i == 0) {
+                    s[c] = xe;
+                    q[c] = xe * xe;
+                } else {
+                    fold_step<FUSED>(xe, s[c], q[c]);
+                }
+            }
+        }
+    }
+}
+
+template <typename T, bool FUSED>
+__global__ __launch_bounds__((ColFull<T, FUSED>::NT))
+__attribute__((amdgpu_waves_per_eu(ColFull<T, FUSED>::NW / 4, ColFull<T, FUSED>::NW / 4))) void reduce_col_full_kernel(
+    const T* __restrict__ X, int64_t ldx, int64_t rows, int64_t cols, float* __restrict__ out_sum,
+    float* __restrict__ out_sq)
+{
+    typedef ColFull<T, FUSED> P;
+    constexpr int CPL = P::CPL, SW = P::SW, LPQ = P::LPQ, NW = P::NW;
+    __shared__ float part[2][NW][SW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // strip of this workgroup: XCD x gets one contiguous run of strips
+    const int n_strips = (int)((cols + SW - 1) / SW);
+    const int b = blockIdx.x;
+    const int qq = n_strips / 8, rr = n_strips % 8, x = b % 8, j = b / 8;
+    const int strip = x * qq + (x < rr ? x : rr) + j;
+    const int64_t col0 = (int64_t)strip * SW + (lane & 3) * CPL;
+    const int slot = wave * 16 + (lane >> 2);
+    const int n_leaf = (int)((rows + kLeaf - 1) / kLeaf);
+
+    float s[CPL], q[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; c++) s[c] = 0.0f, q[c] = 0.0f;
+#pragma unroll
+    for (int l = 0; l < LPQ; l++) {
+        const int leaf = slot * LPQ + l;
+        if (leaf < n_leaf) {
+            const int64_t r0 = (int64_t)leaf * kLeaf;
+            const int n = (int)((rows - r0) < kLeaf ? (rows - r0) : kLeaf);
+            float ls[CPL], lq[CPL];
+            fold_leaf_rows<T, CPL, FUSED>(X + r0 * ldx + col0, ldx, n, col0, cols, ls, lq);
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                if (l == 0) {
+                    s[c] = ls[c];
+                    q[c] = lq[c];
+                } else {  // tree level 1 inside the quad: (leaf 2k) + (leaf 2k+1)
+                    s[c] = s[c] + ls[c];
+                    q[c] = q[c] + lq[c];
+                }
+            }
+        }
+    }
+    // quad-node distances 1, 2, 4, 8 inside the wave (the right node is 4d
+    // lanes up); a node exists when its first leaf does
+#pragma unroll
+    for (int d = 1; d <= 8; d <<= 1) {
+        const bool take = (slot & (2 * d - 1)) == 0 && (slot + d) * LPQ < n_leaf;
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+            const float os = __shfl_down(s[c], 4 * d, 64);
+            const float oq = __shfl_down(q[c], 4 * d, 64);
+            if (take) {
+                s[c] = s[c] + os;
+                q[c] = q[c] + oq;
+            }
+        }
+    }
+    if (lane < 4) {
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+            part[0][wave][lane * CPL + c] = s[c];
+            part[1][wave][lane * CPL + c] = q[c];
+        }
+    }
+    __syncthreads();
+    // the wave nodes: node w starts at leaf 16 LPQ w
+    if (threadIdx.x < SW) {
+        const int c = threadIdx.x;
+        const int64_t col = (int64_t)strip * SW + c;
+        float vs[NW], vq[NW];
+#pragma unroll
+        for (int w = 0; w < NW; w++) vs[w] = part[0][w][c], vq[w] = part[1][w][c];
+#pragma unroll
+        for (int d = 1; d < NW; d <<= 1)
+#pragma unroll
+            for (int w = 0; w + d < NW; w += 2 * d)
+                if (16 * LPQ * (w + d) < n_leaf) {
+                    vs[w] = vs[w] + vs[w + d];
+                    vq[w] = vq[w] + vq[w + d];
+                }
+        if (col < cols) {
+            if (out_sum) out_sum[col] = vs[0];
+            if (out_sq) out_sq[col] = vq[0];
+        }
+    }
+}
+
 // ---- free-order twins (bench only) --------------------------------------------
 // Row: coalesced strided lanes (lane l sums elements l*4.., every 1024th
 // float4 of the row), a count-down butterfly, an LDS sum over the waves.
@@ -467,6 +681,27 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
         if (e != hipSuccess || nb == 1) return e;
         return launch_blocks(ws, rows, nb, (int64_t)nb, (int64_t)1, out_sum, out_sq, stream);
     }
+    if (p.col_full) {
+        const int sw = p.bf16 ? ColFull<uint16_t, true>::SW : ColFull<float, true>::SW;
+        const int nt = p.bf16 ? ColFull<uint16_t, true>::NT : ColFull<float, true>::NT;
+        dim3 grid((unsigned)((cols + sw - 1) / sw)), block(nt);
+        if (p.bf16) {
+            if (p.fused)
+                hipLaunchKernelGGL((reduce_col_full_kernel<uint16_t, true>), grid, block, 0, stream, (const uint16_t*)X,
+                                   ldx, rows, cols, out_sum, out_sq);
+            else
+                hipLaunchKernelGGL((reduce_col_full_kernel<uint16_t, false>), grid, block, 0, stream, (const uint16_t*)X,
+                                   ldx, rows, cols, out_sum, out_sq);
+        } else {
+            if (p.fused)
+                hipLaunchKernelGGL((reduce_col_full_kernel<float, true>), grid, block, 0, stream, (const float*)X, ldx,
+                                   rows, cols, out_sum, out_sq);
+            else
+                hipLaunchKernelGGL((reduce_col_full_kernel<float, false>), grid, block, 0, stream, (const float*)X, ldx,
+                                   rows, cols, out_sum, out_sq);
+        }
+        return hipGetLastError();
+    }
     const int cpl = p.bf16 ? p.cols_per_lane : 4;
     const int lpw = p.leaves_per_wg;
     const int nb = (int)reduce_col_blocks(rows, lpw);
@@ -489,7 +724,7 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
     if (!done) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nb == 1) return e;
-    return launch_blocks(ws, cols, nb, (int64_t)1, cols, out_sum, out_sq, stream);
+    return launch_col_blocks(ws, cols, nb, out_sum, out_sq, stream);
 }
 
 hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, const void* X, int64_t ldx,

@@ -143,9 +143,11 @@ typedef enum { BG_TREE_BALANCED = 0 } bg_tree;
 
 typedef struct {
     int32_t leaves_per_wg;  /* column axis: leaves one workgroup folds: 4, 8, 16
-                               or 32 (0: the fewest keeping <= 64 block roots) */
+                               or 32 (0: the fewest keeping <= 64 block roots);
+                               256: one pass, a workgroup per narrow column
+                               strip over every row (rows <= 8192)          */
     int32_t cols_per_wg;    /* column axis: columns one workgroup covers: 256,
-                               or 512 for bf16 (0: 16 bytes per lane)          */
+                               or 512 for bf16 (0: 256)                        */
     int32_t reserved0, reserved1;
 } bg_reduce_schedule;
 

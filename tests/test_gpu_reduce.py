@@ -102,6 +102,28 @@ def test_col_ragged(in_type, rows, ld, cols, lpw):
     assert same(s, rs) and same(q, rq)
 
 
+@pytest.mark.parametrize("in_type", ["fp32", "bf16"])
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("rows,ld,cols", [(1000, 304, 300), (8192, 256, 256), (33, 8, 5), (4096 + 32 * 3 + 7, 520, 513),
+                                          (32, 256, 256), (8192, 4104, 4100), (8191, 40, 33), (1, 16, 3),
+                                          (8193, 64, 64)])
+def test_col_ragged_default_and_one_pass(in_type, fused, rows, ld, cols):
+    """The default column path (two kernels) and the one-pass path (a
+    workgroup per column strip over every row, rows <= 8192): short last
+    leaves, odd leaf counts, ragged strips, a single row."""
+    print_case("col_ragged_default", in_type, fused, rows, cols)
+    if in_type == "fp32":
+        X = synth.f32_spread(199 + rows, (rows, ld), -12, 12)
+    else:
+        X = synth.bf16_spread(199 + rows, (rows, ld), -12, 12)
+    rs, rq = oracle_reduce(X, "col", in_type, fused, cols=cols)
+    s, q = run_reduce(X, "col", in_type, fused, cols=cols)
+    assert same(s, rs) and same(q, rq)
+    if rows <= 8192:
+        s, q = run_reduce(X, "col", in_type, fused, cols=cols, schedule={"leaves_per_wg": 256})
+        assert same(s, rs) and same(q, rq)
+
+
 def test_ops_write_only_what_they_ask_for():
     X = synth.f32_normal(5, (16, 8192))
     s, q = run_reduce(X, "row", "fp32", op="sum")
