@@ -25,7 +25,7 @@ The same JSON line also carries:
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--no-cpu-baseline] [--no-extra]
        [--only-headline] [--copy-calibration]
-       python bench.py --summarize-trace <rocprofv3 kernel_trace.csv>
+       python bench.py --summarize-trace <rocprofv3 kernel_trace.csv> [timed steps, 50]
 """
 import argparse
 import json
@@ -173,7 +173,7 @@ def free_twin_us(g, args, torch):
         fn = lambda: g.bg.bench_gemm_bf16_free(g.dA, g.dB, dF, split_k)  # noqa: E731
         t, _ = time_steps(fn, args.steps, args.warmup, torch)
         tg = graph_time(fn, args.steps, torch)
-        if best is None or tg < best[1]:
+        if best is None or tg * 1e3 < best[1]:
             best = (t * 1e3, tg * 1e3, "none" if split_k == 1 else "auto (atomic)")
     return best
 
@@ -308,24 +308,31 @@ def reduce_extras(args, torch, bg, synth):
     return out
 
 
-def summarize_trace(path):
+def summarize_trace(path, tail):
     """Markdown table of a rocprofv3 kernel-trace CSV grouped by kernel and grid
     size (one workload per grid), so a kernel that serves several workloads
-    gets one row per workload."""
+    gets one row per workload.  The last column averages the final `tail`
+    dispatches of a row in launch order: for a workload the bench times last
+    with `tail` steps, those are its timed launches (the warm-up ones, some at
+    a lower clock, fall out)."""
     import csv
     import statistics
     groups = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             grid = r.get("Grid_Size") or r.get("Grid_Size_X")
-            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-            groups.setdefault((r["Kernel_Name"], grid, r.get("Workgroup_Size_X", "")), []).append(dur)
-    print("| kernel | grid (threads) | block | calls | mean us | median us | min us |")
-    print("|---|---|---|---|---|---|---|")
-    for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            start = int(r["Start_Timestamp"])
+            dur = int(r["End_Timestamp"]) - start
+            groups.setdefault((r["Kernel_Name"], grid, r.get("Workgroup_Size_X", "")), []).append((start, dur))
+    print(f"| kernel | grid (threads) | block | calls | mean us | median us | min us | mean of last {tail} us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (name, grid, wg), sv in sorted(groups.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        sv.sort()
+        v = [d for _, d in sv]
         short = name.split("(")[0].replace("void ", "")
+        last = f"{statistics.mean(v[-tail:]) / 1e3:.2f}" if len(v) >= tail else "-"
         print(f"| `{short}` | {grid} | {wg} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | "
-              f"{statistics.median(v) / 1e3:.2f} | {min(v) / 1e3:.2f} |")
+              f"{statistics.median(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | {last} |")
 
 
 def kernel_source_digest():
@@ -357,8 +364,8 @@ def stored_traffic():
 
 
 def main():
-    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
-        summarize_trace(sys.argv[2])
+    if len(sys.argv) in (3, 4) and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2], int(sys.argv[3]) if len(sys.argv) == 4 else 50)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

@@ -726,9 +726,9 @@ struct TileLauncher<2> {
     {
         static_assert(INSTR == BG_MFMA_F32_32X32X16_BF16 && BK == 32, "the pipelined path: 32x32x16, k tiles of 32");
         const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-        // default walk: down whole tile columns (each XCD's run of tiles then
-        // shares B panels and streams A; measured best on MI355X)
-        const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
+        const int wg_per_cu = p.out_bf16 && p.S == 1 && !p.atomic ? PipeLds<BM, BN, NS, 1>::WG_PER_CU
+                                                                    : PipeLds<BM, BN, NS, 0>::WG_PER_CU;
+        const int group_m = p.group_m > 0 ? p.group_m : walk_group_m(tiles_m, tiles_n, BM, BN, wg_per_cu);
         dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.S), block(64 * WM * WN);
         if (p.atomic)  // free-order twin only
             hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 3>), grid, block, 0, stream, A, lda, B, ldb,

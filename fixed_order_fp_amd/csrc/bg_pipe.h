@@ -27,6 +27,20 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int gro
     tn = in / gsize;
 }
 
+// Default group height of that walk (host side).  One XCD (32 CUs on gfx950)
+// runs c = 32 * wg_per_cu of its tiles at a time, about gm tile rows by c / gm
+// tile columns, and its L2 fetches gm * bm rows of A plus (c / gm) * bn rows
+// of B for them; gm = sqrt(c * bn / bm) makes that smallest.
+inline int walk_group_m(int tiles_m, int tiles_n, int bm, int bn, int wg_per_cu)
+{
+    const long long per_xcd = ((long long)tiles_m * tiles_n + 7) / 8;
+    long long c = 32LL * (wg_per_cu < 1 ? 1 : wg_per_cu);
+    if (c > per_xcd) c = per_xcd;
+    int g = (int)(__builtin_sqrt((double)c * bn / bm) + 0.5);
+    if (g > tiles_m) g = tiles_m;
+    return g < 1 ? 1 : g;
+}
+
 // 16 bytes from global memory into LDS at byte address lds_addr + 16 * lane
 // (global_load_lds_dwordx4; M0 holds the LDS address and is restored).  It is
 // issued as inline assembly so that the compiler, which cannot place an LDS

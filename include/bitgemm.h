@@ -101,7 +101,9 @@ typedef struct {
                                  2: global -> LDS, multi-stage pipeline (k
                                  tiles of 32; 32x32x16 instruction only)   */
     int32_t group_m;          /* tile rows per group of the workgroup walk
-                                 (0 = 8, or every tile row for path 2)     */
+                                 (0 = 8; for path 2, the height that makes
+                                 each XCD's concurrent tiles fetch the
+                                 fewest A and B rows)                      */
     int32_t stages;           /* k tiles held in LDS by path 2 (0 = the
                                  tile's default)                           */
 } bg_gemm_schedule;
