@@ -5,7 +5,11 @@ The headline line times the order-fixed bf16 GEMM C = A B^T of the
 batch-invariance sweep at its largest batch (M=4000, N=9728, K=2560, one
 descriptor: 32x32x16 bf16 MFMA, split-K 1, bf16 output rounded once), with the
 inputs resident in HBM.  A step is one call of that GEMM.  Before timing, a
-sample of outputs is checked bit for bit against the oracle.
+sample of outputs is checked bit for bit against the oracle.  Every timed
+workload rotates its calls over identical copies of its inputs totalling more
+than the 256 MB MALL, so that no call finds its inputs left in that cache by
+the previous ones ("inputs" says how many copies); "hot_*" fields time the
+same calls on one copy.
 
 The same JSON line also carries:
   roofline      the GEMM kernel's achieved TFLOP/s (algorithmic 2*M*N*K per
@@ -13,8 +17,9 @@ The same JSON line also carries:
                 stream) against the dense bf16 MFMA peak;
   cpu_baseline  the oracle timed on a bounded sample of the same outputs on
                 the host cores;
-  free_order    the free-order twin of the same GEMM (split-K by CU count,
-                fp32 atomics) and the time ratio fixed / free;
+  free_order    the free-order twin of the same GEMM (the same kernels with
+                fp32 output, no split or atomic split-K by CU count,
+                whichever is faster) and the time ratio fixed / free;
   extra         the other workloads (smaller batches, the split-K sweep, the
                 small split-K GEMM, W8A8, the row and column reductions),
                 each parity-checked and timed the same way, with its
@@ -47,6 +52,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Inputs are rotated over copies totalling more than the 256 MB MALL, so that
+# a call does not find the inputs of the previous calls still cached there.
+ROTATE_BYTES = 320 << 20
+
+
+class Rotation:
+    """Round-robin over identical copies of a call's input tensors (about
+    ROTATE_BYTES in all; one set when the inputs alone exceed it)."""
+
+    def __init__(self, tensors):
+        nbytes = sum(t.numel() * t.element_size() for t in tensors)
+        self.n = max(1, min(32, -(-ROTATE_BYTES // max(1, nbytes))))
+        self.sets = [list(tensors)] + [[t.clone() for t in tensors] for _ in range(self.n - 1)]
+        self.mb = self.n * nbytes / 1e6
+        self.i = 0
+
+    def next(self):
+        cur = self.sets[self.i % self.n]
+        self.i += 1
+        return cur
+
+    def note(self):
+        return f"inputs rotated over {self.n} copies ({self.mb:.0f} MB)" if self.n > 1 else \
+            f"inputs {self.mb:.0f} MB, larger than the MALL"
+
+
 class Gemm:
     """One order-fixed GEMM workload resident on the GPU."""
 
@@ -65,9 +96,16 @@ class Gemm:
                               device="cuda")
         nws = bg.gemm_workspace_bytes(self.desc, self.M, self.N, self.K)
         self.ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        self.rot = Rotation([self.dA, self.dB])
 
     def run(self):
+        """One call on the first copy of the inputs."""
         self.bg.gemm_bf16(self.desc, self.dA, self.dB, self.dC, self.ws)
+
+    def run_rot(self):
+        """One call on the next copy of the inputs."""
+        A, B = self.rot.next()
+        self.bg.gemm_bf16(self.desc, A, B, self.dC, self.ws)
 
     def flops(self):
         return 2.0 * self.M * self.N * self.K
@@ -170,7 +208,9 @@ def free_twin_us(g, args, torch):
     dF = torch.empty((g.M, g.N), dtype=torch.float32, device="cuda")
     best = None
     for split_k in (1, 0):
-        fn = lambda: g.bg.bench_gemm_bf16_free(g.dA, g.dB, dF, split_k)  # noqa: E731
+        def fn(split_k=split_k):
+            A, B = g.rot.next()
+            g.bg.bench_gemm_bf16_free(A, B, dF, split_k)
         t, _ = time_steps(fn, args.steps, args.warmup, torch)
         tg = graph_time(fn, args.steps, torch)
         if best is None or tg * 1e3 < best[1]:
@@ -186,14 +226,18 @@ def gemm_extras(X, W, args, torch, bg, synth):
         g = Gemm(f"gemm_bf16 M={M}", X[:M].copy(), W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"},
                  torch, bg)
         p = g.parity(128)
-        t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-        tg = graph_time(g.run, args.steps, torch)
+        t, _ = time_steps(g.run_rot, args.steps, args.warmup, torch)
+        tg = graph_time(g.run_rot, args.steps, torch)
+        tg_hot = graph_time(g.run, args.steps, torch)
         free, free_g, free_split = free_twin_us(g, args, torch)
         out[f"batch_sweep_M{M}"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
                                     "TFLOP/s": round(g.flops() / tg / 1e9, 2),
-                                    "GB/s": round(g.bytes() / tg / 1e6, 1), "free_us": round(free, 2),
+                                    "GB/s": round(g.bytes() / tg / 1e6, 1),
+                                    "frac_hbm": round(g.bytes() / tg / 1e6 / PEAK_HBM_GBS, 4),
+                                    "hot_graph_us": round(tg_hot * 1e3, 2), "free_us": round(free, 2),
                                     "free_graph_us": round(free_g, 2), "free_split": free_split,
-                                    "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p}
+                                    "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p,
+                                    "inputs": g.rot.note()}
         log(f"bench: M={M}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A4, W4 = synth.gemm_splitk_sweep()
     free = None
@@ -210,13 +254,16 @@ def gemm_extras(X, W, args, torch, bg, synth):
         diff32 = int((cur.view(torch.int32) != base.view(torch.int32)).sum().item())
         diff16 = int((cur.to(torch.bfloat16).view(torch.int16) != base.to(torch.bfloat16).view(torch.int16))
                      .sum().item())
-        t, _ = time_steps(g.run, args.steps, args.warmup, torch)
-        tg = graph_time(g.run, args.steps, torch)
+        t, _ = time_steps(g.run_rot, args.steps, args.warmup, torch)
+        tg = graph_time(g.run_rot, args.steps, torch)
+        tg_hot = graph_time(g.run, args.steps, torch)
         if free is None:
             free, free_g, free_split = free_twin_us(g, args, torch)
         out[f"splitk_S{S}"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
                                "TFLOP/s": round(g.flops() / tg / 1e9, 2),
-                               "GB/s": round(g.bytes() / tg / 1e6, 1), "free_us": round(free, 2),
+                               "GB/s": round(g.bytes() / tg / 1e6, 1),
+                               "hot_graph_us": round(tg_hot * 1e3, 2), "inputs": g.rot.note(),
+                               "free_us": round(free, 2),
                                "free_graph_us": round(free_g, 2), "free_split": free_split,
                                "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p,
                                "outputs_differing_from_S1": {"fp32": diff32, "after_bf16_rounding": diff16,
@@ -251,16 +298,23 @@ def w8a8_extra(args, torch, bg, synth):
     Yo, acco = oracle.w8a8_pow2(a_q, w_q, a_s, w_s)
     par = {"checked": int(M * N), "acc_mismatches": int(np.sum(dacc.cpu().numpy() != acco)),
            "y_mismatches": int(np.sum(dY.cpu().numpy().view(np.uint16) != Yo))}
-    fn = lambda: bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY)  # noqa: E731
+    rot = Rotation([dA, dW, sa, sw])
+
+    def fn():
+        a, w, x, y = rot.next()
+        bg.gemm_w8a8_pow2(d, a, w, x, y, dY)
+
     t, _ = time_steps(fn, args.steps, args.warmup, torch)
     tg = graph_time(fn, args.steps, torch)
+    tg_hot = graph_time(lambda: bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY), args.steps, torch)
     ops = 2.0 * M * N * K
     byts = M * K + N * K + 4 * (M + N) + 2 * M * N
     log(f"bench: W8A8: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us")
     return {"w8a8_1024x6144x2048": {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
                                     "TOP/s": round(ops / tg / 1e9, 2),
                                     "frac_int8_peak": round(ops / tg / 1e9 / PEAK_INT8_TOPS, 4),
-                                    "GB/s": round(byts / tg / 1e6, 1), "parity": par}}
+                                    "GB/s": round(byts / tg / 1e6, 1), "hot_graph_us": round(tg_hot * 1e3, 2),
+                                    "inputs": rot.note(), "parity": par}}
 
 
 def reduce_extras(args, torch, bg, synth):
@@ -290,17 +344,25 @@ def reduce_extras(args, torch, bg, synth):
         bad = int(np.sum(s.cpu().numpy()[idx].view(np.uint32) != rs.view(np.uint32)))
         if q is not None:
             bad += int(np.sum(q.cpu().numpy()[idx].view(np.uint32) != rq.view(np.uint32)))
-        fn = lambda: bg.reduce_tree(d, dX, s, q, ws)  # noqa: E731
-        ffn = lambda: bg.bench_reduce_free(axis, in_type, dX, s, q)  # noqa: E731
+        rot = Rotation([dX])
+
+        def fn():
+            bg.reduce_tree(d, rot.next()[0], s, q, ws)
+
+        def ffn():
+            bg.bench_reduce_free(axis, in_type, rot.next()[0], s, q)
+
         t, _ = time_steps(fn, args.steps, args.warmup, torch)
         tg = graph_time(fn, args.steps, torch)
+        tg_hot = graph_time(lambda: bg.reduce_tree(d, dX, s, q, ws), args.steps, torch)
         tf, _ = time_steps(ffn, args.steps, args.warmup, torch)
         tfg = graph_time(ffn, args.steps, torch)
         byts = rows * cols * elt + 4 * n_out * (2 if q is not None else 1)
         gbs = byts / tg / 1e6
         out[f"reduce_{axis}_{in_type}_{rows}x{cols}"] = {
             "us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2), "GB/s": round(gbs, 1),
-            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "free_us": round(tf * 1e3, 2),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "hot_graph_us": round(tg_hot * 1e3, 2),
+            "inputs": rot.note(), "free_us": round(tf * 1e3, 2),
             "free_graph_us": round(tfg * 1e3, 2), "fixed_over_free_time": round(tg / tfg, 3),
             "parity": {"sampled_outputs": 64, "mismatches": bad}}
         log(f"bench: reduce {axis}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us, {gbs:.0f} GB/s "
@@ -396,7 +458,10 @@ def main():
     head = Gemm("gemm_bf16 M=4000", X, W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"}, torch, bg)
     par = head.parity(512)
     log(f"bench: parity {par}")
-    ms, wall = time_steps(head.run, args.steps, args.warmup, torch)
+    # the same kernel on one resident copy of the inputs (the MALL then holds
+    # them), then the timed launches proper, rotating over input copies
+    ms_hot, _ = time_steps(head.run, args.steps, args.warmup, torch)
+    ms, wall = time_steps(head.run_rot, args.steps, args.warmup, torch)
     tflops = head.flops() / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.4f} ms per call, {tflops:.1f} TFLOP/s")
 
@@ -416,7 +481,7 @@ def main():
         "config": {"workload": "order-fixed bf16 GEMM C=A*B^T, batch-invariance sweep at M=4000 "
                                "(N=9728, K=2560), 32x32x16 bf16 MFMA, split-K 1, bf16 out",
                    "M": 4000, "N": 9728, "K": 2560, "split_k": 1, "mfma": "F32_32X32X16_BF16",
-                   "out": "bf16"},
+                   "out": "bf16", "inputs": head.rot.note(), "hot_ms_per_step": round(ms_hot, 5)},
         "parity": par,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
