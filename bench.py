@@ -199,7 +199,33 @@ def cpu_baseline(g, budget_s=12.0):
             chunk *= 2
     tflops = 2.0 * g.K * done / t_total / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} outputs of the M=4000 N=9728 K=2560 GEMM, {t_total:.1f} s"}
+            "sample": f"{done} outputs of the M=4000 N=9728 K=2560 GEMM, {t_total:.1f} s", "host": host_cpu()}
+
+
+def host_cpu():
+    """The host CPU's model name (for the oracle timings)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rate(fn, work, unit, sample, budget_s=2.0):
+    """The oracle on a bounded sample of one workload: repeat `fn` (which
+    does `work` units) for about `budget_s` seconds; the rate in `unit`."""
+    import oracle
+    n, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        t += time.perf_counter() - t0
+        n += 1
+    return {"value": round(work * n / t, 6), "unit": unit, "threads": oracle.default_threads(),
+            "kind": "oracle", "sample": sample}
 
 
 def free_twin_us(g, args, torch):
@@ -238,6 +264,15 @@ def gemm_extras(X, W, args, torch, bg, synth):
                                     "free_graph_us": round(free_g, 2), "free_split": free_split,
                                     "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p,
                                     "inputs": g.rot.note()}
+        if M == 1 and not args.no_cpu_baseline:
+            import numpy as np
+            import oracle
+            model = bg.load_profile()["models"]["F32_32X32X16_BF16"]
+            ni = np.arange(0, g.N, 8)
+            mi = np.zeros_like(ni)
+            out[f"batch_sweep_M{M}"]["cpu_oracle"] = oracle_rate(
+                lambda: oracle.gemm_bf16_points(dict(g.spec, mfma_model=model), g.A_host, g.B_host, mi, ni),
+                2.0 * g.K * len(ni) / 1e12, "TFLOP/s", f"{len(ni)} outputs of the M=1 row")
         log(f"bench: M={M}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A4, W4 = synth.gemm_splitk_sweep()
     free = None
@@ -268,6 +303,15 @@ def gemm_extras(X, W, args, torch, bg, synth):
                                "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p,
                                "outputs_differing_from_S1": {"fp32": diff32, "after_bf16_rounding": diff16,
                                                              "of": int(g.M * g.N)}}
+        if S == 16 and not args.no_cpu_baseline:
+            import numpy as np
+            import oracle
+            model = bg.load_profile()["models"]["F32_32X32X16_BF16"]
+            rng = np.random.default_rng(11)
+            mi, ni = rng.integers(0, g.M, 256), rng.integers(0, g.N, 256)
+            out[f"splitk_S{S}"]["cpu_oracle"] = oracle_rate(
+                lambda: oracle.gemm_bf16_points(dict(g.spec, mfma_model=model), g.A_host, g.B_host, mi, ni),
+                2.0 * g.K * len(ni) / 1e12, "TFLOP/s", f"{len(ni)} sampled outputs at S=16")
         log(f"bench: split-K S={S}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us (free {free:.2f} / {free_g:.2f} us)")
     A1, B1 = synth.gemm_small()
     g = Gemm("small", A1, B1, {"mfma": "F32_32X32X16_BF16", "split_k": 2, "cut_rule": "EXPLICIT",
@@ -310,7 +354,11 @@ def w8a8_extra(args, torch, bg, synth):
     ops = 2.0 * M * N * K
     byts = M * K + N * K + 4 * (M + N) + 2 * M * N
     log(f"bench: W8A8: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us")
-    return {"w8a8_1024x6144x2048": {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = oracle_rate(lambda: oracle.w8a8_pow2(a_q[:16], w_q, a_s[:16], w_s), 2.0 * 16 * N * K / 1e12,
+                          "TOP/s", "16 rows of activations (16 x 6144 outputs)")
+    return {"w8a8_1024x6144x2048": {"cpu_oracle": cpu, "us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
                                     "TOP/s": round(ops / tg / 1e9, 2),
                                     "frac_int8_peak": round(ops / tg / 1e9 / PEAK_INT8_TOPS, 4),
                                     "GB/s": round(byts / tg / 1e6, 1), "hot_graph_us": round(tg_hot * 1e3, 2),
@@ -365,6 +413,16 @@ def reduce_extras(args, torch, bg, synth):
             "inputs": rot.note(), "free_us": round(tf * 1e3, 2),
             "free_graph_us": round(tfg * 1e3, 2), "fixed_over_free_time": round(tg / tfg, 3),
             "parity": {"sampled_outputs": 64, "mismatches": bad}}
+        if not args.no_cpu_baseline:
+            if axis == "row":
+                sub2 = Xh[:512]
+                smp = "512 rows"
+            else:
+                sub2 = np.ascontiguousarray(Xh[:, :256])
+                smp = "256 columns"
+            key = f"reduce_{axis}_{in_type}_{rows}x{cols}"
+            out[key]["cpu_oracle"] = oracle_rate(lambda: oracle.reduce(sub2, axis, in_type=in_type),
+                                                 sub2.size * elt / 1e9, "GB/s", smp)
         log(f"bench: reduce {axis}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us, {gbs:.0f} GB/s "
             f"(free {tf * 1e3:.2f} / {tfg * 1e3:.2f} us)")
     return out

@@ -409,11 +409,12 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
         p.bm = s.bm, p.bn = s.bn, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
         p.path = path, p.stages = s.stages;
     } else if (p.mfma == BG_MFMA_I32_32X32X32_I8) {
-        // speed only: the pipelined kernel; 128x128 tiles where they give a
-        // workgroup per CU, otherwise deep-pipelined small tiles
+        // speed only: the pipelined kernel; 128x128 tiles with 5 stages (two
+        // workgroups per CU) where they give a workgroup per CU, otherwise
+        // deep-pipelined small tiles (measured with inputs not in the MALL)
         const bool big = ((M + 127) / 128) * ((N + 127) / 128) >= 192;
         p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
-        p.path = 2, p.stages = big ? 4 : 8;
+        p.path = 2, p.stages = big ? 5 : 8;
     } else {
         const bool big = M >= 128 && N >= 128 && ((M + 127) / 128) * ((N + 127) / 128) >= 128;
         p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
