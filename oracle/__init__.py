@@ -87,6 +87,11 @@ def lib():
                                    C.c_int64, P, P, P, C.c_int64, P, C.c_int64, C.c_int32]
         L.or_reduce.argtypes = [C.c_int, C.c_int, C.c_int64, C.c_int64, P, C.c_int64,
                                 C.c_int32, C.c_int32, P, P, C.c_int32]
+        L.or_quantize_rows_int8.argtypes = [C.c_int64, C.c_int64, P, C.c_int64, P, C.c_int64, P, C.c_int32]
+        L.or_pow2_scale.restype = C.c_float
+        L.or_pow2_scale.argtypes = [C.c_float, C.c_int]
+        L.or_requantize_pow2.argtypes = [C.c_int64, C.c_int64, P, C.c_int64, P, C.c_int, P, C.c_int64, P,
+                                         C.c_int32]
         L.or_abi_version.restype = C.c_int
         _lib = L
     return _lib
@@ -294,6 +299,41 @@ def w8a8_pow2(A_q, W_q, a_scale, w_scale, threads=None):
     if rc != 0:
         raise OverflowError("an int8 accumulator left the int32 range")
     return Y, acc
+
+
+# --------------------------------------------------------------------------
+# int8 quantisation on either side of W8A8
+# --------------------------------------------------------------------------
+def quantize_rows_int8(X, threads=None):
+    """Per-token absmax int8 quantisation of float32 X [M][K].  Returns
+    (Q int8 [M][K], scale float32 [M])."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    M, K = X.shape
+    Q = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    lib().or_quantize_rows_int8(M, K, _ptr(X), K, _ptr(Q), K, _ptr(s), threads or default_threads())
+    return Q, s
+
+
+POW2_MODES = {"nearest": 0, "ceil": 1}
+
+
+def pow2_scale(s, mode="nearest"):
+    """The power-of-two scale that replaces scale s."""
+    return float(np.float32(lib().or_pow2_scale(float(np.float32(s)), POW2_MODES[mode])))
+
+
+def requantize_pow2(W, w_scale, mode="nearest", threads=None):
+    """Requantise int8 W [N][K] with scales w_scale [N] to power-of-two
+    scales.  Returns (W2 int8 [N][K], s2 float32 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.int8)
+    s = np.ascontiguousarray(w_scale, dtype=np.float32)
+    N, K = W.shape
+    W2 = np.empty((N, K), dtype=np.int8)
+    s2 = np.empty(N, dtype=np.float32)
+    lib().or_requantize_pow2(N, K, _ptr(W), K, _ptr(s), POW2_MODES[mode], _ptr(W2), K, _ptr(s2),
+                             threads or default_threads())
+    return W2, s2
 
 
 # --------------------------------------------------------------------------

@@ -448,6 +448,70 @@ int or_w8a8_pow2(int64_t M, int64_t N, int64_t K,
 }
 
 /* ------------------------------------------------------------------------ */
+/* int8 quantisation on either side of W8A8                                 */
+/* ------------------------------------------------------------------------ */
+static int8_t clamp_q(float r)
+{
+    if (r != r) return 0;
+    if (r > 127.0f) return 127;
+    if (r < -127.0f) return -127;
+    return (int8_t)r;
+}
+
+void or_quantize_rows_int8(int64_t M, int64_t K, const float* X, int64_t ldx,
+                           int8_t* Q, int64_t ldq, float* scale, int32_t n_threads)
+{
+#pragma omp parallel for schedule(dynamic, 16) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int64_t m = 0; m < M; m++) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float a = fabsf(X[m * ldx + k]);
+            if (a > amax) amax = a;
+        }
+        float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+        for (int64_t k = 0; k < K; k++) Q[m * ldq + k] = clamp_q(rintf(X[m * ldx + k] / s));
+        scale[m] = s;
+    }
+}
+
+float or_pow2_scale(float s, int mode)
+{
+    if (!(s > 0.0f) || isinf(s)) return s;
+    int ex;
+    (void)frexpf(s, &ex); /* s in [2^(ex-1), 2^ex) */
+    int e;
+    if (mode == OR_POW2_CEIL) {
+        e = (s == ldexpf(1.0f, ex - 1)) ? ex - 1 : ex;
+    } else {
+        /* log2 s rounds up exactly when s >= 2^(ex - 1/2), i.e. when
+         * s*s >= 2^(2 ex - 1); s*s is exact in double */
+        double sq = (double)s * (double)s;
+        e = (sq >= ldexp(1.0, 2 * ex - 1)) ? ex : ex - 1;
+    }
+    return ldexpf(1.0f, e);
+}
+
+void or_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
+                        int mode, int8_t* W2, int64_t ldw2, float* w_scale2, int32_t n_threads)
+{
+#pragma omp parallel for schedule(dynamic, 16) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int64_t n = 0; n < N; n++) {
+        float s = w_scale[n];
+        if (!(s > 0.0f) || isinf(s)) {
+            for (int64_t k = 0; k < K; k++) W2[n * ldw2 + k] = W[n * ldw + k];
+            w_scale2[n] = s;
+            continue;
+        }
+        float s2 = or_pow2_scale(s, mode);
+        for (int64_t k = 0; k < K; k++) {
+            float t = (float)W[n * ldw + k] * s; /* one rounding */
+            W2[n * ldw2 + k] = clamp_q(rintf(t / s2));
+        }
+        w_scale2[n] = s2;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* fixed-order reductions                                                   */
 /* ------------------------------------------------------------------------ */
 static float load_x(int in_type, const void* X, int64_t idx)

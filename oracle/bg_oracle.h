@@ -156,6 +156,29 @@ int or_w8a8_pow2(int64_t M, int64_t N, int64_t K,
                  uint16_t* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
                  int32_t n_threads);
 
+/* ---- int8 quantisation on either side of W8A8 ---------------------------
+ * Activations, per token (per row): scale = fp32(max |x|) / 127, one
+ * rounding (an all-zero row takes scale 1); q = clamp(rint(x / scale),
+ * -127, 127), the division rounded once and rint taking ties to even; a NaN
+ * quotient (from a non-finite input) gives 0.  The pages run W8A8 on int8
+ * activations without printing this step; this is the plainest reading of
+ * per-token absmax quantisation.
+ *
+ * Weights, per output row ("Deterministic LLM Inference ... Power-of-Two
+ * INT8 Quantization Scales", section V: requantise the int8 weights under the
+ * constrained scale rather than only rewriting the scale): s2 = 2^e with
+ * e = round(log2 s) (mode 0, nearest in ratio, decided exactly by s^2 against
+ * 2^(2e-1)) or e = ceil(log2 s) (mode 1, never shrinks the scale); each
+ * weight becomes clamp(rint(fp32(q * s) / s2), -127, 127): the product
+ * rounded once, the division by a power of two exact.  A row whose scale is
+ * not a positive finite number is copied unchanged. */
+void or_quantize_rows_int8(int64_t M, int64_t K, const float* X, int64_t ldx,
+                           int8_t* Q, int64_t ldq, float* scale, int32_t n_threads);
+enum { OR_POW2_NEAREST = 0, OR_POW2_CEIL = 1 };
+float or_pow2_scale(float s, int mode);
+void or_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
+                        int mode, int8_t* W2, int64_t ldw2, float* w_scale2, int32_t n_threads);
+
 /* ---- fixed-order reductions ---------------------------------------------
  * out[i] = balanced tree over leaf sums; a leaf is leaf_len consecutive
  * elements of the reduced axis folded in index order with no +0 seed
