@@ -365,6 +365,61 @@ def w8a8_extra(args, torch, bg, synth):
                                     "inputs": rot.note(), "parity": par}}
 
 
+def quant_extras(args, torch, bg, synth):
+    """Per-token int8 quantisation of the W8A8 activations (1024 x 2048 fp32)
+    and power-of-two requantisation of its weights (6144 x 2048 int8), both
+    HBM-bound, checked in full against the oracle."""
+    import numpy as np
+    import oracle
+    out = {}
+    x = synth.f32_normal(1005, (1024, 2048))
+    dX = torch.from_numpy(x).cuda()
+    dQ = torch.empty((1024, 2048), dtype=torch.int8, device="cuda")
+    da = torch.empty(1024, dtype=torch.float32, device="cuda")
+    bg.quantize_act_int8(dX, dQ, da)
+    torch.cuda.synchronize()
+    Qo, ao = oracle.quantize_rows_int8(x)
+    par = {"checked": int(x.size), "mismatches": int(np.sum(dQ.cpu().numpy() != Qo)) +
+           int(np.sum(da.cpu().numpy().view(np.uint32) != ao.view(np.uint32)))}
+    rot = Rotation([dX])
+
+    def fq():
+        bg.quantize_act_int8(rot.next()[0], dQ, da)
+
+    t, _ = time_steps(fq, args.steps, args.warmup, torch)
+    tg = graph_time(fq, args.steps, torch)
+    byts = x.size * 5 + 4 * 1024
+    out["quantize_act_1024x2048"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
+                                     "GB/s": round(byts / tg / 1e6, 1),
+                                     "frac_hbm": round(byts / tg / 1e6 / PEAK_HBM_GBS, 4),
+                                     "inputs": rot.note(), "parity": par}
+    W = synth.int8_uniform(2005, (6144, 2048))
+    s = np.exp(np.random.default_rng(11).uniform(-9, -3, 6144)).astype(np.float32)
+    dW, ds = torch.from_numpy(W).cuda(), torch.from_numpy(s).cuda()
+    dW2, ds2 = torch.empty_like(dW), torch.empty_like(ds)
+    bg.requantize_weights_pow2(dW, ds, dW2, ds2, "nearest")
+    torch.cuda.synchronize()
+    W2o, s2o = oracle.requantize_pow2(W, s, "nearest")
+    par = {"checked": int(W.size), "mismatches": int(np.sum(dW2.cpu().numpy() != W2o)) +
+           int(np.sum(ds2.cpu().numpy().view(np.uint32) != s2o.view(np.uint32)))}
+    rot = Rotation([dW, ds])
+
+    def fr():
+        w, sc = rot.next()
+        bg.requantize_weights_pow2(w, sc, dW2, ds2, "nearest")
+
+    t, _ = time_steps(fr, args.steps, args.warmup, torch)
+    tg = graph_time(fr, args.steps, torch)
+    byts = W.size * 2 + 8 * 6144
+    out["requantize_pow2_6144x2048"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
+                                        "GB/s": round(byts / tg / 1e6, 1),
+                                        "frac_hbm": round(byts / tg / 1e6 / PEAK_HBM_GBS, 4),
+                                        "inputs": rot.note(), "parity": par}
+    log(f"bench: quantize {out['quantize_act_1024x2048']['graph_us']} us, requantize "
+        f"{out['requantize_pow2_6144x2048']['graph_us']} us")
+    return out
+
+
 def reduce_extras(args, torch, bg, synth):
     """The row reduction (fp32 16384 x 8192, sum and sum of squares from one
     read) and the column sum (bf16 8192 x 4096), against HBM bandwidth, with
@@ -573,6 +628,7 @@ def main():
     if not args.no_extra:
         extra.update(gemm_extras(X, W, args, torch, bg, synth))
         extra.update(w8a8_extra(args, torch, bg, synth))
+        extra.update(quant_extras(args, torch, bg, synth))
         extra.update(reduce_extras(args, torch, bg, synth))
     if extra:
         line["extra"] = extra

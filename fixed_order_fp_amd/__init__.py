@@ -86,6 +86,10 @@ _SYMBOLS = {
     "bg_gemm_w8a8_pow2": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                     C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                     C.c_void_p, C.c_int64, C.c_void_p]),
+    "bg_quantize_act_int8": (C.c_int, [C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64,
+                                       C.c_void_p, C.c_void_p]),
+    "bg_requantize_weights_pow2": (C.c_int, [C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
+                                             C.c_uint32, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "bg_reduce_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p]),
     "bg_reduce_tree": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -262,6 +266,23 @@ def gemm_w8a8_pow2(desc, A, W, a_scale, w_scale, Y, acc_out=None, stream=None):
     _check(lib().bg_gemm_w8a8_pow2(C.byref(desc), M, N, K, _ptr(A), A.stride(0), _ptr(W), W.stride(0),
                                    _ptr(a_scale), _ptr(w_scale), _ptr(Y), Y.stride(0), _ptr(acc_out),
                                    0 if acc_out is None else acc_out.stride(0), _stream(stream)))
+
+
+def quantize_act_int8(X, Q, a_scale, stream=None):
+    """Per-token int8 quantisation: X fp32 [M][K] -> Q int8 [M][K], a_scale fp32 [M]."""
+    M, K = X.shape
+    _check(lib().bg_quantize_act_int8(M, K, _ptr(X), X.stride(0), _ptr(Q), Q.stride(0), _ptr(a_scale),
+                                      _stream(stream)))
+
+
+POW2 = {"nearest": 0, "ceil": 1}
+
+
+def requantize_weights_pow2(W, w_scale, W2, w_scale2, mode="nearest", stream=None):
+    """int8 W [N][K] with scales w_scale [N] -> W2, w_scale2 with power-of-two scales."""
+    N, K = W.shape
+    _check(lib().bg_requantize_weights_pow2(N, K, _ptr(W), W.stride(0), _ptr(w_scale), POW2[mode], _ptr(W2),
+                                            W2.stride(0), _ptr(w_scale2), _stream(stream)))
 
 
 def reduce_tree(desc, X, out_sum=None, out_sumsq=None, ws=None, stream=None):

@@ -520,6 +520,45 @@ bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols, co
     return BG_OK;
 }
 
+bg_status bg_quantize_act_int8(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q, int64_t ldq,
+                               float* a_scale, hipStream_t stream)
+{
+    if (M < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
+    if (M > 0x7fffffff) return fail(BG_E_UNSUPPORTED, "at most 2^31 - 1 rows");
+    if (ldx < K || ldq < K) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (M == 0) return BG_OK;
+    if (!a_scale || (K > 0 && (!X || !Q))) return fail(BG_E_INVALID, "NULL tensor");
+    if (((uintptr_t)X & 3u) || ((uintptr_t)a_scale & 3u)) return fail(BG_E_ALIGN, "X and a_scale must be 4-byte aligned");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    const bool vec = aligned16(X) && ldx % 4 == 0 && K % 4 == 0 && ((uintptr_t)Q & 3u) == 0 && ldq % 4 == 0;
+    hipError_t e = bg::launch_quantize_rows(M, K, X, ldx, Q, ldq, a_scale, vec, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
+bg_status bg_requantize_weights_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
+                                     uint32_t mode, int8_t* W2, int64_t ldw2, float* w_scale2,
+                                     hipStream_t stream)
+{
+    if (N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
+    if (N > 0x7fffffff) return fail(BG_E_UNSUPPORTED, "at most 2^31 - 1 rows");
+    if (mode != BG_POW2_NEAREST && mode != BG_POW2_CEIL) return fail(BG_E_INVALID, "unknown mode");
+    if (ldw < K || ldw2 < K) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (N == 0) return BG_OK;
+    if (!w_scale || !w_scale2 || (K > 0 && (!W || !W2))) return fail(BG_E_INVALID, "NULL tensor");
+    if (((uintptr_t)w_scale & 3u) || ((uintptr_t)w_scale2 & 3u)) return fail(BG_E_ALIGN, "scales must be 4-byte aligned");
+    const uintptr_t w0 = (uintptr_t)W, w1 = w0 + (uintptr_t)((N - 1) * ldw + K);
+    const uintptr_t o0 = (uintptr_t)W2, o1 = o0 + (uintptr_t)((N - 1) * ldw2 + K);
+    if (K > 0 && w0 < o1 && o0 < w1) return fail(BG_E_INVALID, "W2 may not overlap W");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    const bool vec = aligned16(W) && aligned16(W2) && ldw % 16 == 0 && ldw2 % 16 == 0 && K % 16 == 0;
+    hipError_t e = bg::launch_requantize_pow2(N, K, W, ldw, w_scale, (int)mode, W2, ldw2, w_scale2, vec, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
 bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                                   int64_t ldb, float* C, int64_t ldc, int32_t split_k, hipStream_t stream)
 {

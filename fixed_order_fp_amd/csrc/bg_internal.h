@@ -96,6 +96,12 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
 hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, const void* X, int64_t ldx,
                               float* out_sum, float* out_sq, int n_cu, hipStream_t stream);
 
+hipError_t launch_quantize_rows(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q, int64_t ldq,
+                                float* scale, bool vec, hipStream_t stream);
+hipError_t launch_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
+                                  int mode, int8_t* W2, int64_t ldw2, float* w_scale2, bool vec,
+                                  hipStream_t stream);
+
 // which tile shapes the GEMM kernel is instantiated for
 hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
 bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct, int stages);

@@ -236,6 +236,41 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
                             void* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
                             hipStream_t stream);
 
+/* ---- int8 quantisation on either side of W8A8 ----------------------------- */
+
+/* Per-token int8 quantisation of activations (the input of bg_gemm_w8a8_pow2;
+ * the pages run W8A8 on int8 activations without printing this step, and this
+ * is the plainest per-token absmax reading):
+ *   a_scale[m] = fp32(max_k |X[m][k]|) / 127, rounded once (1 for a row of
+ *   zeros); Q[m][k] = clamp(rint(X[m][k] / a_scale[m]), -127, 127), the
+ *   division rounded once, rint taking ties to even, a NaN quotient giving 0.
+ *   The maximum is exact, so the result does not depend on any order.
+ * X: fp32 [M][ldx] (device, caller-owned); Q: int8 [M][ldq]; a_scale: fp32 [M].
+ * Inputs are expected finite (an infinite element makes its row's scale
+ * infinite and its codes 0).  M, K >= 0, M < 2^31; X and Q may be NULL when
+ * K = 0 (every scale is then 1); X 4-byte aligned (16-byte X rows with
+ * K % 4 == 0 take the vector path).  Errors come back synchronously with
+ * nothing enqueued. */
+bg_status bg_quantize_act_int8(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q, int64_t ldq,
+                               float* a_scale, hipStream_t stream);
+
+/* Requantisation of int8 weights to power-of-two scales ("Deterministic LLM
+ * Inference ... Power-of-Two INT8 Quantization Scales", section V: the
+ * weights are requantised under the constrained scale, not just the scale
+ * rewritten), per output row n:
+ *   s2 = 2^e, e = round(log2 w_scale[n]) for BG_POW2_NEAREST (nearest in
+ *   ratio; decided exactly, a tie cannot occur) or e = ceil(log2 w_scale[n])
+ *   for BG_POW2_CEIL (never shrinks the scale, so nothing clips);
+ *   W2[n][k] = clamp(rint(fp32(W[n][k] * w_scale[n]) / s2), -127, 127).
+ *   A row whose scale is not a positive finite number is copied unchanged.
+ * W, W2: int8 [N][ldw] / [N][ldw2] (may not overlap); w_scale, w_scale2:
+ * fp32 [N].  N, K >= 0, N < 2^31 (W and W2 may be NULL when K = 0).  The
+ * outputs feed bg_gemm_w8a8_pow2. */
+enum { BG_POW2_NEAREST = 0, BG_POW2_CEIL = 1 };
+bg_status bg_requantize_weights_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
+                                     uint32_t mode, int8_t* W2, int64_t ldw2, float* w_scale2,
+                                     hipStream_t stream);
+
 /* Workspace bytes bg_reduce_tree needs (column axis: one fp32 partial per
  * column per workgroup row-block). */
 bg_status bg_reduce_workspace_bytes(const bg_reduce_desc* d, int64_t rows, int64_t cols,
