@@ -365,6 +365,72 @@ def w8a8_extra(args, torch, bg, synth):
                                     "inputs": rot.note(), "parity": par}}
 
 
+def gemm_reduce_extras(X, W, args, torch, bg):
+    """The headline GEMM with fused fixed-order reductions of its fp32 C: the
+    column sum (bias-gradient style) and the row sum + sum of squares (norm
+    statistics), each against the same results done unfused (the GEMM writing
+    fp32 C, then bg_reduce_tree over it) and against the plain bf16 GEMM;
+    sampled columns / rows checked against the oracle's composition."""
+    import numpy as np
+    import oracle
+    out = {}
+    M, K = X.shape
+    N = W.shape[0]
+    g = Gemm("gemm_bf16 M=4000 (fused reductions)", X, W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"},
+             torch, bg)
+    t_plain, _ = time_steps(g.run_rot, args.steps, args.warmup, torch)
+    dF = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    d32 = bg.gemm_desc({"mfma": "F32_32X32X16_BF16"}, out_type="fp32")
+    spec = dict(g.spec, out_type="fp32", mfma_model=bg.load_profile()["models"]["F32_32X32X16_BF16"])
+    for axis, op in (("col", "sum"), ("row", "sum_and_sumsq")):
+        rd = bg.reduce_desc({"in_type": "fp32", "axis": axis, "op": op})
+        n_out = N if axis == "col" else M
+        s = torch.empty(n_out, dtype=torch.float32, device="cuda")
+        q = torch.empty(n_out, dtype=torch.float32, device="cuda") if op == "sum_and_sumsq" else None
+        nws = bg.gemm_bf16_reduce_workspace_bytes(g.desc, rd, M, N, K)
+        ws = torch.empty(nws // 4 + 1, dtype=torch.float32, device="cuda")
+
+        def fused():
+            A, B = g.rot.next()
+            bg.gemm_bf16_reduce(g.desc, rd, A, B, g.dC, s, q, ws)
+
+        fused()
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(5)
+        if axis == "col":
+            idx = np.sort(rng.choice(N, 4, replace=False))
+            mi, ni = np.repeat(np.arange(M), 4), np.tile(idx, M)
+            sub = oracle.gemm_bf16_points(spec, g.A_host, g.B_host, mi, ni).reshape(M, 4)
+        else:
+            idx = np.sort(rng.choice(M, 2, replace=False))
+            mi, ni = np.repeat(idx, N), np.tile(np.arange(N), 2)
+            sub = oracle.gemm_bf16_points(spec, g.A_host, g.B_host, mi, ni).reshape(2, N)
+        rs, rq = oracle.reduce(sub, axis, leaf_len=32, in_type="fp32")
+        bad = int(np.sum(s.cpu().numpy()[idx].view(np.uint32) != rs.view(np.uint32)))
+        if q is not None:
+            bad += int(np.sum(q.cpu().numpy()[idx].view(np.uint32) != rq.view(np.uint32)))
+        t_f, _ = time_steps(fused, args.steps, args.warmup, torch)
+        rdu = bg.reduce_desc({"in_type": "fp32", "axis": axis, "op": op})
+        nwu = bg.reduce_workspace_bytes(rdu, M, N)
+        wsu = torch.empty(max(nwu, 16), dtype=torch.uint8, device="cuda")
+
+        def unfused():
+            A, B = g.rot.next()
+            bg.gemm_bf16(d32, A, B, dF, None)
+            bg.reduce_tree(rdu, dF, s, q, wsu)
+
+        t_u, _ = time_steps(unfused, args.steps, args.warmup, torch)
+        out[f"gemm_reduce_{axis}_{op}"] = {
+            "us": round(t_f * 1e3, 2), "plain_gemm_us": round(t_plain * 1e3, 2),
+            "unfused_us": round(t_u * 1e3, 2), "fused_over_plain_time": round(t_f / t_plain, 4),
+            "fused_over_unfused_time": round(t_f / t_u, 4), "TFLOP/s": round(g.flops() / t_f / 1e9, 2),
+            "inputs": g.rot.note(),
+            "parity": {"sampled_outputs": int(len(idx)), "mismatches": bad}}
+        log(f"bench: GEMM + {axis} {op}: fused {t_f * 1e3:.1f} us, plain GEMM {t_plain * 1e3:.1f} us, "
+            f"unfused {t_u * 1e3:.1f} us")
+    return out
+
+
 def quant_extras(args, torch, bg, synth):
     """Per-token int8 quantisation of the W8A8 activations (1024 x 2048 fp32)
     and power-of-two requantisation of its weights (6144 x 2048 int8), both
@@ -629,6 +695,7 @@ def main():
         extra.update(gemm_extras(X, W, args, torch, bg, synth))
         extra.update(w8a8_extra(args, torch, bg, synth))
         extra.update(quant_extras(args, torch, bg, synth))
+        extra.update(gemm_reduce_extras(X, W, args, torch, bg))
         extra.update(reduce_extras(args, torch, bg, synth))
     if extra:
         line["extra"] = extra

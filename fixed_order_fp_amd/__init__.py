@@ -86,6 +86,11 @@ _SYMBOLS = {
     "bg_gemm_w8a8_pow2": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                     C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                     C.c_void_p, C.c_int64, C.c_void_p]),
+    "bg_gemm_bf16_reduce_workspace_bytes": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                                      C.c_void_p]),
+    "bg_gemm_bf16_reduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
+                                      C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "bg_quantize_act_int8": (C.c_int, [C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64,
                                        C.c_void_p, C.c_void_p]),
     "bg_requantize_weights_pow2": (C.c_int, [C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
@@ -266,6 +271,22 @@ def gemm_w8a8_pow2(desc, A, W, a_scale, w_scale, Y, acc_out=None, stream=None):
     _check(lib().bg_gemm_w8a8_pow2(C.byref(desc), M, N, K, _ptr(A), A.stride(0), _ptr(W), W.stride(0),
                                    _ptr(a_scale), _ptr(w_scale), _ptr(Y), Y.stride(0), _ptr(acc_out),
                                    0 if acc_out is None else acc_out.stride(0), _stream(stream)))
+
+
+def gemm_bf16_reduce_workspace_bytes(desc, rdesc, M, N, K):
+    n = C.c_size_t(0)
+    _check(lib().bg_gemm_bf16_reduce_workspace_bytes(C.byref(desc), C.byref(rdesc), M, N, K, C.byref(n)))
+    return n.value
+
+
+def gemm_bf16_reduce(desc, rdesc, A, B, C_out, out_sum=None, out_sumsq=None, ws=None, stream=None):
+    """C = A B^T (bf16) plus the fixed-order reduction rdesc of the fp32 C."""
+    M, K = A.shape
+    N = B.shape[0]
+    _check(lib().bg_gemm_bf16_reduce(C.byref(desc), C.byref(rdesc), M, N, K, _ptr(A), A.stride(0), _ptr(B),
+                                     B.stride(0), _ptr(C_out), C_out.stride(0), _ptr(out_sum), _ptr(out_sumsq),
+                                     _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)))
 
 
 def quantize_act_int8(X, Q, a_scale, stream=None):

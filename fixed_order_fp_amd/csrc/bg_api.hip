@@ -183,6 +183,34 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
     else set(128, 64, 32, 2, 2, 2, 4);
 }
 
+// the reduction descriptor of a GEMM with fused reductions: fp32 values (C)
+bg_status check_fused_reduce(const bg_reduce_desc* rd)
+{
+    if (!rd) return fail(BG_E_INVALID, "NULL reduction descriptor");
+    if (rd->version != 1) return fail(BG_E_INVALID, "reduction descriptor version must be 1");
+    if (rd->in_type != BG_FP32) return fail(BG_E_INVALID, "the fused reductions read the fp32 C: in_type fp32");
+    if (rd->acc_type != BG_FP32 || rd->out_type != BG_FP32) return fail(BG_E_INVALID, "accumulation and output are fp32");
+    if (rd->op < BG_RED_SUM || rd->op > BG_RED_SUM_AND_SUMSQ) return fail(BG_E_INVALID, "unknown op");
+    if (rd->axis != BG_AXIS_ROW && rd->axis != BG_AXIS_COL) return fail(BG_E_INVALID, "unknown axis");
+    if (rd->leaf_order != BG_LEAF_SEQUENTIAL_NO_SEED) return fail(BG_E_INVALID, "unknown leaf_order");
+    if (rd->sq_fma != BG_SQ_FUSED && rd->sq_fma != BG_SQ_UNFUSED) return fail(BG_E_INVALID, "unknown sq_fma");
+    if (rd->tree != BG_TREE_BALANCED) return fail(BG_E_INVALID, "unknown tree");
+    if (rd->odd_rule != BG_ODD_CARRY_LAST) return fail(BG_E_INVALID, "unknown odd_rule");
+    if (rd->leaf_len != 32) return fail(BG_E_UNSUPPORTED, "only leaves of 32 elements are built");
+    return BG_OK;
+}
+
+// leaves and outputs of the fused reduction; workspace bytes
+void fused_reduce_shape(const bg_reduce_desc* rd, int64_t M, int64_t N, int64_t& n_leaf, int64_t& n_out,
+                        size_t& bytes)
+{
+    n_out = rd->axis == BG_AXIS_COL ? N : M;
+    const int64_t len = rd->axis == BG_AXIS_COL ? M : N;
+    n_leaf = (len + 31) / 32;
+    const int arrays = ((rd->op & BG_RED_SUM) ? 1 : 0) + ((rd->op & BG_RED_SUMSQ) ? 1 : 0);
+    bytes = (size_t)n_leaf * (size_t)n_out * sizeof(float) * (size_t)arrays;
+}
+
 }  // namespace
 
 extern "C" {
@@ -516,6 +544,95 @@ bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols, co
     st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_reduce(p, rows, cols, X, ldx, out_sum, out_sumsq, (float*)ws, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
+bg_status bg_gemm_bf16_reduce_workspace_bytes(const bg_gemm_desc* d, const bg_reduce_desc* rd, int64_t M,
+                                              int64_t N, int64_t K, size_t* bytes)
+{
+    (void)K;
+    if (!d || !bytes) return fail(BG_E_INVALID, "NULL argument");
+    bg_status st = check_fused_reduce(rd);
+    if (st != BG_OK) return st;
+    if (M < 0 || N < 0) return fail(BG_E_INVALID, "negative size");
+    int64_t n_leaf, n_out;
+    fused_reduce_shape(rd, M, N, n_leaf, n_out, *bytes);
+    return BG_OK;
+}
+
+bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                              float* out_sum, float* out_sumsq, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    bg_status st = check_common_order(d);
+    if (st != BG_OK) return st;
+    if (d->a_type != BG_BF16 || d->b_type != BG_BF16) return fail(BG_E_INVALID, "bf16 operands");
+    if (d->acc_type != BG_FP32) return fail(BG_E_INVALID, "bf16 GEMM accumulates in fp32");
+    if (d->out_type != BG_FP32 && d->out_type != BG_BF16) return fail(BG_E_INVALID, "out_type must be fp32 or bf16");
+    if (d->mfma != BG_MFMA_F32_32X32X16_BF16)
+        return fail(BG_E_UNSUPPORTED, "the fused reductions are built for the 32x32x16 instruction");
+    if (d->partial_type != BG_FP32 || d->merge_type != BG_FP32)
+        return fail(BG_E_UNSUPPORTED, "only fp32 partials merged in fp32 are built");
+    if (d->combine != BG_COMBINE_BALANCED) return fail(BG_E_UNSUPPORTED, "only the balanced combine is built");
+    if (d->epilogue != BG_EPI_NONE) return fail(BG_E_INVALID, "bg_gemm_bf16_reduce has no other epilogue");
+    if (d->split_k != 1) return fail(BG_E_UNSUPPORTED, "the fused reductions take split_k 1");
+    st = check_fused_reduce(rd);
+    if (st != BG_OK) return st;
+    if (M < 0 || N < 0 || K < 1) return fail(BG_E_INVALID, "bad sizes");
+    if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (!(rd->op & BG_RED_SUM)) out_sum = nullptr;
+    if (!(rd->op & BG_RED_SUMSQ)) out_sumsq = nullptr;
+    int64_t n_leaf, n_out;
+    size_t need;
+    fused_reduce_shape(rd, M, N, n_leaf, n_out, need);
+    if (n_leaf > 1024) return fail(BG_E_UNSUPPORTED, "the reduced axis holds at most 1024 leaves (32768 elements)");
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");
+    if ((rd->op & BG_RED_SUM) && !out_sum) return fail(BG_E_INVALID, "op asks for the sum but out_sum is NULL");
+    if ((rd->op & BG_RED_SUMSQ) && !out_sumsq) return fail(BG_E_INVALID, "op asks for sumsq but out_sumsq is NULL");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 8 || ldb % 8 || ldc % 8)
+        return fail(BG_E_ALIGN, "pointers must be 16-byte aligned and leading dimensions multiples of 8");
+    if (((uintptr_t)out_sum & 3u) || ((uintptr_t)out_sumsq & 3u)) return fail(BG_E_ALIGN, "outputs must be 4-byte aligned");
+    if (!ws || ws_bytes < need) return fail(BG_E_WORKSPACE, "the fused reductions need a workspace");
+    if ((uintptr_t)ws & 3u) return fail(BG_E_ALIGN, "workspace must be 4-byte aligned");
+
+    bg::GemmPlan p{};
+    p.S = 1;
+    p.cuts.c[0] = 0;
+    p.cuts.c[1] = K;
+    p.mfma = (int)d->mfma;
+    p.out_bf16 = d->out_type == BG_BF16;
+    const bg_gemm_schedule& s = d->sched;
+    p.group_m = s.group_m;
+    if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
+        if ((s.bk && s.bk != 32) || (s.load_path && s.load_path != 2) ||
+            !bg::gemm_bf16_red_has_tile(s.bm, s.bn, s.waves_m, s.waves_n, s.stages))
+            return fail(BG_E_UNSUPPORTED, "schedule is not built with the fused reductions");
+        p.bm = s.bm, p.bn = s.bn, p.bk = 32, p.waves_m = s.waves_m, p.waves_n = s.waves_n, p.direct = 2;
+        p.stages = s.stages;
+    } else {  // speed only: the tiles built with the reductions
+        auto set = [&](int bm, int bn, int wm, int wn, int ns) {
+            p.bm = bm, p.bn = bn, p.bk = 32, p.waves_m = wm, p.waves_n = wn, p.direct = 2, p.stages = ns;
+        };
+        const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+        if (big >= 384) set(320, 256, 2, 4, 4);
+        else if (M > 64 && ((M + 255) / 256) * ((N + 127) / 128) >= 150) set(256, 128, 2, 2, 4);
+        else set(64, 64, 2, 2, 8);
+    }
+    float* ws_sum = (float*)ws;
+    float* ws_sq = (float*)ws + ((rd->op & BG_RED_SUM) ? n_leaf * n_out : 0);
+    p.red = rd->axis == BG_AXIS_COL ? 1 : 2;
+    p.red_args.ws_sum = out_sum ? ws_sum : nullptr;
+    p.red_args.ws_sq = out_sumsq ? ws_sq : nullptr;
+    p.red_args.n_out = n_out;
+    p.red_args.fused = rd->sq_fma == BG_SQ_FUSED;
+    st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_gemm_bf16_reduce(p, M, N, (const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc,
+                                               stream);
+    if (e == hipSuccess)
+        e = bg::launch_leaf_tree(p.red_args.ws_sum, p.red_args.ws_sq, n_out, (int)n_leaf, out_sum, out_sumsq, stream);
     if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
     return BG_OK;
 }

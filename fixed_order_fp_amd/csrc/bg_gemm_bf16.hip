@@ -403,12 +403,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32
 // split partial added into C with atomics (the free-order twin only)
-template <int BM, int BN, int WM, int WN, int NS, int OUT>
+// RED: 0 none, 1 and 2 fused reductions of the fp32 C tile (column and row
+// leaves; S = 1, OUT 0 or 1).
+template <int BM, int BN, int WM, int WN, int NS, int OUT, int RED = 0>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
     PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU)))
 void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
                            int64_t ldb, void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M,
-                           int64_t N, Cuts cuts, int tiles_m, int tiles_n, int group_m)
+                           int64_t N, Cuts cuts, int tiles_m, int tiles_n, int group_m, RedArgs red)
 {
     constexpr int BK = 32, CPR = BK / kChunk, KS = BK / 16;
     constexpr int NW = WM * WN, NT = 64 * NW;
@@ -571,8 +573,66 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
     for (; t < n_steady; t++) turn(t, std::true_type{});
     for (; t < n_turns; t++) turn(t, std::false_type{});
 
-    // epilogue.  Block (j, i), element e of lane l: row m = wm*WTM + 32i + l%32,
-    // columns n = wn*WTN + 32j + 8(e/4) + 4(l/32) + (0..3) for e%4 = 0..3.
+    // Block (j, i), element e of lane l: row m = wm*WTM + 32i + l%32, columns
+    // n = wn*WTN + 32j + 8(e/4) + 4(l/32) + (0..3) for e%4 = 0..3.
+    //
+    // Fused reductions of the fp32 C values (before any rounding to the output
+    // type): each wave stages one 32x32 block at a time in its own LDS slice
+    // (rows padded to 33 floats, so both a column and a row walk are free of
+    // bank conflicts); lane c < 32 folds column c of the block over its rows
+    // (RED 1: a leaf of 32 rows) or row c over its columns (RED 2: a leaf of
+    // 32 columns) in index order, with no seed (s = x0, s = s + xi; q = x0 x0,
+    // q = fma(xi, xi, q) or q + xi xi), and writes the leaf node.  The leaf's
+    // elements past M or N are left out (a short last leaf).
+    if constexpr (RED != 0) {
+        static_assert(OUT == 0 || OUT == 1, "fused reductions take the unsplit C");
+        static_assert(NW * 32 * 33 * 4 <= LDS_BYTES, "the reduction slices fit in LDS");
+        __syncthreads();  // every wave is done with the operand stages
+        float* st = (float*)lds + wave * (32 * 33);
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int u = 0; u < 4; u++) st[r_in * 33 + 8 * q + 4 * h + u] = acc[j][i][4 * q + u];
+                const int64_t rb = m0 + wm * WTM + 32 * i, cb = n0 + wn * WTN + 32 * j;
+                const int64_t n_el = RED == 1 ? M - rb : N - cb;             // elements of this lane's leaf
+                const int64_t o = (RED == 1 ? cb : rb) + lane;                // this lane's output
+                const int64_t o_end = RED == 1 ? N : M;
+                if (lane < 32 && o < o_end && n_el > 0) {
+                    const int n = n_el < 32 ? (int)n_el : 32;
+                    const float* x = st + (RED == 1 ? lane : lane * 33);
+                    constexpr int STEP = RED == 1 ? 33 : 1;
+                    auto step = [&](float v, float& sv, float& qv) {
+                        sv = sv + v;
+                        if (red.fused) {
+                            qv = __builtin_fmaf(v, v, qv);
+                        } else {
+                            const float vv = v * v;
+                            qv = qv + vv;
+                        }
+                    };
+                    float sv = x[0], qv = x[0] * x[0];
+                    if (n == 32) {  // a whole leaf: its 32 elements are read at once, then folded
+                        float xv[32];
+#pragma unroll
+                        for (int e = 1; e < 32; e++) xv[e] = x[e * STEP];
+#pragma unroll
+                        for (int e = 1; e < 32; e++) step(xv[e], sv, qv);
+                    } else {  // the short last leaf
+                        for (int e = 1; e < n; e++) step(x[e * STEP], sv, qv);
+                    }
+                    const int64_t leaf = (RED == 1 ? rb : cb) / 32;
+                    if (red.ws_sum) red.ws_sum[leaf * red.n_out + o] = sv;
+                    if (red.ws_sq) red.ws_sq[leaf * red.n_out + o] = qv;
+                }
+            }
+        __syncthreads();  // the slices are free again
+    }
+
+    // epilogue
     if constexpr (OUT == 1) {
         __syncthreads();  // every wave is done with the operand stages
         unsigned char* cl = (unsigned char*)lds;
@@ -732,16 +792,16 @@ struct TileLauncher<2> {
         dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.S), block(64 * WM * WN);
         if (p.atomic)  // free-order twin only
             hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 3>), grid, block, 0, stream, A, lda, B, ldb,
-                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m, RedArgs{});
         else if (p.S > 1)
             hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, stream, A, lda, B, ldb,
-                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m, RedArgs{});
         else if (p.out_bf16)
             hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, stream, A, lda, B, ldb,
-                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m, RedArgs{});
         else
             hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, stream, A, lda, B, ldb,
-                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m);
+                               C, ldc, ws, M, N, p.cuts, tiles_m, tiles_n, group_m, RedArgs{});
         return hipGetLastError();
     }
 };
@@ -898,6 +958,53 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, 
         return launch_combine<false>(p.S, M, N, ws, C, ldc, stream);
     }
     return hipSuccess;
+}
+
+// Tiles built with the fused reductions (32x32x16, pipelined path): the
+// large-output tile, a mid-size tile and the small-M tile.
+#define BG_GEMM_RED_TILES(X) \
+    X(320, 256, 2, 4, 4)     \
+    X(256, 128, 2, 2, 4)     \
+    X(64, 64, 2, 2, 8)
+
+bool gemm_bf16_red_has_tile(int bm, int bn, int waves_m, int waves_n, int stages)
+{
+#define BG_RHAS(BM_, BN_, WM_, WN_, NS_)                                                         \
+    if (bm == BM_ && bn == BN_ && waves_m == WM_ && waves_n == WN_ && (stages == 0 || stages == NS_)) \
+        return true;
+    BG_GEMM_RED_TILES(BG_RHAS)
+#undef BG_RHAS
+    return false;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int OUT, int RED>
+static hipError_t launch_red_tile(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                                  const uint16_t* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream)
+{
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int group_m = p.group_m > 0 ? p.group_m
+                                      : walk_group_m(tiles_m, tiles_n, BM, BN, PipeLds<BM, BN, NS, OUT>::WG_PER_CU);
+    dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, OUT, RED>), grid, block, 0, stream, A, lda, B, ldb,
+                       C, ldc, (float*)nullptr, M, N, p.cuts, tiles_m, tiles_n, group_m, p.red_args);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                                   const uint16_t* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream)
+{
+    if (p.S != 1 || (p.red != 1 && p.red != 2) || p.mfma != BG_MFMA_F32_32X32X16_BF16) return hipErrorInvalidValue;
+#define BG_RLAUNCH(BM_, BN_, WM_, WN_, NS_)                                                                       \
+    if (p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_ && (p.stages == 0 || p.stages == NS_)) { \
+        if (p.out_bf16)                                                                                             \
+            return p.red == 1 ? launch_red_tile<BM_, BN_, WM_, WN_, NS_, 1, 1>(p, M, N, A, lda, B, ldb, C, ldc, stream) \
+                              : launch_red_tile<BM_, BN_, WM_, WN_, NS_, 1, 2>(p, M, N, A, lda, B, ldb, C, ldc, stream); \
+        return p.red == 1 ? launch_red_tile<BM_, BN_, WM_, WN_, NS_, 0, 1>(p, M, N, A, lda, B, ldb, C, ldc, stream)   \
+                          : launch_red_tile<BM_, BN_, WM_, WN_, NS_, 0, 2>(p, M, N, A, lda, B, ldb, C, ldc, stream);   \
+    }
+    BG_GEMM_RED_TILES(BG_RLAUNCH)
+#undef BG_RLAUNCH
+    return hipErrorInvalidValue;
 }
 
 }  // namespace bg

@@ -48,6 +48,16 @@ struct Cuts {
     int64_t c[BG_MAX_SPLIT + 1];
 };
 
+// Reductions of the fp32 C tile in the GEMM epilogue: one fp32 leaf node per
+// 32 consecutive rows (column axis) or columns (row axis) of C and per output,
+// written as ws[leaf][n_out]; NULL pointers skip that output.
+struct RedArgs {
+    float* ws_sum;
+    float* ws_sq;
+    int64_t n_out;  // N for the column axis, M for the row axis
+    int fused;      // sum of squares by fma
+};
+
 struct GemmPlan {
     int S;           // splits
     Cuts cuts;       // cut points, cuts.c[0] = 0, cuts.c[S] = K
@@ -59,6 +69,8 @@ struct GemmPlan {
     int stages;      // k tiles in LDS (pipelined path)
     int group_m;     // tile rows per group of the workgroup walk
     bool atomic;     // free-order twin: splits added into a zeroed fp32 C with atomics
+    int red;         // fused reduction of C: 0 none, 1 column leaves, 2 row leaves
+    RedArgs red_args;
 };
 
 hipError_t launch_probe(int mfma, int64_t n_cases, const void* A, const void* B, const void* C,
@@ -96,6 +108,10 @@ hipError_t launch_reduce(const ReducePlan& p, int64_t rows, int64_t cols, const 
 hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, const void* X, int64_t ldx,
                               float* out_sum, float* out_sq, int n_cu, hipStream_t stream);
 
+// Balanced tree over leaf nodes ws[leaf][n_out] (n_leaf <= 1024) per output.
+hipError_t launch_leaf_tree(const float* ws_sum, const float* ws_sq, int64_t n_out, int n_leaf, float* out_sum,
+                            float* out_sq, hipStream_t stream);
+
 hipError_t launch_quantize_rows(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q, int64_t ldq,
                                 float* scale, bool vec, hipStream_t stream);
 hipError_t launch_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
@@ -105,5 +121,9 @@ hipError_t launch_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t
 // which tile shapes the GEMM kernel is instantiated for
 hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
 bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct, int stages);
+// tiles built with the fused reductions (pipelined path, S = 1)
+bool gemm_bf16_red_has_tile(int bm, int bn, int waves_m, int waves_n, int stages);
+hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                                   const uint16_t* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream);
 
 }  // namespace bg

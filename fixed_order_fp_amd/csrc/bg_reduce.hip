@@ -310,6 +310,50 @@ hipError_t launch_col_blocks(const float* ws, int64_t cols, int nb, float* out_s
     return hipGetLastError();
 }
 
+// ---- leaf sums written by another kernel (the GEMM epilogue) ----------------
+// ws_sum / ws_sq hold one fp32 leaf node per leaf and output, [leaf][n_out].
+// A workgroup of 16 waves takes 64 adjacent outputs; wave p folds the aligned
+// runs of 32 leaves p and p + 16 (exact level-5 subtrees of the balanced tree;
+// at most 32 runs: 1024 leaves, one round for up to 512), with the loads of
+// both outputs in flight at once, and the run roots are paired through LDS as
+// the tree's top levels.
+__global__ __launch_bounds__(1024) void leaf_tree_kernel(const float* __restrict__ ws_sum,
+                                                         const float* __restrict__ ws_sq, int64_t n_out,
+                                                         int n_leaf, float* __restrict__ out_sum,
+                                                         float* __restrict__ out_sq)
+{
+    __shared__ float part[2][32][64];
+    const int lane = threadIdx.x & 63;
+    const int p = threadIdx.x >> 6;
+    const int64_t o = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t oc = o < n_out ? o : n_out - 1;  // past the last output: a valid re-read, never stored
+    const int n_runs = (n_leaf + 31) / 32;
+    for (int r = p; r < n_runs; r += 16) {
+        const int first = r * 32;
+        const int n = n_leaf - first < 32 ? n_leaf - first : 32;
+        float vs[32], vq[32];
+#pragma unroll
+        for (int b = 0; b < 32; b++) {
+            const int64_t at = (int64_t)(first + (b < n ? b : n - 1)) * n_out + oc;
+            vs[b] = ws_sum ? ws_sum[at] : 0.0f;
+            vq[b] = ws_sq ? ws_sq[at] : 0.0f;
+        }
+        part[0][r][lane] = tree_upto<32>(vs, n);
+        part[1][r][lane] = tree_upto<32>(vq, n);
+    }
+    __syncthreads();
+    if (p == 0 && o < n_out) {
+        float rs[32], rq[32];
+#pragma unroll
+        for (int r = 0; r < 32; r++) {
+            rs[r] = r < n_runs ? part[0][r][lane] : 0.0f;
+            rq[r] = r < n_runs ? part[1][r][lane] : 0.0f;
+        }
+        if (out_sum) out_sum[o] = tree_upto<32>(rs, n_runs);
+        if (out_sq) out_sq[o] = tree_upto<32>(rq, n_runs);
+    }
+}
+
 // ---- column axis ------------------------------------------------------------
 // A workgroup of 4 waves covers 64 * CPL adjacent columns (CPL * sizeof(T) =
 // 16 or 8 bytes per lane) and 4 * LPWAVE consecutive leaves starting at leaf
@@ -760,6 +804,14 @@ hipError_t launch_reduce_free(int axis, bool bf16, int64_t rows, int64_t cols, c
     else
         hipLaunchKernelGGL(free_col_kernel<float>, grid, block, 0, stream, (const float*)X, ldx, rows, cols, rows_per,
                            out_sum, out_sq);
+    return hipGetLastError();
+}
+
+hipError_t launch_leaf_tree(const float* ws_sum, const float* ws_sq, int64_t n_out, int n_leaf, float* out_sum,
+                            float* out_sq, hipStream_t stream)
+{
+    dim3 grid((unsigned)((n_out + 63) / 64)), block(1024);
+    hipLaunchKernelGGL(leaf_tree_kernel, grid, block, 0, stream, ws_sum, ws_sq, n_out, n_leaf, out_sum, out_sq);
     return hipGetLastError();
 }
 

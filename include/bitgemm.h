@@ -236,6 +236,29 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
                             void* Y, int64_t ldy, int32_t* acc_out, int64_t ld_acc,
                             hipStream_t stream);
 
+/* ---- GEMM with fused reductions of C -------------------------------------- */
+
+/* C = A * B^T exactly as bg_gemm_bf16 (split_k must be 1; the 32x32x16
+ * instruction), plus a fixed-order reduction of the fp32 C values -- the
+ * accumulators before any rounding to out_type -- along one axis, in the
+ * tree bg_reduce_tree applies ([T] 3.1 and 5.1; [T]'s evaluation of
+ * performance cost, Figures 5(b) and 6, fuses such epilogues, among them the
+ * column sum a matrix-multiply epilogue emits): rd->axis COL gives one output per
+ * column n over the rows of C (a bias-gradient style column sum), ROW one per
+ * row m over its columns (norm statistics); leaves of 32 consecutive elements
+ * folded in index order with no seed, then a balanced tree over the leaves.
+ * The result equals bg_reduce_tree(rd) applied to the fp32 C of the same
+ * GEMM.  rd->in_type must be FP32; the reduced axis holds at most 1024 leaves.
+ * out_sum / out_sumsq: fp32 [N] (COL) or [M] (ROW), NULL where rd->op leaves
+ * them out.  ws: at least bg_gemm_bf16_reduce_workspace_bytes() bytes, 4-byte
+ * aligned (one fp32 node per leaf and output).  M or N = 0 enqueues nothing
+ * and writes no output. */
+bg_status bg_gemm_bf16_reduce_workspace_bytes(const bg_gemm_desc* d, const bg_reduce_desc* rd, int64_t M,
+                                              int64_t N, int64_t K, size_t* bytes);
+bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, int64_t M, int64_t N, int64_t K,
+                              const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                              float* out_sum, float* out_sumsq, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- int8 quantisation on either side of W8A8 ----------------------------- */
 
 /* Per-token int8 quantisation of activations (the input of bg_gemm_w8a8_pow2;
