@@ -92,6 +92,13 @@ def lib():
         L.or_pow2_scale.argtypes = [C.c_float, C.c_int]
         L.or_requantize_pow2.argtypes = [C.c_int64, C.c_int64, P, C.c_int64, P, C.c_int, P, C.c_int64, P,
                                          C.c_int32]
+        L.or_ozaki_gemm.restype = C.c_int
+        L.or_ozaki_gemm.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int, P, C.c_int64, P, C.c_int64, C.c_int,
+                                    P, C.c_int64, C.c_int32]
+        L.or_ozaki_slice_row.restype = C.c_int
+        L.or_ozaki_slice_row.argtypes = [C.c_int64, C.c_int, P, P]
+        L.or_bf16_from_f64.restype = C.c_uint16
+        L.or_bf16_from_f64.argtypes = [C.c_double]
         L.or_abi_version.restype = C.c_int
         _lib = L
     return _lib
@@ -334,6 +341,40 @@ def requantize_pow2(W, w_scale, mode="nearest", threads=None):
     lib().or_requantize_pow2(N, K, _ptr(W), K, _ptr(s), POW2_MODES[mode], _ptr(W2), K, _ptr(s2),
                              threads or default_threads())
     return W2, s2
+
+
+# --------------------------------------------------------------------------
+# Ozaki-scheme GEMM
+# --------------------------------------------------------------------------
+def ozaki_gemm(A, B, in_type="fp32", out_type="fp32", threads=None):
+    """C = A B^T by four 7-bit slices per operand row, exact integer slice
+    products and a fixed-order fp64 recombination rounded once.  A, B: float32
+    arrays, or uint16 bf16 bits with in_type='bf16'.  Returns float32 or
+    uint16 (bf16 bits)."""
+    dt = np.uint16 if in_type == "bf16" else np.float32
+    A = np.ascontiguousarray(A, dtype=dt)
+    B = np.ascontiguousarray(B, dtype=dt)
+    M, K = A.shape
+    N = B.shape[0]
+    C_out = np.empty((M, N), dtype=np.uint16 if out_type == "bf16" else np.float32)
+    rc = lib().or_ozaki_gemm(M, N, K, int(in_type == "bf16"), _ptr(A), K, _ptr(B), K, int(out_type == "bf16"),
+                             _ptr(C_out), N, threads or default_threads())
+    if rc != 0:
+        raise OverflowError("a slice product left the int32 range")
+    return C_out
+
+
+def ozaki_slice_row(x, in_type="fp32"):
+    """(q int8 [4][K], e) for one row."""
+    dt = np.uint16 if in_type == "bf16" else np.float32
+    x = np.ascontiguousarray(x, dtype=dt)
+    q = np.empty((4, x.size), dtype=np.int8)
+    e = lib().or_ozaki_slice_row(x.size, int(in_type == "bf16"), _ptr(x), _ptr(q))
+    return q, e
+
+
+def bf16_from_f64(v):
+    return int(lib().or_bf16_from_f64(float(v)))
 
 
 # --------------------------------------------------------------------------

@@ -512,6 +512,97 @@ void or_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, cons
 }
 
 /* ------------------------------------------------------------------------ */
+/* Ozaki-scheme GEMM                                                        */
+/* ------------------------------------------------------------------------ */
+static double ozaki_elem(int in_bf16, const void* x, int64_t k)
+{
+    if (in_bf16) return (double)or_f32_from_bf16(((const uint16_t*)x)[k]);
+    return (double)((const float*)x)[k];
+}
+
+int or_ozaki_slice_row(int64_t K, int in_bf16, const void* x, int8_t* q)
+{
+    double amax = 0.0;
+    for (int64_t k = 0; k < K; k++) {
+        double a = fabs(ozaki_elem(in_bf16, x, k));
+        if (a > amax) amax = a;
+    }
+    int e = 0;
+    if (amax > 0.0) (void)frexp(amax, &e); /* amax in [2^(e-1), 2^e) */
+    for (int64_t k = 0; k < K; k++) {
+        double r = ldexp(ozaki_elem(in_bf16, x, k), -e); /* exact; |r| < 1 */
+        for (int s = 0; s < 4; s++) {
+            r = r * 128.0;         /* exact */
+            double t = trunc(r);   /* |t| <= 127 */
+            q[s * K + k] = (int8_t)t;
+            r = r - t;             /* exact */
+        }
+    }
+    return e;
+}
+
+uint16_t or_bf16_from_f64(double v)
+{
+    if (v != v) return 0x7fc0;
+    double a = fabs(v);
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    int ulp_e = e - 8;                  /* bf16 keeps 8 significant bits */
+    if (ulp_e < -133) ulp_e = -133;     /* subnormal spacing 2^-133 */
+    double m = ldexp(a, -ulp_e);        /* exact */
+    double r = nearbyint(m);            /* ties to even (default rounding mode) */
+    double y = ldexp(r, ulp_e);
+    float f = (float)y;                 /* exact: y has at most 8 significant bits */
+    if (y >= 0x1p128) f = INFINITY;
+    uint32_t u = f32_bits(f);
+    return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7fff));
+}
+
+int or_ozaki_gemm(int64_t M, int64_t N, int64_t K, int in_bf16, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, int out_bf16, void* C, int64_t ldc, int32_t n_threads)
+{
+    const size_t esz = in_bf16 ? 2 : 4;
+    int8_t* qa = (int8_t*)malloc((size_t)(M > 0 ? M : 1) * 4 * (size_t)(K > 0 ? K : 1));
+    int8_t* qb = (int8_t*)malloc((size_t)(N > 0 ? N : 1) * 4 * (size_t)(K > 0 ? K : 1));
+    int* ea = (int*)malloc(sizeof(int) * (size_t)(M > 0 ? M : 1));
+    int* eb = (int*)malloc(sizeof(int) * (size_t)(N > 0 ? N : 1));
+    for (int64_t m = 0; m < M; m++)
+        ea[m] = or_ozaki_slice_row(K, in_bf16, (const char*)A + (size_t)m * (size_t)lda * esz, qa + m * 4 * K);
+    for (int64_t n = 0; n < N; n++)
+        eb[n] = or_ozaki_slice_row(K, in_bf16, (const char*)B + (size_t)n * (size_t)ldb * esz, qb + n * 4 * K);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 64) num_threads(n_threads > 0 ? n_threads : 1) reduction(| : bad)
+    for (int64_t i = 0; i < M * N; i++) {
+        int64_t m = i / N, n = i % N;
+        int64_t acc[4][4];
+        for (int s = 0; s < 4; s++)
+            for (int t = 0; t < 4; t++) {
+                int64_t a = 0;
+                for (int64_t k = 0; k < K; k++) a += (int64_t)qa[m * 4 * K + s * K + k] * qb[n * 4 * K + t * K + k];
+                if (a > INT32_MAX || a < INT32_MIN) bad = 1;
+                acc[s][t] = a;
+            }
+        double v = 0.0;
+        for (int lev = 6; lev >= 0; lev--)
+            for (int s = 0; s < 4; s++) {
+                int t = lev - s;
+                if (t < 0 || t > 3) continue;
+                v = v + ldexp((double)acc[s][t], -7 * (lev + 2));
+            }
+        v = ldexp(v, ea[m] + eb[n]);
+        if (out_bf16) ((uint16_t*)C)[m * ldc + n] = or_bf16_from_f64(v);
+        else ((float*)C)[m * ldc + n] = (float)v;
+    }
+    free(qa);
+    free(qb);
+    free(ea);
+    free(eb);
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* fixed-order reductions                                                   */
 /* ------------------------------------------------------------------------ */
 static float load_x(int in_type, const void* X, int64_t idx)

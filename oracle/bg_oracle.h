@@ -179,6 +179,25 @@ float or_pow2_scale(float s, int mode);
 void or_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
                         int mode, int8_t* W2, int64_t ldw2, float* w_scale2, int32_t n_threads);
 
+/* ---- Ozaki-scheme GEMM ("GPU Mechanism", exact GEMM by error-free
+ * transformation, intervention (a)) -------------------------------------
+ * C = A B^T with A [M][K], B [N][K] (fp32, or bf16 bits when in_bf16).  Each
+ * row x of A and of B: e = the frexp exponent of max |x| (0 for a zero row);
+ * r = x * 2^-e in [-1, 1); for s = 0..3: r = r * 128, q_s = trunc(r) (an int8
+ * in [-127, 127]), r = r - q_s.  For each output and each slice pair (s, t):
+ * acc_st = sum_k qA_s[m][k] * qB_t[n][k] exactly (an integer: no order).  The
+ * value sum over pairs of acc_st * 2^(-7 (s + t + 2)) is added in fp64 in the
+ * fixed order s + t = 6, 5, ..., 0 (least significant first), s ascending
+ * within a level; it is scaled by 2^(eA_m + eB_n) and rounded once to the
+ * output (fp32, or bf16 when out_bf16; round to nearest even).  Returns -1
+ * if a slice product left the int32 range (K > 133,144). */
+int or_ozaki_gemm(int64_t M, int64_t N, int64_t K, int in_bf16, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, int out_bf16, void* C, int64_t ldc, int32_t n_threads);
+/* The slicing of one row (K elements): q [4][K] int8, returns e. */
+int or_ozaki_slice_row(int64_t K, int in_bf16, const void* x, int8_t* q);
+/* double -> bf16 bits, one rounding (nearest even). */
+uint16_t or_bf16_from_f64(double v);
+
 /* ---- fixed-order reductions ---------------------------------------------
  * out[i] = balanced tree over leaf sums; a leaf is leaf_len consecutive
  * elements of the reduced axis folded in index order with no +0 seed

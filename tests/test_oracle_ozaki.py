@@ -1,0 +1,129 @@
+"""Pins for the oracle's Ozaki-scheme GEMM ("GPU Mechanism", exact GEMM by
+error-free transformation: four 7-bit integer slices per operand scaled by
+powers of two from frexp, exact integer slice products, a fixed-order fp64
+recombination and one rounding).  Each check is a fact the scheme fixes: the
+slices rebuild the rows they came from, integer accumulation makes the result
+independent of the k order, inputs the slices hold exactly give the exactly
+rounded product, power-of-two row scaling passes straight through, and the
+single rounding from fp64 to bf16 is not a rounding through fp32."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+
+def exact_rounded_f32(a_row, b_row):
+    """sum_k a_k b_k as an exact fraction, rounded once to float32."""
+    s = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a_row, b_row))
+    return np.float32(float(s)) if s == 0 else _rne32(s)
+
+
+def _rne32(fr):
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - 23)
+    q, r = divmod(a, ulp)
+    if r * 2 > ulp or (r * 2 == ulp and q % 2 == 1):
+        q += 1
+    return np.float32(sign * float(q * ulp))
+
+
+def test_slices_rebuild_rows_they_hold():
+    """A row whose elements all lie within 28 bits below its largest is cut
+    exactly: sum_s q_s 2^(-7(s+1)) 2^e gives it back, every q_s in [-127, 127]."""
+    rng = np.random.default_rng(1)
+    x = (rng.integers(-2 ** 20, 2 ** 20, 300) * 2.0 ** -30).astype(np.float32)
+    x[0] = np.float32(2.0 ** -10 * 0.99)  # the largest magnitude
+    q, e = oracle.ozaki_slice_row(x)
+    assert np.abs(q).max() <= 127
+    back = sum(q[s].astype(np.float64) * 2.0 ** (-7 * (s + 1)) for s in range(4)) * 2.0 ** e
+    assert np.array_equal(back, x.astype(np.float64))
+
+
+def test_zero_row_and_signs():
+    q, e = oracle.ozaki_slice_row(np.zeros(9, np.float32))
+    assert e == 0 and not q.any()
+    x = synth.f32_normal(2, (1, 64))[0]
+    q1, e1 = oracle.ozaki_slice_row(x)
+    q2, e2 = oracle.ozaki_slice_row(-x)
+    assert e1 == e2 and np.array_equal(q2, -q1)   # truncation toward zero is odd
+
+
+def test_small_integers_are_exact():
+    """Integer entries up to 127: one slice holds them, every slice product is
+    exact and the fp64 sum is exact, so C is the integer product."""
+    rng = np.random.default_rng(3)
+    A = rng.integers(-127, 128, (20, 200)).astype(np.float32)
+    B = rng.integers(-127, 128, (30, 200)).astype(np.float32)
+    C = oracle.ozaki_gemm(A, B)
+    assert np.array_equal(C.astype(np.int64), A.astype(np.int64) @ B.astype(np.int64).T)
+
+
+def test_k_order_does_not_matter():
+    """Permuting k in both operands leaves every bit: the slice products are
+    integers, whose sum has no order."""
+    A = synth.f32_spread(4, (16, 333), -8, 8)
+    B = synth.f32_spread(5, (24, 333), -8, 8)
+    C = oracle.ozaki_gemm(A, B)
+    for seed in range(3):
+        p = np.random.default_rng(seed).permutation(333)
+        Cp = oracle.ozaki_gemm(A[:, p], B[:, p])
+        assert np.array_equal(C.view(np.uint32), Cp.view(np.uint32))
+
+
+def test_held_inputs_give_the_exactly_rounded_product():
+    """bf16 entries whose exponents lie within 20 of their row's largest are
+    held exactly by the slices; with K small the fp64 sum is exact too, so C
+    is the exact dot product rounded once."""
+    rng = np.random.default_rng(6)
+    A = synth.bf16_spread(7, (6, 24), -10, 10)
+    B = synth.bf16_spread(8, (7, 24), -10, 10)
+    C = oracle.ozaki_gemm(A, B, in_type="bf16")
+    Af, Bf = synth.bf16_bits_to_f32(A), synth.bf16_bits_to_f32(B)
+    for m in range(6):
+        for n in range(7):
+            assert C[m, n] == exact_rounded_f32(Af[m], Bf[n])
+    del rng
+
+
+def test_power_of_two_row_scaling_passes_through():
+    A = synth.f32_normal(9, (8, 128))
+    B = synth.f32_normal(10, (9, 128))
+    C = oracle.ozaki_gemm(A, B)
+    for j in (-7, 3, 20):
+        Cs = oracle.ozaki_gemm(np.ldexp(A, j).astype(np.float32), B)
+        assert np.array_equal(Cs, np.ldexp(C, j).astype(np.float32))
+
+
+def test_accuracy_is_fp32_class():
+    """Against a float64 product: within a few units of 2^-28 of sum |a||b|
+    (what the slices drop) plus the final rounding."""
+    A = synth.f32_normal(11, (32, 1000))
+    B = synth.f32_normal(12, (40, 1000))
+    C = oracle.ozaki_gemm(A, B).astype(np.float64)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    bound = np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T * 2.0 ** -26 + np.abs(ref) * 2.0 ** -24
+    assert np.all(np.abs(C - ref) <= bound)
+
+
+def test_one_rounding_to_bf16():
+    """From fp64 to bf16 in one step: equal to torch's fp32 -> bf16 cast for
+    values that are floats, and different from a rounding through fp32 where
+    that second rounding would land on a tie."""
+    rng = np.random.default_rng(13)
+    f = (rng.standard_normal(2000) * np.exp(rng.uniform(-40, 40, 2000))).astype(np.float32)
+    f[:4] = [np.float32(1e-40), np.float32(-3e38), np.float32(0.0), np.float32(-0.0)]
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_from_f64(float(v)) for v in f], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -40   # just above the bf16 tie between 1 and 1 + 2^-7
+    assert oracle.bf16_from_f64(v) == 0x3F81          # one rounding: up
+    assert oracle.bf16_from_f64(float(np.float32(v))) == 0x3F80   # through fp32 it would tie down to even
+    assert oracle.bf16_from_f64(3.5e38) == 0x7F80     # past the largest bf16: infinity
