@@ -431,6 +431,43 @@ def gemm_reduce_extras(X, W, args, torch, bg, ms_plain):
     return out
 
 
+def ozaki_extra(X, W, args, torch, bg, ms_plain):
+    """The headline shape through the Ozaki-scheme GEMM (bf16 in, bf16 out):
+    its time against the order-fixed bf16 GEMM, the int8 rate of its 16
+    slice products, and sampled outputs against the oracle (the slicing is
+    per row, so the oracle runs on the sampled rows and columns only)."""
+    import numpy as np
+    import oracle
+    M, K = X.shape
+    N = W.shape[0]
+    dX = torch.from_numpy(X.view(np.int16)).cuda()
+    dW = torch.from_numpy(W.view(np.int16)).cuda()
+    rot = Rotation([dX, dW])
+    dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = torch.empty(bg.gemm_ozaki_workspace_bytes(M, N, K) // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def fn():
+        a, b = rot.next()
+        bg.gemm_ozaki(a, b, dC, "bf16", "bf16", ws)
+
+    fn()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    mi = np.sort(rng.choice(M, 4, replace=False))
+    ni = np.sort(rng.choice(N, 32, replace=False))
+    Co = oracle.ozaki_gemm(X[mi], W[ni], in_type="bf16", out_type="bf16")
+    got = dC.cpu().numpy().view(np.uint16)[np.ix_(mi, ni)]
+    bad = int(np.sum(got != Co))
+    t, _ = time_steps(fn, max(5, args.steps // 5), max(3, args.warmup // 20), torch)
+    flops = 2.0 * M * N * K
+    log(f"bench: Ozaki GEMM {t * 1e3:.1f} us ({t / ms_plain:.1f}x the order-fixed bf16 GEMM)")
+    return {"ozaki_gemm_4000x9728x2560": {
+        "us": round(t * 1e3, 2), "TFLOP/s": round(flops / t / 1e9, 2),
+        "int8_TOP/s": round(16 * flops / t / 1e9, 2), "over_fixed_bf16_time": round(t / ms_plain, 3),
+        "inputs": rot.note(), "workspace_MB": round(ws.numel() * 4 / 1e6, 1),
+        "parity": {"sampled_outputs": int(len(mi) * len(ni)), "mismatches": bad}}}
+
+
 def quant_extras(args, torch, bg, synth):
     """Per-token int8 quantisation of the W8A8 activations (1024 x 2048 fp32)
     and power-of-two requantisation of its weights (6144 x 2048 int8), both
@@ -696,6 +733,7 @@ def main():
         extra.update(w8a8_extra(args, torch, bg, synth))
         extra.update(quant_extras(args, torch, bg, synth))
         extra.update(gemm_reduce_extras(X, W, args, torch, bg, ms))
+        extra.update(ozaki_extra(X, W, args, torch, bg, ms))
         extra.update(reduce_extras(args, torch, bg, synth))
     if extra:
         line["extra"] = extra

@@ -91,6 +91,10 @@ _SYMBOLS = {
     "bg_gemm_bf16_reduce": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
                                       C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "bg_gemm_ozaki_workspace_bytes": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_void_p]),
+    "bg_gemm_ozaki": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_uint32, C.c_void_p, C.c_int64, C.c_void_p,
+                                C.c_int64, C.c_uint32, C.c_void_p, C.c_int64, C.c_void_p, C.c_size_t,
+                                C.c_void_p]),
     "bg_quantize_act_int8": (C.c_int, [C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_int64,
                                        C.c_void_p, C.c_void_p]),
     "bg_requantize_weights_pow2": (C.c_int, [C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
@@ -287,6 +291,21 @@ def gemm_bf16_reduce(desc, rdesc, A, B, C_out, out_sum=None, out_sumsq=None, ws=
                                      B.stride(0), _ptr(C_out), C_out.stride(0), _ptr(out_sum), _ptr(out_sumsq),
                                      _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+def gemm_ozaki_workspace_bytes(M, N, K):
+    n = C.c_size_t(0)
+    _check(lib().bg_gemm_ozaki_workspace_bytes(M, N, K, C.byref(n)))
+    return n.value
+
+
+def gemm_ozaki(A, B, C_out, in_type, out_type, ws, stream=None):
+    """C = A B^T by the Ozaki scheme (int8 slices, exact integer products)."""
+    M, K = A.shape
+    N = B.shape[0]
+    _check(lib().bg_gemm_ozaki(M, N, K, DTYPE[in_type], _ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                               DTYPE[out_type], _ptr(C_out), C_out.stride(0), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def quantize_act_int8(X, Q, a_scale, stream=None):

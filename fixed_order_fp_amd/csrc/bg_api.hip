@@ -637,6 +637,64 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
     return BG_OK;
 }
 
+static size_t align16z(size_t x) { return (x + 15) & ~(size_t)15; }
+
+bg_status bg_gemm_ozaki_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes)
+{
+    if (!bytes) return fail(BG_E_INVALID, "NULL argument");
+    if (M < 0 || N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
+    const size_t Kp = (size_t)((K + 15) / 16 * 16);
+    *bytes = align16z(4 * (size_t)M * Kp) + align16z(4 * (size_t)N * Kp) + align16z(4 * (size_t)M) +
+             align16z(4 * (size_t)N) + 16 * (size_t)M * (size_t)N * 4;
+    return BG_OK;
+}
+
+bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, uint32_t out_type, void* C, int64_t ldc, void* ws,
+                        size_t ws_bytes, hipStream_t stream)
+{
+    if (in_type != BG_FP32 && in_type != BG_BF16) return fail(BG_E_INVALID, "in_type must be fp32 or bf16");
+    if (out_type != BG_FP32 && out_type != BG_BF16) return fail(BG_E_INVALID, "out_type must be fp32 or bf16");
+    if (M < 0 || N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
+    if (M > 0x1fffffff || N > 0x1fffffff) return fail(BG_E_UNSUPPORTED, "M and N must stay below 2^29");
+    const int64_t Kp = (K + 15) / 16 * 16;
+    if (Kp > 133144) return fail(BG_E_UNSUPPORTED, "K above 133,144 could leave the int32 range");
+    if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");
+    const uintptr_t ea = in_type == BG_BF16 ? 1u : 3u, ec = out_type == BG_BF16 ? 1u : 3u;
+    if (((uintptr_t)A & ea) || ((uintptr_t)B & ea) || ((uintptr_t)C & ec))
+        return fail(BG_E_ALIGN, "A, B and C must be aligned to their element size");
+    size_t need = 0;
+    (void)bg_gemm_ozaki_workspace_bytes(M, N, K, &need);
+    if (!ws || ws_bytes < need) return fail(BG_E_WORKSPACE, "the Ozaki GEMM needs a workspace");
+    if (!aligned16(ws)) return fail(BG_E_ALIGN, "workspace must be 16-byte aligned");
+    bg::OzakiWs w{};
+    w.Kp = Kp;
+    char* base = (char*)ws;
+    w.qa = (int8_t*)base;
+    base += align16z(4 * (size_t)M * (size_t)Kp);
+    w.qb = (int8_t*)base;
+    base += align16z(4 * (size_t)N * (size_t)Kp);
+    w.ea = (int*)base;
+    base += align16z(4 * (size_t)M);
+    w.eb = (int*)base;
+    base += align16z(4 * (size_t)N);
+    w.acc = (int32_t*)base;
+    // speed only: the pipelined int8 tiles (every shape gives the same integers)
+    bg::W8A8Plan p{};
+    p.mfma = BG_MFMA_I32_32X32X32_I8;
+    const bool big = ((4 * M + 127) / 128) * ((4 * N + 127) / 128) >= 192;
+    p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
+    p.path = 2, p.stages = big ? 5 : 8;
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_ozaki(p, M, N, K, in_type == BG_BF16, A, lda, B, ldb, out_type == BG_BF16, C, ldc, w,
+                                    stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
 bg_status bg_quantize_act_int8(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q, int64_t ldq,
                                float* a_scale, hipStream_t stream)
 {

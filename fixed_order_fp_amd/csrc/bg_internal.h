@@ -92,6 +92,21 @@ hipError_t launch_w8a8(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const
                        const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
                        int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream);
 
+// Ozaki-scheme GEMM workspace: slices [4][M][Kp] and [4][N][Kp] int8, row
+// exponents, the stacked int32 products [4M][4N].
+struct OzakiWs {
+    int64_t Kp;
+    int8_t* qa;
+    int8_t* qb;
+    int* ea;
+    int* eb;
+    int32_t* acc;
+};
+// Y == nullptr: the int32 accumulators only (pipelined tiles)
+hipError_t launch_ozaki(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, bool in_bf16, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, bool out_bf16, void* C, int64_t ldc, const OzakiWs& w,
+                        hipStream_t stream);
+
 struct ReducePlan {
     int axis;          // BG_AXIS_ROW | BG_AXIS_COL
     bool bf16;         // input type

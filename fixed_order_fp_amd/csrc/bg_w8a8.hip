@@ -204,7 +204,9 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
 // columns at a time and stages the bf16 tile in LDS for row-contiguous
 // 16-byte stores.  A short last k tile (K not a multiple of 64) is copied
 // through registers with zeros past K.
-template <int BM, int BN, int WM, int WN, int NS, bool ACC_OUT>
+// MODE 0: Y; 1: Y and the int32 accumulators; 2: the accumulators only (no
+// scales, no Y: the integer products other paths build on)
+template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
     PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU)))
 void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* __restrict__ W, int64_t ldw,
@@ -349,32 +351,36 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
 
     // epilogue: block (j, i), element 4q+u of lane l is row m = wm*WTM + 32i +
     // l%32, column n = wn*WTN + 32j + 8q + 4(l/32) + u
+    constexpr bool WANT_Y = MODE != 2, WANT_ACC = MODE != 0;
     __syncthreads();  // every wave is done with the operand stages
     unsigned char* cl = (unsigned char*)lds;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const int m = wm * WTM + i * 32 + r_in;
         const int64_t gm = m0 + m;
-        const float as = a_scale[gm < M ? gm : M - 1];
+        float as = 0.0f;
+        if constexpr (WANT_Y) as = a_scale[gm < M ? gm : M - 1];
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int n = wn * WTN + j * 32 + 8 * q;  // chunk n/8; lane half h takes bytes 8h..8h+7
                 const int64_t gn = n0 + n + 4 * h;
-                float y[4];
+                if constexpr (WANT_Y) {
+                    float y[4];
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const float ws = w_scale[gn + u < N ? gn + u : N - 1];
-                    const float f = (float)acc[j][i][4 * q + u];  // v_cvt_f32_i32: round to nearest even
-                    const float tt = f * ws;                       // exact: a power of two
-                    y[u] = tt * as;                                // the one rounding
+                    for (int u = 0; u < 4; u++) {
+                        const float ws = w_scale[gn + u < N ? gn + u : N - 1];
+                        const float f = (float)acc[j][i][4 * q + u];  // v_cvt_f32_i32: round to nearest even
+                        const float tt = f * ws;                       // exact: a power of two
+                        y[u] = tt * as;                                // the one rounding
+                    }
+                    uint2 w;
+                    w.x = bf16x2_rne(y[0], y[1]);
+                    w.y = bf16x2_rne(y[2], y[3]);
+                    *(uint2*)(cl + m * (BN * 2) + c_swizzle<CHR>(n / 8, m) * 16 + h * 8) = w;
                 }
-                uint2 w;
-                w.x = bf16x2_rne(y[0], y[1]);
-                w.y = bf16x2_rne(y[2], y[3]);
-                *(uint2*)(cl + m * (BN * 2) + c_swizzle<CHR>(n / 8, m) * 16 + h * 8) = w;
-                if constexpr (ACC_OUT) {
+                if constexpr (WANT_ACC) {
                     if (gm < M && gn < N) {
                         int32_t* pa = acc_out + gm * ld_acc + gn;
                         if (gn + 4 <= N) {
@@ -387,16 +393,18 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
                 }
             }
     }
-    __syncthreads();
-    for (int c = tid; c < BM * CHR; c += NT) {
-        const int row = c / CHR, ch = c % CHR;
-        const int64_t gm = m0 + row, gn = n0 + ch * 8;
-        if (gm >= M || gn >= N) continue;
-        const u32x4 v = *(const u32x4*)(cl + row * (BN * 2) + c_swizzle<CHR>(ch, row) * 16);
-        if (gn + 8 <= N) {
-            *(u32x4*)(Y + gm * ldy + gn) = v;
-        } else {
-            for (int u = 0; u < 8 && gn + u < N; u++) Y[gm * ldy + gn + u] = (uint16_t)(v[u / 2] >> (16 * (u % 2)));
+    if constexpr (WANT_Y) {
+        __syncthreads();
+        for (int c = tid; c < BM * CHR; c += NT) {
+            const int row = c / CHR, ch = c % CHR;
+            const int64_t gm = m0 + row, gn = n0 + ch * 8;
+            if (gm >= M || gn >= N) continue;
+            const u32x4 v = *(const u32x4*)(cl + row * (BN * 2) + c_swizzle<CHR>(ch, row) * 16);
+            if (gn + 8 <= N) {
+                *(u32x4*)(Y + gm * ldy + gn) = v;
+            } else {
+                for (int u = 0; u < 8 && gn + u < N; u++) Y[gm * ldy + gn + u] = (uint16_t)(v[u / 2] >> (16 * (u % 2)));
+            }
         }
     }
 }
@@ -409,11 +417,14 @@ hipError_t launch_pipe(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
     dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
-    if (acc_out)
-        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, true>), grid, block, 0, stream, A, lda, W, ldw,
+    if (!Y)
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, stream, A, lda, W, ldw,
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+    else if (acc_out)
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, stream, A, lda, W, ldw,
                            a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
     else
-        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, false>), grid, block, 0, stream, A, lda, W, ldw,
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, stream, A, lda, W, ldw,
                            a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
@@ -497,6 +508,7 @@ hipError_t launch_w8a8(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const
                        const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
                        int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream)
 {
+    if (!Y && p.path != 2) return hipErrorInvalidValue;  // accumulators only: the pipelined kernel
 #define BG_LAUNCH(I, BM_, BN_, WM_, WN_, P_, NS_)                                                              \
     if (p.mfma == I && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_ && p.path == P_ &&   \
         (p.stages == 0 || p.stages == NS_))                                                                    \

@@ -259,6 +259,28 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
                               const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                               float* out_sum, float* out_sumsq, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Ozaki-scheme GEMM ----------------------------------------------------- */
+
+/* C = A * B^T by error-free transformation ("GPU Mechanism", exact GEMM by
+ * error-free transformation, intervention (a)): every row of A and of B is
+ * scaled by 2^-e (e the frexp exponent of its largest magnitude; 0 for a
+ * zero row) and cut into four 7-bit integer slices, r = 128 r, q = trunc(r),
+ * r = r - q; the 16 slice products are exact int32 dot products (int8 MFMA:
+ * integer sums have no order, so the result cannot depend on tiling or CU
+ * count); per output the scaled products acc_st 2^(-7 (s + t + 2)) are added
+ * in fp64 in the fixed order s + t = 6 .. 0, s ascending within a level,
+ * scaled by 2^(eA + eB) and rounded once to out_type (nearest even).  The
+ * accuracy is fp32-class: slices keep 28 bits below each row's largest
+ * element.  Inputs must be finite.
+ * A: [M][lda], B: [N][ldb] of in_type (BG_FP32 or BG_BF16), K contiguous;
+ * C: [M][ldc] of out_type.  ws: at least bg_gemm_ozaki_workspace_bytes(),
+ * 16-byte aligned (slices, exponents and the 16 M N int32 products).
+ * M, N < 2^29; K rounded up to 16 at most 133,144. */
+bg_status bg_gemm_ozaki_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, uint32_t out_type, void* C, int64_t ldc, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 /* ---- int8 quantisation on either side of W8A8 ----------------------------- */
 
 /* Per-token int8 quantisation of activations (the input of bg_gemm_w8a8_pow2;
