@@ -658,7 +658,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
-              "(the method shards by output columns or rows with no exchange; see DESIGN.md)",
+              "(the method shards by output columns or rows with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

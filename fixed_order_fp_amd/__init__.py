@@ -173,7 +173,7 @@ def gemm_desc(spec=None, **overrides):
     the oracle share): mfma, split_k, cut_rule, cuts, cut_unit, combine,
     out_type, epilogue, a_type/b_type/acc_type, and an optional 'schedule'
     dict (bm, bn, bk, waves_m, waves_n).  Unset fields keep the library
-    defaults; the profile hash is this build's."""
+    defaults; the profile hash is the library's."""
     spec = dict(spec or {}, **overrides)
     d = GemmDesc()
     _check(lib().bg_desc_default_gemm(C.byref(d)))

@@ -2,9 +2,9 @@
 // signature, launch plans, and the entry points declared in bitgemm.h.
 //
 // A descriptor is a frozen record of the fields that decide the arithmetic;
-// two equal records owe each other the same bits ("Taming Bitwise Behavior",
+// identical records must produce identical bits ("Taming Bitwise Behavior",
 // section 4).  The schedule sub-struct is excluded from the signature: it only
-// chooses tiles and waves (section 3.2.2; appendix E).  A descriptor this build
+// chooses tiles and waves (section 3.2.2; appendix E).  A descriptor the library
 // cannot realise exactly is refused, never replaced by another order (the
 // "GPU Mechanism" page's forced-algorithm refusal).
 #include <mutex>

@@ -1,11 +1,12 @@
 // bg_ozaki.hip -- Ozaki-scheme GEMM on the int8 MFMA path (gfx950).
 //
-// "GPU Mechanism", exact GEMM by error-free transformation (intervention (a),
-// ExactGEMM): four 7-bit integer slices per operand row scaled by a power of
-// two from frexp, slice products by an exact integer GEMM, a fixed-order fp64
-// recombination and one rounding.  Integer accumulation has no order, so the
-// result cannot depend on the tile, the CU count or anything else that moves
-// a floating-point sum.
+// "GPU Mechanism", the exact-GEMM paragraph and intervention (a) (ExactGEMM):
+// each operand row is scaled by a power of two taken from frexp and cut into
+// four signed 7-bit pieces; an integer GEMM multiplies the pieces exactly;
+// the piece products are summed in fp64 in a set order and rounded once.  An
+// integer sum is the same whatever order its terms arrive in, so neither the
+// tile, the CU count nor anything else that moves a floating-point sum can
+// reach the result.
 //
 //   slicing (one workgroup per row): e = frexp exponent of max |x| (0 for a
 //     zero row); r = x * 2^-e in fp64 (exact, |r| < 1); for s = 0..3:

@@ -7,8 +7,8 @@
 // served by L2 (one row is at most a few tens of KB).
 //
 // Weights ("Deterministic LLM Inference ... Power-of-Two INT8 Quantization
-// Scales", section V: requantise the int8 weights under the constrained scale,
-// not just the scale): per output row, s2 = 2^e with e = round(log2 s)
+// Scales", section V: the int8 weights themselves are recomputed for the
+// power-of-two scale; changing the scale alone would not do): per output row, s2 = 2^e with e = round(log2 s)
 // (nearest in ratio) or ceil(log2 s); each weight becomes
 // clamp(rint(fp32(q * s) / s2), -127, 127), the product rounded once and the
 // division by a power of two exact (done as a multiplication by the exact

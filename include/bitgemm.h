@@ -10,8 +10,8 @@
  *        (arXiv 2609.11356).  3.1 dependence tree of a reduction; 3.2.1 one
  *        rounding per matrix instruction; 3.2.2 the GEMM descriptor fields
  *        (instruction_k, k_loop_step, span, k_cuts, partial_dtype,
- *        merge_dtype); 4 the frozen descriptor ("equal records owe each other
- *        the same bits") and the black-box +L/-L/r instruments; 5.1 the
+ *        merge_dtype); 4 the frozen descriptor (identical records, identical
+ *        bits) and the black-box +L/-L/r instruments; 5.1 the
  *        count-up, neighbours-first lane tree; appendix E (a descriptor fixes
  *        the arithmetic, not the schedule; host cost of a descriptor path).
  *   [E]  "GPU Arithmetic Emulator" README, "Tensor Core Matmul" (block-FMA
@@ -35,7 +35,7 @@
  *     with a message from bg_last_error() (thread-local).  A launch failure is
  *     BG_E_HIP.  No C++ exception crosses the ABI.  On any non-BG_OK status no
  *     work has been enqueued.
- *   - Refusal: a descriptor this build cannot realise exactly (an unsupported
+ *   - Refusal: a descriptor the library cannot realise exactly (an unsupported
  *     field value, a profile measured on another device) is refused with
  *     BG_E_UNSUPPORTED / BG_E_PROFILE; another order is never substituted [G].
  *   - Alignment: tensor pointers 16-byte aligned; leading dimensions a
@@ -61,11 +61,11 @@ typedef struct ihipStream_t* hipStream_t; /* the HIP runtime's stream handle */
 typedef enum {
     BG_OK = 0,
     BG_E_INVALID = 1,     /* malformed descriptor or arguments            */
-    BG_E_UNSUPPORTED = 2, /* well-formed, but this build cannot realise it */
+    BG_E_UNSUPPORTED = 2, /* well-formed, but the library cannot realise it */
     BG_E_WORKSPACE = 3,   /* workspace missing or too small               */
     BG_E_ALIGN = 4,       /* pointer or leading dimension misaligned      */
     BG_E_ARCH = 5,        /* the current device is not gfx950             */
-    BG_E_PROFILE = 6,     /* descriptor's MFMA profile is not this build's */
+    BG_E_PROFILE = 6,     /* descriptor's MFMA profile is not the library's */
     BG_E_HIP = 7          /* a HIP runtime call failed                    */
 } bg_status;
 
@@ -183,7 +183,7 @@ const char* bg_last_error(void); /* message of this thread's last failure */
 uint64_t bg_profile_hash(void);
 
 /* Fill a descriptor with the defaults: bf16 x bf16 -> fp32 acc, bf16 out,
- * 32x32x16 instruction, S = 1, balanced combine, this build's profile hash. */
+ * 32x32x16 instruction, S = 1, balanced combine, the library's profile hash. */
 bg_status bg_desc_default_gemm(bg_gemm_desc* d);
 bg_status bg_desc_default_reduce(bg_reduce_desc* d);
 
@@ -242,8 +242,8 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
  * instruction), plus a fixed-order reduction of the fp32 C values -- the
  * accumulators before any rounding to out_type -- along one axis, in the
  * tree bg_reduce_tree applies ([T] 3.1 and 5.1; [T]'s evaluation of
- * performance cost, Figures 5(b) and 6, fuses such epilogues, among them the
- * column sum a matrix-multiply epilogue emits): rd->axis COL gives one output per
+ * performance cost, Figures 5(b) and 6, fuses such epilogues, a GEMM's
+ * column sum among them): rd->axis COL gives one output per
  * column n over the rows of C (a bias-gradient style column sum), ROW one per
  * row m over its columns (norm statistics); leaves of 32 consecutive elements
  * folded in index order with no seed, then a balanced tree over the leaves.
@@ -261,13 +261,13 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
 
 /* ---- Ozaki-scheme GEMM ----------------------------------------------------- */
 
-/* C = A * B^T by error-free transformation ("GPU Mechanism", exact GEMM by
- * error-free transformation, intervention (a)): every row of A and of B is
- * scaled by 2^-e (e the frexp exponent of its largest magnitude; 0 for a
- * zero row) and cut into four 7-bit integer slices, r = 128 r, q = trunc(r),
- * r = r - q; the 16 slice products are exact int32 dot products (int8 MFMA:
- * integer sums have no order, so the result cannot depend on tiling or CU
- * count); per output the scaled products acc_st 2^(-7 (s + t + 2)) are added
+/* C = A * B^T by the Ozaki scheme ("GPU Mechanism", the exact-GEMM
+ * paragraph and intervention (a)): every row of A and of B is scaled by 2^-e
+ * (e the frexp exponent of its largest magnitude; 0 for a zero row) and cut
+ * into four signed pieces of 7 bits, r = 128 r, q = trunc(r), r = r - q; the
+ * 16 piece products are exact int32 dot products (int8 MFMA: an integer sum
+ * comes out the same whatever order its terms arrive in, so tiling and CU
+ * count cannot reach the result); per output the scaled products acc_st 2^(-7 (s + t + 2)) are added
  * in fp64 in the fixed order s + t = 6 .. 0, s ascending within a level,
  * scaled by 2^(eA + eB) and rounded once to out_type (nearest even).  The
  * accuracy is fp32-class: slices keep 28 bits below each row's largest
@@ -301,8 +301,8 @@ bg_status bg_quantize_act_int8(int64_t M, int64_t K, const float* X, int64_t ldx
 
 /* Requantisation of int8 weights to power-of-two scales ("Deterministic LLM
  * Inference ... Power-of-Two INT8 Quantization Scales", section V: the
- * weights are requantised under the constrained scale, not just the scale
- * rewritten), per output row n:
+ * int8 weights themselves are recomputed for the power-of-two scale;
+ * changing the scale alone would not do), per output row n:
  *   s2 = 2^e, e = round(log2 w_scale[n]) for BG_POW2_NEAREST (nearest in
  *   ratio; decided exactly, a tie cannot occur) or e = ceil(log2 w_scale[n])
  *   for BG_POW2_CEIL (never shrinks the scale, so nothing clips);

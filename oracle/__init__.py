@@ -347,8 +347,8 @@ def requantize_pow2(W, w_scale, mode="nearest", threads=None):
 # Ozaki-scheme GEMM
 # --------------------------------------------------------------------------
 def ozaki_gemm(A, B, in_type="fp32", out_type="fp32", threads=None):
-    """C = A B^T by four 7-bit slices per operand row, exact integer slice
-    products and a fixed-order fp64 recombination rounded once.  A, B: float32
+    """C = A B^T from four signed 7-bit pieces per operand row: the piece
+    products are exact integers, summed in fp64 in a set order, rounded once.  A, B: float32
     arrays, or uint16 bf16 bits with in_type='bf16'.  Returns float32 or
     uint16 (bf16 bits)."""
     dt = np.uint16 if in_type == "bf16" else np.float32

@@ -1,5 +1,5 @@
 """Static checks of the accumulation chains in libbitgemm's own GEMM kernels,
-read from the AMDGCN this build produces (hipcc --cuda-device-only -S).
+read from the AMDGCN the library's sources compile to (hipcc --cuda-device-only -S).
 
 The order fields of a descriptor fix, for every output, one chain of matrix
 instructions over ascending k; a schedule field (tile, waves, stages, walk,

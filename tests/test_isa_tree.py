@@ -1,5 +1,5 @@
 """Static check of every compiled GEMM variant's accumulation chains (the
-AMDGCN of this build, read by tests/isa_tree.py): one matrix instruction, the
+AMDGCN the library compiles to, read by tests/isa_tree.py): one matrix instruction, the
 descriptor's, accumulating in place; nothing else writing an accumulator in
 the k walk; the same number of instructions per accumulator per turn.  The
 planted-mistake cases show each check fires on the kind of change that would

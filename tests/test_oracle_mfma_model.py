@@ -4,7 +4,8 @@ Family E ("Taming Bitwise Behavior", section 3.2.1) is checked against the
 exact rational sum with an independently written correct rounding; family B
 (emulator README, "Tensor Core Matmul") against an independent big-integer
 restatement of its four steps.  Both draw ordinary and exponent-spread inputs,
-since narrow exponents hide a regrouping ("Taming", appendix E)."""
+because with a narrow exponent range two groupings often
+round alike ("Taming", appendix E)."""
 import itertools
 
 import numpy as np

@@ -1,7 +1,7 @@
-"""Pins for the oracle's Ozaki-scheme GEMM ("GPU Mechanism", exact GEMM by
-error-free transformation: four 7-bit integer slices per operand scaled by
-powers of two from frexp, exact integer slice products, a fixed-order fp64
-recombination and one rounding).  Each check is a fact the scheme fixes: the
+"""Pins for the oracle's Ozaki-scheme GEMM ("GPU Mechanism", the exact-GEMM
+paragraph and intervention (a): each operand row scaled by a frexp power of
+two and cut into four signed 7-bit pieces, the piece products exact integers,
+their fp64 sum taken in a set order and rounded once).  Each check is a fact the scheme fixes: the
 slices rebuild the rows they came from, integer accumulation makes the result
 independent of the k order, inputs the slices hold exactly give the exactly
 rounded product, power-of-two row scaling passes straight through, and the
