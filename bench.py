@@ -134,6 +134,40 @@ class Gemm:
         return {"sampled": int(n_points), "mismatches": bad}
 
 
+def host_cost(head, torch, bg, n=100, reps=5):
+    """Host time of one headline call through the C ABI (descriptor checks,
+    order signature, plan, launch): wall time per call over n back-to-back
+    enqueues, with the ctypes arguments built once.  The kernels queue up on
+    the GPU meanwhile (n is well inside the launch queue), so the host is not
+    held back.  The same loop over bg_abi_version, which does nothing, gives
+    the ctypes share.  Best of `reps` batches."""
+    import ctypes as C
+    lib = bg.lib()
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ws = head.ws
+    args = (C.byref(head.desc), head.M, head.N, head.K, C.c_void_p(head.dA.data_ptr()), head.dA.stride(0),
+            C.c_void_p(head.dB.data_ptr()), head.dB.stride(0), C.c_void_p(head.dC.data_ptr()), head.dC.stride(0),
+            None if ws is None else C.c_void_p(ws.data_ptr()), 0 if ws is None else ws.numel(), stream)
+    fn, noop = lib.bg_gemm_bf16, lib.bg_abi_version
+    best, best_noop = float("inf"), float("inf")
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            if fn(*args) != 0:
+                raise RuntimeError(lib.bg_last_error().decode())
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(n):
+            noop()
+        t3 = time.perf_counter()
+        best, best_noop = min(best, (t1 - t0) / n * 1e6), min(best_noop, (t3 - t2) / n * 1e6)
+    return {"host_us_per_call": round(best, 2), "ctypes_noop_us": round(best_noop, 3), "calls": n,
+            "note": "wall time per enqueue of the headline call from Python (ctypes included), best of "
+                    f"{reps} batches; the plan is derived on every call, no cache"}
+
+
 def time_steps(fn, steps, warmup, torch):
     """Warm up, then time exactly `steps` calls between synchronisations with
     HIP events recorded on the stream the kernels are launched on."""
@@ -722,6 +756,8 @@ def main():
     # by CU count, whichever is faster)
     us_free, _, free_split = free_twin_us(head, args, torch)
     ms_free = us_free / 1e3
+    line["host"] = host_cost(head, torch, bg)
+    log(f"bench: host {line['host']}")
     line["free_order"] = {"ms": round(ms_free, 5), "TFLOP/s": round(head.flops() / (ms_free * 1e-3) / 1e12, 3),
                           "fixed_over_free_time": round(ms / ms_free, 4), "split": free_split,
                           "note": "free twin writes fp32 (4 B/output) where the fixed path writes bf16"}

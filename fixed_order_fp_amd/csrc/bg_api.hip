@@ -137,6 +137,33 @@ bg_status check_common_order(const bg_gemm_desc* d)
 // latency rather than by the MFMA rate.  Needs p.S and p.cuts set.
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Speed only (int32 sums are exact in any order): the pipelined int8 tile.
+// Outputs of at least 1.5 rounds of 256x256 tiles take that tile (the fewest
+// operand bytes per product; 1.27x the 128x128 tile's rate on the stacked
+// 16000 x 38912 x 2560 product).  Below that, where 128x128 tiles give a
+// workgroup per CU, the big tile is the one that moves fewer operand bytes
+// per CU: rounds x workgroups per CU x (BM + BN), one workgroup per CU
+// (128x192, 8 waves) costing ~1.4x per byte against two (128x128, 5 stages),
+// as measured at 1024 x 6144 x 2048 with inputs not in the MALL.  Otherwise
+// deep-pipelined small tiles.
+void choose_w8a8_pipe(bg::W8A8Plan& p, int64_t M, int64_t N)
+{
+    const int64_t n_cu = 256;
+    const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), t192 = ceil_div(M, 128) * ceil_div(N, 192);
+    p.path = 2;
+    if (ceil_div(M, 256) * ceil_div(N, 256) >= n_cu * 3 / 2) {
+        p.bm = 256, p.bn = 256, p.waves_m = 2, p.waves_n = 4, p.stages = 4;
+    } else if (t128 >= 192) {
+        const double c128 = (double)ceil_div(t128, 2 * n_cu) * 2 * 256;
+        const double c192 = (double)ceil_div(t192, n_cu) * 320 * 1.4;
+        if (c192 < c128) p.bm = 128, p.bn = 192, p.waves_m = 4, p.waves_n = 2;
+        else p.bm = 128, p.bn = 128, p.waves_m = 2, p.waves_n = 2;
+        p.stages = 5;
+    } else {
+        p.bm = 64, p.bn = 64, p.waves_m = 2, p.waves_n = 2, p.stages = 8;
+    }
+}
+
 void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
 {
     auto set = [&](int bm, int bn, int bk, int wm, int wn, int direct, int stages) {
@@ -437,12 +464,7 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
         p.bm = s.bm, p.bn = s.bn, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
         p.path = path, p.stages = s.stages;
     } else if (p.mfma == BG_MFMA_I32_32X32X32_I8) {
-        // speed only: the pipelined kernel; 128x128 tiles with 5 stages (two
-        // workgroups per CU) where they give a workgroup per CU, otherwise
-        // deep-pipelined small tiles (measured with inputs not in the MALL)
-        const bool big = ((M + 127) / 128) * ((N + 127) / 128) >= 192;
-        p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
-        p.path = 2, p.stages = big ? 5 : 8;
+        choose_w8a8_pipe(p, M, N);
     } else {
         const bool big = M >= 128 && N >= 128 && ((M + 127) / 128) * ((N + 127) / 128) >= 128;
         p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
@@ -684,9 +706,7 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
     // speed only: the pipelined int8 tiles (every shape gives the same integers)
     bg::W8A8Plan p{};
     p.mfma = BG_MFMA_I32_32X32X32_I8;
-    const bool big = ((4 * M + 127) / 128) * ((4 * N + 127) / 128) >= 192;
-    p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
-    p.path = 2, p.stages = big ? 5 : 8;
+    choose_w8a8_pipe(p, 4 * M, 4 * N);
     bg_status st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_ozaki(p, M, N, K, in_type == BG_BF16, A, lda, B, ldb, out_type == BG_BF16, C, ldc, w,

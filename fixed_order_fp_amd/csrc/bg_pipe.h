@@ -94,9 +94,10 @@ __device__ __forceinline__ void wait_turns(int newer)
 template <int CHR>
 __device__ __forceinline__ int c_swizzle(int ch, int m)
 {
-    static_assert(CHR == 4 || CHR == 8 || CHR == 16 || CHR == 32 || CHR == 40,
-                  "staged row widths: 32, 64, 128, 256 or 320 columns");
+    static_assert(CHR == 4 || CHR == 8 || CHR == 16 || CHR == 24 || CHR == 32 || CHR == 40,
+                  "staged row widths: 32, 64, 128, 192, 256 or 320 columns");
     if constexpr (CHR == 40) return ch < 32 ? ch ^ (m & 31) : ch ^ (m & 7);
+    else if constexpr (CHR == 24) return ch < 16 ? ch ^ (m & 15) : ch ^ (m & 7);
     else return ch ^ (m & (CHR - 1));
 }
 

@@ -456,6 +456,10 @@ using namespace w8a8_impl;
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 4) \
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 5) \
     X(BG_MFMA_I32_32X32X32_I8, 256, 256, 2, 4, 2, 4) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 192, 2, 2, 2, 4) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 192, 2, 2, 2, 5) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 192, 2, 2, 2, 6) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 192, 4, 2, 2, 5) \
     X(BG_MFMA_I32_32X32X32_I8, 128, 64, 2, 2, 2, 8)  \
     X(BG_MFMA_I32_32X32X32_I8, 64, 64, 2, 2, 2, 8)   \
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 1, 2) \
