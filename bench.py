@@ -186,6 +186,22 @@ def time_steps(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def per_launch_ms(fn, steps, torch):
+    """Median and minimum of single-launch times: `steps` more launches, each
+    between two HIP events on its stream (a separate pass after the timed
+    one, so the contract's timed region holds launches only)."""
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return {"median": round(t[len(t) // 2], 5), "min": round(t[0], 5), "launches": steps}
+
+
 def graph_time(fn, reps, torch, replays=5):
     """Per-call time of `fn` with `reps` calls captured in one HIP graph and
     replayed, so that host launch cost is off the clock (for the short
@@ -712,6 +728,7 @@ def main():
     # them), then the timed launches proper, rotating over input copies
     ms_hot, _ = time_steps(head.run, args.steps, args.warmup, torch)
     ms, wall = time_steps(head.run_rot, args.steps, args.warmup, torch)
+    per_launch = per_launch_ms(head.run_rot, args.steps, torch)
     tflops = head.flops() / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.4f} ms per call, {tflops:.1f} TFLOP/s")
 
@@ -731,7 +748,8 @@ def main():
         "config": {"workload": "order-fixed bf16 GEMM C=A*B^T, batch-invariance sweep at M=4000 "
                                "(N=9728, K=2560), 32x32x16 bf16 MFMA, split-K 1, bf16 out",
                    "M": 4000, "N": 9728, "K": 2560, "split_k": 1, "mfma": "F32_32X32X16_BF16",
-                   "out": "bf16", "inputs": head.rot.note(), "hot_ms_per_step": round(ms_hot, 5)},
+                   "out": "bf16", "inputs": head.rot.note(), "hot_ms_per_step": round(ms_hot, 5),
+                   "per_launch_ms": per_launch},
         "parity": par,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

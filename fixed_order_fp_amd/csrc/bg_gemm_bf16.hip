@@ -467,6 +467,13 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
     // copy k tile `turn` into its stage; the short last tile (k_end not a
     // multiple of 32 past k_begin) goes through registers with zeros past
     // k_end (cut points are multiples of 8, so a chunk is all in or all out)
+    // round r of this wave's copies of a whole k tile `turn` (the last
+    // round's slots past the stage's end belong to no wave)
+    auto copy_round = [&](int turn, int r) {
+        const int s = r * NW + wave;
+        if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS)
+            dma16(src[r] + (int64_t)turn * BK, lds_base + (uint32_t)((turn % NS) * STAGE + s * 64) * 16u);
+    };
     auto issue = [&](int turn) {
         const int st = turn % NS;
         const int64_t kb = (int64_t)turn * BK;
@@ -475,7 +482,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
             const int s = r * NW + wave;
             if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS) {
                 if (turn < n_full) {
-                    dma16(src[r] + kb, lds_base + (uint32_t)(st * STAGE + s * 64) * 16u);
+                    copy_round(turn, r);
                 } else {
                     u32x4 v = {0u, 0u, 0u, 0u};
                     if (k_begin + kb + kcs[r] * kChunk < k_end) v = *(const u32x4*)(src[r] + kb);
@@ -528,6 +535,25 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
             for (int i = 0; i < TM; i++)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
     };
+    // the same products with this wave's copies of a whole k tile `turn`
+    // spread evenly among them (after instruction q of TM TN, the first
+    // ROUNDS q / (TM TN) rounds are out) instead of issued in one burst ahead
+    // of them: measured 3-5 % faster on the large tiles
+    auto mm_issue = [&](const bf16x8* a, const bf16x8* b, int turn) {
+        int q = 0, r = 0;
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+                ++q;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < ROUNDS; u++)
+                    if (r < ROUNDS && r * (TM * TN) < ROUNDS * q - (TM * TN - 1)) copy_round(turn, r++);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
 
     // prologue: tiles 0 .. NS-2 in flight, tile 0 landed and visible
 #pragma unroll
@@ -559,14 +585,17 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
         __builtin_amdgcn_s_barrier();
         // every wave is past its reads of tile t-1: its stage takes tile t+NS-1
         if constexpr (FULL) {
-            issue(t + NS - 1);
+            rd(t + 1, 0, xa[0], xb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_issue(xa[1], xb[1], t + NS - 1);
+            __builtin_amdgcn_sched_barrier(0);
         } else {
             if (t + NS - 1 < n_turns) issue(t + NS - 1);
+            rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
+            __builtin_amdgcn_sched_barrier(0);
+            mm(xa[1], xb[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
-        __builtin_amdgcn_sched_barrier(0);
-        mm(xa[1], xb[1]);
-        __builtin_amdgcn_sched_barrier(0);
     };
     const int n_steady = n_full - (NS - 1);
     int t = 0;

@@ -258,6 +258,14 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
     }
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)lds);
 
+    // round r of this wave's copies of a whole k tile `turn` (the last
+    // round's slots past the stage's end belong to no wave)
+    auto copy_round = [&](int turn, int r) {
+        const int s = r * NW + wave;
+        if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS)
+            dma16(rows[r] + (int64_t)turn * PK + kcs[r] * kChunk,
+                  lds_base + (uint32_t)((turn % NS) * STAGE + s * 64) * 16u);
+    };
     auto issue = [&](int turn) {
         const int st = turn % NS;
         const int64_t kb = (int64_t)turn * PK;
@@ -265,11 +273,10 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
         for (int r = 0; r < ROUNDS; r++) {
             const int s = r * NW + wave;
             if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS) {
-                const int64_t k = kb + kcs[r] * kChunk;
                 if (turn < n_full)
-                    dma16(rows[r] + k, lds_base + (uint32_t)(st * STAGE + s * 64) * 16u);
+                    copy_round(turn, r);
                 else
-                    lds[st * STAGE + s * 64 + lane] = load_chunk_i8(rows[r], k, K);
+                    lds[st * STAGE + s * 64 + lane] = load_chunk_i8(rows[r], kb + kcs[r] * kChunk, K);
             }
         }
     };
@@ -311,6 +318,24 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
             for (int i = 0; i < TM; i++)
                 acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j][i], 0, 0, 0);
     };
+    // the same products with this wave's copies of a whole k tile `turn`
+    // spread evenly among them (after instruction q of TM TN, the first
+    // ROUNDS q / (TM TN) rounds are out) instead of issued in one burst
+    auto mm_issue = [&](const i32x4* a, const i32x4* b, int turn) {
+        int q = 0, r = 0;
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j][i], 0, 0, 0);
+                ++q;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < ROUNDS; u++)
+                    if (r < ROUNDS && r * (TM * TN) < ROUNDS * q - (TM * TN - 1)) copy_round(turn, r++);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
 
 #pragma unroll
     for (int s = 0; s < NS - 1; s++)
@@ -335,14 +360,17 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
         }
         __builtin_amdgcn_s_barrier();
         if constexpr (FULL) {
-            issue(t + NS - 1);
+            rd(t + 1, 0, xa[0], xb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mm_issue(xa[1], xb[1], t + NS - 1);
+            __builtin_amdgcn_sched_barrier(0);
         } else {
             if (t + NS - 1 < n_turns) issue(t + NS - 1);
+            rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
+            __builtin_amdgcn_sched_barrier(0);
+            mm(xa[1], xb[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
-        __builtin_amdgcn_sched_barrier(0);
-        mm(xa[1], xb[1]);
-        __builtin_amdgcn_sched_barrier(0);
     };
     const int n_steady = n_full - (NS - 1);
     int t = 0;
