@@ -187,8 +187,8 @@ def time_steps(fn, steps, warmup, torch):
 
 
 def per_launch_ms(fn, steps, torch):
-    """Median and minimum of single-launch times: `steps` more launches, each
-    between two HIP events on its stream (a separate pass after the timed
+    """Median and minimum of single-launch times: `steps` launches, each
+    between two HIP events on its stream (a separate pass before the timed
     one, so the contract's timed region holds launches only)."""
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -727,8 +727,8 @@ def main():
     # the same kernel on one resident copy of the inputs (the MALL then holds
     # them), then the timed launches proper, rotating over input copies
     ms_hot, _ = time_steps(head.run, args.steps, args.warmup, torch)
-    ms, wall = time_steps(head.run_rot, args.steps, args.warmup, torch)
     per_launch = per_launch_ms(head.run_rot, args.steps, torch)
+    ms, wall = time_steps(head.run_rot, args.steps, args.warmup, torch)
     tflops = head.flops() / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.4f} ms per call, {tflops:.1f} TFLOP/s")
 
