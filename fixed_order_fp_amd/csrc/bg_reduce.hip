@@ -360,25 +360,33 @@ __global__ __launch_bounds__(1024) void leaf_tree_kernel(const float* __restrict
 // block `blk`; wave w folds leaves [w LPWAVE, (w+1) LPWAVE) of that run one
 // after the other and pairs them into its node; the four wave nodes are then
 // paired through LDS.
+//
+// One lane's piece of one row.  Every element is read once and each load
+// instruction covers whole contiguous row segments, so the loads are
+// streaming (non-temporal): 5-8 % faster here.  The row axis keeps ordinary
+// loads: its lanes read a leaf as several 16-byte pieces of the same lines,
+// which then come back from the cache (streaming loads made it 1.5-2.4x
+// slower).
 template <typename T, int CPL>
 __device__ __forceinline__ void load_row_vec(const T* p, float* x)
 {
     if constexpr (std::is_same<T, float>::value) {
         static_assert(CPL == 4, "fp32 rows are read 16 bytes per lane");
-        const u32x4 v = *(const u32x4*)p;
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
 #pragma unroll
         for (int c = 0; c < 4; c++) x[c] = __uint_as_float(v[c]);
     } else if constexpr (CPL == 8) {
-        const u32x4 v = *(const u32x4*)p;
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
 #pragma unroll
         for (int c = 0; c < 8; c++) x[c] = bf16_lane(v, c);
     } else {
         static_assert(CPL == 4, "bf16 rows are read 16 or 8 bytes per lane");
-        const uint2 v = *(const uint2*)p;
-        x[0] = __uint_as_float(v.x << 16);
-        x[1] = __uint_as_float(v.x & 0xffff0000u);
-        x[2] = __uint_as_float(v.y << 16);
-        x[3] = __uint_as_float(v.y & 0xffff0000u);
+        const unsigned long long w = __builtin_nontemporal_load((const unsigned long long*)p);
+        const uint32_t lo = (uint32_t)w, hi = (uint32_t)(w >> 32);
+        x[0] = __uint_as_float(lo << 16);
+        x[1] = __uint_as_float(lo & 0xffff0000u);
+        x[2] = __uint_as_float(hi << 16);
+        x[3] = __uint_as_float(hi & 0xffff0000u);
     }
 }
 
