@@ -7,6 +7,7 @@
 // chooses tiles and waves (section 3.2.2; appendix E).  A descriptor the library
 // cannot realise exactly is refused, never replaced by another order (the
 // "GPU Mechanism" page's forced-algorithm refusal).
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -195,15 +196,29 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
         set(64, 64, 32, 2, 2, 2, 8);
         return;
     }
-    // deep splits: the largest tile that still gives ~150 workgroups;
-    // shallow splits: small tiles (their prologue and epilogue weigh less)
+    // deep splits: the tile whose busiest CU finishes first.  Each CU moves
+    // operands at ~38 GB/s and multiplies at ~8.1 TFLOP/s (both measured on
+    // these kernels, at the clock they settle at), so a tile costs rounds of
+    // workgroups x max(copy time, MFMA time) of one workgroup over the
+    // deepest split.  Shallow splits: small tiles (their prologue and
+    // epilogue weigh less).
     auto wgs = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn) * p.S; };
     const int64_t turns = p.cuts.c[1] / 32;
     if (turns >= 64) {
-        if (wgs(256, 128) >= 150) set(256, 128, 32, 2, 2, 2, 4);
-        else if (wgs(128, 128) >= 150) set(128, 128, 32, 2, 2, 2, 5);
-        else if (wgs(128, 64) >= 150) set(128, 64, 32, 2, 2, 2, 8);
-        else set(64, 64, 32, 2, 2, 2, 8);
+        struct Cand { int bm, bn, wm, wn, ns; };
+        static const Cand cands[] = {{320, 256, 2, 4, 4}, {256, 256, 2, 4, 4}, {192, 256, 2, 4, 4}, {256, 128, 2, 2, 4},
+                                     {192, 128, 2, 2, 4}, {128, 128, 2, 2, 5}, {128, 64, 2, 2, 8}, {64, 64, 2, 2, 8}};
+        int64_t kmax = 0;
+        for (int s = 0; s < p.S; s++) kmax = std::max<int64_t>(kmax, p.cuts.c[s + 1] - p.cuts.c[s]);
+        const Cand* pick = nullptr;
+        double best = 0.0;
+        for (const Cand& c : cands) {
+            const double copy = (double)(c.bm + c.bn) * (double)kmax * 2.0 / 38e9;
+            const double mfma = (double)c.bm * c.bn * (double)kmax * 2.0 / 8.1e12;
+            const double t = (double)ceil_div(wgs(c.bm, c.bn), n_cu) * std::max(copy, mfma);
+            if (!pick || t < best) pick = &c, best = t;
+        }
+        set(pick->bm, pick->bn, 32, pick->wm, pick->wn, 2, pick->ns);
         return;
     }
     if (wgs(64, 64) <= 2048) set(64, 64, 32, 2, 2, 2, 8);

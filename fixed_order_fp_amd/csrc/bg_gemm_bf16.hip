@@ -922,6 +922,9 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
     X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 4, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 32, 2, 2, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 32, 2, 2, 2, 6)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 192, 128, 32, 2, 2, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 192, 128, 32, 2, 2, 2, 6)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 192, 256, 32, 2, 4, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2, 5)          \
     X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 32, 2, 2, 2, 8)          \

@@ -18,6 +18,8 @@ SCHEDULES = {
                           dict(bm=256, bn=256, bk=32, waves_m=2, waves_n=2, load_path=2),
                           dict(bm=256, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2, group_m=3),
                           dict(bm=256, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
+                          dict(bm=192, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2),
+                          dict(bm=192, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
                           dict(bm=128, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
                           dict(bm=128, bn=64, bk=32, waves_m=2, waves_n=2, load_path=2),
                           dict(bm=64, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2),
