@@ -193,3 +193,41 @@ def test_free_twin_computes_the_product(M, split_k):
     if split_k == 1:
         fixed = run_gemm({"mfma": "F32_32X32X16_BF16"}, X, W, out="fp32")
         assert np.array_equal(fixed.view(np.uint32), dC.cpu().numpy().view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# the full workloads, in the launch configuration the bench times (default
+# schedules), on outputs sampled for the oracle
+# ---------------------------------------------------------------------------
+def test_batch_sweep_full_size():
+    """N = 9728, K = 2560, bf16 out, M in {1, 8, 64, 512, 4000} with one
+    descriptor: sampled outputs of every M match the oracle, and every row is
+    bit-identical across all M (each M takes its own tile shape)."""
+    import oracle
+    X, W = synth.gemm_batch_sweep(M=4000)
+    full = run_gemm({}, X, W, out="bf16")
+    rng = np.random.default_rng(9)
+    spec = oracle_desc({"out_type": "bf16"}, "F32_32X32X16_BF16")
+    for M in (1, 8, 64, 512, 4000):
+        print_case("batch sweep full size", M)
+        C = full if M == 4000 else run_gemm({}, X[:M], W, out="bf16")
+        assert np.array_equal(C, full[:M]), f"rows of M={M} differ from the same rows at M=4000"
+        mi = rng.integers(0, M, 96)
+        ni = rng.integers(0, W.shape[0], 96)
+        ref = oracle.gemm_bf16_points(spec, X, W, mi, ni)
+        assert np.array_equal(C[mi, ni], ref), f"M={M}: sampled outputs differ from the oracle"
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8, 16])
+def test_splitk_sweep_full_size(S):
+    """M = 256, N = 2560, K = 9728, fp32 out, cuts at multiples of 256 with
+    the remainder last: sampled outputs match the oracle for each S."""
+    import oracle
+    A, B = synth.gemm_splitk_sweep()
+    print_case("split-K sweep full size", S)
+    C = run_gemm({"split_k": S}, A, B, out="fp32")
+    rng = np.random.default_rng(100 + S)
+    mi = rng.integers(0, A.shape[0], 96)
+    ni = rng.integers(0, B.shape[0], 96)
+    ref = oracle.gemm_bf16_points(oracle_desc({"split_k": S, "out_type": "fp32"}, "F32_32X32X16_BF16"), A, B, mi, ni)
+    assert np.array_equal(C[mi, ni].view(np.uint32), ref.view(np.uint32))
