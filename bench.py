@@ -664,11 +664,20 @@ def summarize_trace(path, tail):
 
 
 def kernel_source_digest():
-    """sha256 of the GEMM kernel source: stored counter readings apply only to
-    the kernel they were taken on."""
+    """sha256 of the GEMM kernel's code (bg_gemm_bf16.hip and the pipeline and
+    internal headers it includes) with comments and whitespace removed: stored
+    counter readings apply only to the code they were taken on, and an edit
+    of comments alone does not void them."""
     import hashlib
-    with open(os.path.join(ROOT, "fixed_order_fp_amd", "csrc", "bg_gemm_bf16.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    h = hashlib.sha256()
+    for name in ("bg_gemm_bf16.hip", "bg_pipe.h", "bg_internal.h"):
+        with open(os.path.join(ROOT, "fixed_order_fp_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(name.encode() + b"\0" + re.sub(r"\s+", "", src).encode())
+    return h.hexdigest()
 
 
 def stored_traffic():

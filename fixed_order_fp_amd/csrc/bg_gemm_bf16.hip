@@ -392,13 +392,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 //    NS stages in LDS, turn t+NS-1 copied while turn t is multiplied;
 //  * one barrier per turn, placed before the turn's last k-step: the MFMAs
 //    of the step before it are still queued while waves meet there, and the
-//    first operands of the next turn are read right after it;
+//    first operands of the next turn are read right after it; each wave's
+//    copies of the turn NS-1 ahead are then spread among that last k-step's
+//    MFMAs;
 //  * MFMA operands swapped (the B fragment is the instruction's first operand,
 //    so the instruction computes the transposed 32x32 block): every product
 //    and every k group is the same, and each lane ends up holding 4
 //    consecutive columns of one row of C;
 //  * bf16 output is staged through LDS and written row by row, 16 bytes per
-//    lane with consecutive lanes on consecutive addresses.
+//    lane with consecutive lanes on consecutive addresses, as streaming
+//    stores.
 // The copies bypass the compiler (see dma16) and are waited for explicitly.
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32

@@ -198,11 +198,12 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
 
 // The pipelined W8A8 kernel: the bf16 pipelined kernel's schedule (NS
 // stages of 64-byte k tiles copied straight to LDS, one barrier per turn
-// placed before the last k-step, MFMA operands swapped so that a lane holds 4
-// consecutive columns of one row) on v_mfma_i32_32x32x32_i8, whose int32 sum
-// is exact in any order.  The epilogue applies the fixed order above to 4
-// columns at a time and stages the bf16 tile in LDS for row-contiguous
-// 16-byte stores.  A short last k tile (K not a multiple of 64) is copied
+// placed before the last k-step with the next copies spread among that
+// step's MFMAs, MFMA operands swapped so that a lane holds 4 consecutive
+// columns of one row) on v_mfma_i32_32x32x32_i8, whose int32 sum is exact in
+// any order.  The epilogue applies the fixed order above to 4 columns at a
+// time and stages the bf16 tile in LDS for row-contiguous 16-byte streaming
+// stores.  A short last k tile (K not a multiple of 64) is copied
 // through registers with zeros past K.
 // MODE 0: Y; 1: Y and the int32 accumulators; 2: the accumulators only (no
 // scales, no Y: the integer products other paths build on)
