@@ -49,15 +49,24 @@ __global__ __launch_bounds__(256) void ozaki_slice_kernel(const void* __restrict
     int e = 0;
     if (amax > 0.0f) (void)frexpf(amax, &e);  // amax in [2^(e-1), 2^e)
     if (t == 0) E[r] = e;
-    for (int64_t k = t; k < Kp; k += 256) {
-        double v = k < K ? ldexp((double)elem<IN_BF16>(X, r * ldx + k), -e) : 0.0;
+    // four consecutive k per thread (Kp is a multiple of 16), each slice's
+    // four codes written as one 32-bit word
+    for (int64_t k0 = 4 * (int64_t)t; k0 < Kp; k0 += 1024) {
+        uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            v = v * 128.0;
-            const double q = trunc(v);
-            Q[((int64_t)s * rows + r) * Kp + k] = (int8_t)(int)q;
-            v = v - q;
+        for (int u = 0; u < 4; u++) {
+            const int64_t k = k0 + u;
+            double v = k < K ? ldexp((double)elem<IN_BF16>(X, r * ldx + k), -e) : 0.0;
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                v = v * 128.0;
+                const double q = trunc(v);
+                packed[s] |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * u);
+                v = v - q;
+            }
         }
+#pragma unroll
+        for (int s = 0; s < 4; s++) *(uint32_t*)(Q + ((int64_t)s * rows + r) * Kp + k0) = packed[s];
     }
 }
 
@@ -94,7 +103,8 @@ __global__ __launch_bounds__(256) void ozaki_combine_kernel(const int32_t* __res
         for (int s = 0; s < 4; s++) {
             const int t = lev - s;
             if (t < 0 || t > 3) continue;
-            v = v + ldexp((double)acc[(s * M + m) * ld + t * N + n], -7 * (lev + 2));
+            // each product is read once, by whole lines: a streaming load
+            v = v + ldexp((double)__builtin_nontemporal_load(&acc[(s * M + m) * ld + t * N + n]), -7 * (lev + 2));
         }
     v = ldexp(v, EA[m] + EB[n]);
     if constexpr (OUT_BF16) ((uint16_t*)C)[m * ldc + n] = bf16_from_f64(v);
