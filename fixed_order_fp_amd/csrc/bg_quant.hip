@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void requantize_pow2_kernel(int64_t N, const i
     };
     if constexpr (VEC) {
         for (int64_t k = 16 * (int64_t)t; k < K; k += 2048) {
-            const u32x4 v = *(const u32x4*)(w + k);
+            const u32x4 v = __builtin_nontemporal_load((const u32x4*)(w + k));
             u32x4 r;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void requantize_pow2_kernel(int64_t N, const i
                 r[i] = pack4(code((int8_t)(u & 0xff)), code((int8_t)((u >> 8) & 0xff)),
                              code((int8_t)((u >> 16) & 0xff)), code((int8_t)(u >> 24)));
             }
-            *(u32x4*)(o + k) = r;
+            __builtin_nontemporal_store(r, (u32x4*)(o + k));
         }
     } else {
         for (int64_t k = t; k < K; k += 128) o[k] = code(w[k]);
