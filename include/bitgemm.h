@@ -145,7 +145,8 @@ typedef enum { BG_TREE_BALANCED = 0 } bg_tree;
 
 typedef struct {
     int32_t leaves_per_wg;  /* column axis: leaves one workgroup folds: 4, 8, 16
-                               or 32 (0: the fewest keeping <= 64 block roots);
+                               or 32 (0: 4 for bf16 and 8 for fp32 input,
+                               raised until <= 64 block roots remain);
                                256: one pass, a workgroup per narrow column
                                strip over every row (rows <= 8192)          */
     int32_t cols_per_wg;    /* column axis: columns one workgroup covers: 256,
