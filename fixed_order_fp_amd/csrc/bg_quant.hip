@@ -49,8 +49,21 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
     int8_t* q = Q + m * ldq;
     const int t = threadIdx.x;
 
+    // rows of up to 1024 R floats stay in registers between the two passes
+    // (one read of the row, streaming); longer rows are read twice, the
+    // second time from L2
+    constexpr int R = 8;
+    const bool in_regs = VEC && K <= 1024 * R;
+    f32x4_t reg[R];
     float amax = 0.0f;  // fmaxf ignores a NaN operand, as a "greater than" scan does
-    if constexpr (VEC) {
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < R; i++) {
+            const int64_t k = 4 * (int64_t)t + 1024 * i;
+            reg[i] = k < K ? __builtin_nontemporal_load((const f32x4_t*)(x + k)) : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(reg[i].x), fabsf(reg[i].y)), fmaxf(fabsf(reg[i].z), fabsf(reg[i].w))));
+        }
+    } else if constexpr (VEC) {
         for (int64_t k = 4 * (int64_t)t; k < K; k += 1024) {
             const f32x4_t v = *(const f32x4_t*)(x + k);
             amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -66,7 +79,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
     const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
     if (t == 0) scale[m] = s;
 
-    if constexpr (VEC) {
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < R; i++) {
+            const int64_t k = 4 * (int64_t)t + 1024 * i;
+            if (k < K)
+                *(uint32_t*)(q + k) = pack4(clamp_code(rintf(reg[i].x / s)), clamp_code(rintf(reg[i].y / s)),
+                                            clamp_code(rintf(reg[i].z / s)), clamp_code(rintf(reg[i].w / s)));
+        }
+    } else if constexpr (VEC) {
         for (int64_t k = 4 * (int64_t)t; k < K; k += 1024) {
             const f32x4_t v = *(const f32x4_t*)(x + k);
             *(uint32_t*)(q + k) = pack4(clamp_code(rintf(v.x / s)), clamp_code(rintf(v.y / s)),

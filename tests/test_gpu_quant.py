@@ -59,7 +59,8 @@ def test_workload_1024x2048():
 
 
 @pytest.mark.parametrize("M,K,pad,offset", [(7, 1, 0, 0), (5, 3, 1, 0), (33, 2049, 0, 0), (9, 4097, 3, 1),
-                                            (17, 256, 0, 1), (3, 1000, 24, 0), (2, 0, 0, 0), (1, 8192 + 4, 0, 0)])
+                                            (17, 256, 0, 1), (3, 1000, 24, 0), (2, 0, 0, 0), (1, 8192 + 4, 0, 0),
+                                            (2, 8192, 0, 0)])
 def test_ragged_and_unaligned(M, K, pad, offset):
     print_case("quantize ragged", M, K, pad, offset)
     x = synth.f32_spread(300 + K, (M, K), -20, 20) if K else np.zeros((M, 0), np.float32)
