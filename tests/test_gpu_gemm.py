@@ -231,3 +231,21 @@ def test_splitk_sweep_full_size(S):
     ni = rng.integers(0, B.shape[0], 96)
     ref = oracle.gemm_bf16_points(oracle_desc({"split_k": S, "out_type": "fp32"}, "F32_32X32X16_BF16"), A, B, mi, ni)
     assert np.array_equal(C[mi, ni].view(np.uint32), ref.view(np.uint32))
+
+
+def test_two_rounds_of_large_tiles_match_one_round_tiles():
+    """More 320x256 tiles than CUs (3000 x 8000, 320 tiles in two rounds;
+    ragged M, N and a short last k tile): bytes equal the 256x128 path, whose
+    tiles fit one round, and sampled outputs match the oracle."""
+    import oracle
+    A = synth.bf16_spread(61, (3000, 1000), -20, 20)
+    B = synth.bf16_spread(62, (8000, 1000), -20, 20)
+    print_case("two rounds of 320x256 tiles, 3000x8000x1000")
+    walk = run_gemm({"schedule": dict(bm=320, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2)}, A, B, out="bf16")
+    one = run_gemm({"schedule": dict(bm=256, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2)}, A, B, out="bf16")
+    assert np.array_equal(walk, one)
+    rng = np.random.default_rng(61)
+    mi = rng.integers(0, 3000, 96)
+    ni = rng.integers(0, 8000, 96)
+    ref = oracle.gemm_bf16_points(oracle_desc({"out_type": "bf16"}, "F32_32X32X16_BF16"), A, B, mi, ni)
+    assert np.array_equal(walk[mi, ni], ref)
