@@ -655,6 +655,51 @@ def reduce_extras(args, torch, bg, synth):
     return out
 
 
+def copy_calibration(torch):
+    """Three plain 1 GiB device copies: the known-size reference that the HBM
+    counters of a counter run are scaled by."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("bench: ran 3 plain copies of 1 GiB")
+    del src, dst
+
+
+def reductions_only(args, torch, bg, synth):
+    """Eager, rotated calls of the row reduction (fp32 16384 x 8192, sum and
+    sum of squares) and the column sum (bf16 8192 x 4096), for counter runs:
+    no graphs and no twins, so that every dispatch is one of these kernels."""
+    import numpy as np
+    import oracle
+    res = {}
+    cases = [("row", "fp32", synth.reduce_rows_input(), "sum_and_sumsq", 4),
+             ("col", "bf16", synth.reduce_cols_input(), "sum", 2)]
+    for axis, in_type, Xh, op, elt in cases:
+        rows, cols = Xh.shape
+        d = bg.reduce_desc(dict(in_type=in_type, op=op, axis=axis))
+        dX = torch.from_numpy(Xh.view(np.int16) if in_type == "bf16" else Xh).cuda()
+        n_out = rows if axis == "row" else cols
+        s = torch.empty(n_out, dtype=torch.float32, device="cuda")
+        q = torch.empty(n_out, dtype=torch.float32, device="cuda") if op == "sum_and_sumsq" else None
+        nws = bg.reduce_workspace_bytes(d, rows, cols)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        bg.reduce_tree(d, dX, s, q, ws)
+        torch.cuda.synchronize()
+        idx = np.sort(np.random.default_rng(7).choice(n_out, 16, replace=False))
+        rs, _ = oracle.reduce(Xh[idx] if axis == "row" else Xh[:, idx], axis, in_type=in_type)
+        bad = int(np.sum(s.cpu().numpy()[idx].view(np.uint32) != rs.view(np.uint32)))
+        rot = Rotation([dX])
+        t, _ = time_steps(lambda: bg.reduce_tree(d, rot.next()[0], s, q, ws), args.steps, args.warmup, torch)
+        byts = rows * cols * elt + 4 * n_out * (2 if q is not None else 1)
+        res[f"reduce_{axis}_{in_type}_{rows}x{cols}"] = {"us": round(t * 1e3, 2),
+                                                         "GB/s": round(byts / t / 1e6, 1),
+                                                         "algorithmic_bytes": byts, "inputs": rot.note(),
+                                                         "parity": {"sampled_outputs": 16, "mismatches": bad}}
+    print(json.dumps({"note": "reductions only (counter run)", "reductions": res}), flush=True)
+
+
 def summarize_trace(path, tail):
     """Markdown table of a rocprofv3 kernel-trace CSV grouped by kernel and grid
     size (one workload per grid), so a kernel that serves several workloads
@@ -731,6 +776,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only-headline", action="store_true",
                     help="time the headline GEMM only (for counter runs): no twins, extras or CPU baseline")
+    ap.add_argument("--only-reductions", action="store_true",
+                    help="eager calls of the row and column reductions only (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
@@ -747,6 +794,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.only_reductions:
+        if args.copy_calibration:
+            copy_calibration(torch)
+        reductions_only(args, torch, bg, synth)
+        return
     log("bench: generating the batch-sweep workload")
     X, W = synth.gemm_batch_sweep(M=4000)
     head = Gemm("gemm_bf16 M=4000", X, W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"}, torch, bg)
@@ -786,13 +838,7 @@ def main():
     }
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("bench: ran 3 plain copies of 1 GiB")
-        del src, dst
+        copy_calibration(torch)
     if args.only_headline:
         line["config"]["note"] = "headline only (counter run)"
         print(json.dumps(line), flush=True)
