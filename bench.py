@@ -296,6 +296,20 @@ def oracle_rate(fn, work, unit, sample, budget_s=2.0):
             "kind": "oracle", "sample": sample}
 
 
+def vendor_product_ms(g, args, torch):
+    """The same product from the vendor library: hipBLASLt through
+    torch.nn.functional.linear (C = A B^T, bf16 in and out, the summation
+    order left to the library), on the same rotated inputs.  Context for the
+    order-fixed kernel's speed; nothing is compared bit for bit."""
+    import torch.nn.functional as F
+
+    def fn():
+        A, B = g.rot.next()
+        F.linear(A.view(torch.bfloat16), B.view(torch.bfloat16))
+    ms, _ = time_steps(fn, args.steps, args.warmup, torch)
+    return ms
+
+
 def free_twin_us(g, args, torch):
     """(eager us, graph us, split) of the free-order twin of GEMM workload g,
     tuned over its own knob: no split, or atomic split-K by CU count."""
@@ -854,6 +868,12 @@ def main():
                           "fixed_over_free_time": round(ms / ms_free, 4), "split": free_split,
                           "note": "free twin writes fp32 (4 B/output) where the fixed path writes bf16"}
     log(f"bench: free-order twin {ms_free:.4f} ms")
+    ms_vendor = vendor_product_ms(head, args, torch)
+    line["vendor_free_order"] = {"ms": round(ms_vendor, 5),
+                                 "TFLOP/s": round(head.flops() / (ms_vendor * 1e-3) / 1e12, 3),
+                                 "fixed_over_vendor_time": round(ms / ms_vendor, 4),
+                                 "library": "hipBLASLt via torch.nn.functional.linear, bf16 out, order not fixed"}
+    log(f"bench: vendor library {ms_vendor:.4f} ms")
 
     extra = {}
     if not args.no_extra:
