@@ -437,6 +437,18 @@ def w8a8_extra(args, torch, bg, synth):
     ops = 2.0 * M * N * K
     byts = M * K + N * K + 4 * (M + N) + 2 * M * N
     log(f"bench: W8A8: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us")
+    # context: the vendor library's int8 GEMM (hipBLASLt through
+    # torch._int_mm, exact int32 out, no scale epilogue) on the same operands
+    try:
+        def fv():
+            a, w, _, _ = rot.next()
+            torch._int_mm(a, w.t())
+        tv = graph_time(fv, args.steps, torch)
+        vendor = {"graph_us": round(tv * 1e3, 2), "TOP/s": round(ops / tv / 1e9, 2),
+                  "fixed_over_vendor_time": round(tg / tv, 3),
+                  "library": "hipBLASLt via torch._int_mm, int32 out (no epilogue)"}
+    except Exception as e:  # the library call is context only
+        vendor = {"unavailable": f"{type(e).__name__}: {e}"[:160]}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = oracle_rate(lambda: oracle.w8a8_pow2(a_q[:16], w_q, a_s[:16], w_s), 2.0 * 16 * N * K / 1e12,
@@ -445,7 +457,7 @@ def w8a8_extra(args, torch, bg, synth):
                                     "TOP/s": round(ops / tg / 1e9, 2),
                                     "frac_int8_peak": round(ops / tg / 1e9 / PEAK_INT8_TOPS, 4),
                                     "GB/s": round(byts / tg / 1e6, 1), "hot_graph_us": round(tg_hot * 1e3, 2),
-                                    "inputs": rot.note(), "parity": par}}
+                                    "inputs": rot.note(), "parity": par, "vendor_free_order": vendor}}
 
 
 def gemm_reduce_extras(X, W, args, torch, bg, ms_plain):
