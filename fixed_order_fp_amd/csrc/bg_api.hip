@@ -50,6 +50,17 @@ bg_status check_device()
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// An AQL dispatch packet holds each grid dimension as a 32-bit count of
+// work-items, so a launch of `groups` workgroups of `threads` lanes must keep
+// groups * threads below 2^32; shapes past that are refused, never launched.
+bool grid_fits(int64_t groups, int64_t threads) { return groups >= 0 && groups <= 0xffffffffLL / threads; }
+
+bool tiles_fit(int64_t M, int64_t N, int bm, int bn, int threads)
+{
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+    return tm <= 0xffffffffLL / threads && tn <= 0xffffffffLL / threads && grid_fits(tm * tn, threads);
+}
+
 // ---- order signature: FNV-1a 64 over the order fields, two lanes ----------
 struct Fnv {
     uint64_t h[2] = {0xcbf29ce484222325ull, 0x84222325cbf29ce4ull};
@@ -390,6 +401,7 @@ bg_status bg_gemm_workspace_bytes(const bg_gemm_desc* d, int64_t M, int64_t N, i
     if (!d || !bytes) return fail(BG_E_INVALID, "NULL argument");
     if (M < 0 || N < 0) return fail(BG_E_INVALID, "negative size");
     if (d->split_k < 1 || d->split_k > BG_MAX_SPLIT) return fail(BG_E_INVALID, "split_k must be in 1..64");
+    if (N > 0 && M > (INT64_MAX / 256) / N) return fail(BG_E_UNSUPPORTED, "M x N too large");
     *bytes = d->split_k > 1 ? (size_t)d->split_k * (size_t)M * (size_t)N * sizeof(float) : 0;
     return BG_OK;
 }
@@ -442,6 +454,8 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
     } else {
         choose_gemm_tile(p, M, N);
     }
+    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n) || (p.S > 1 && !grid_fits((M * N + 255) / 256, 256)))
+        return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_gemm_bf16(p, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc,
@@ -490,6 +504,7 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
     if (!aligned16(A) || !aligned16(W) || lda % 16 || ldw % 16 || !aligned16(Y) || ldy % 8 ||
         ((uintptr_t)a_scale & 3u) || ((uintptr_t)w_scale & 3u) || (acc_out && (!aligned16(acc_out) || ld_acc % 4)))
         return fail(BG_E_ALIGN, "pointers must be aligned and leading dimensions multiples of 16 (int8) / 8 / 4");
+    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n)) return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_w8a8(p, M, N, K, A, lda, W, ldw, a_scale, w_scale, (uint16_t*)Y, ldy, acc_out,
@@ -579,7 +594,14 @@ bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols, co
     const int64_t n_out = p.axis == BG_AXIS_ROW ? rows : cols;
     const size_t need = nb > 1 ? (size_t)n_out * (size_t)nb * 2 * sizeof(float) : 0;
     if (need && (!ws || ws_bytes < need)) return fail(BG_E_WORKSPACE, "this shape needs a workspace");
-    if (p.axis == BG_AXIS_ROW && rows > 0x7fffffff) return fail(BG_E_UNSUPPORTED, "too many rows");
+    // row axis: a workgroup per row; column axis: a workgroup per strip of
+    // 256 or more columns, or in one pass per strip of 32 (bf16, 512 lanes) or
+    // 16 (fp32, 1024 lanes); the upper levels take 256 lanes per 64 outputs
+    const bool fits = p.axis == BG_AXIS_ROW ? grid_fits(rows, 256)
+                      : p.col_full          ? grid_fits(p.bf16 ? (cols + 31) / 32 : (cols + 15) / 16, p.bf16 ? 512 : 1024)
+                                            : grid_fits((cols + 63) / 64, 256);
+    if (!fits)
+        return fail(BG_E_UNSUPPORTED, "too many rows or columns for one launch");
     st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_reduce(p, rows, cols, X, ldx, out_sum, out_sumsq, (float*)ws, stream);
@@ -659,6 +681,8 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
         else if (M > 64 && ((M + 255) / 256) * ((N + 127) / 128) >= 150) set(256, 128, 2, 2, 4);
         else set(64, 64, 2, 2, 8);
     }
+    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n) || !grid_fits((n_out + 63) / 64, 1024))
+        return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     float* ws_sum = (float*)ws;
     float* ws_sq = (float*)ws + ((rd->op & BG_RED_SUM) ? n_leaf * n_out : 0);
     p.red = rd->axis == BG_AXIS_COL ? 1 : 2;
@@ -678,10 +702,18 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
 
 static size_t align16z(size_t x) { return (x + 15) & ~(size_t)15; }
 
+// slicing: a workgroup per row of A and of B; combine: a lane per output
+// (which also bounds the workspace, 64 M N bytes of int32 products)
+bool ozaki_fits(int64_t M, int64_t N)
+{
+    return grid_fits(M, 256) && grid_fits(N, 256) && grid_fits((M * N + 255) / 256, 256);
+}
+
 bg_status bg_gemm_ozaki_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes)
 {
     if (!bytes) return fail(BG_E_INVALID, "NULL argument");
     if (M < 0 || N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
+    if (!ozaki_fits(M, N)) return fail(BG_E_UNSUPPORTED, "M, N below 2^24 and M x N below 2^32 for one launch");
     const size_t Kp = (size_t)((K + 15) / 16 * 16);
     *bytes = align16z(4 * (size_t)M * Kp) + align16z(4 * (size_t)N * Kp) + align16z(4 * (size_t)M) +
              align16z(4 * (size_t)N) + 16 * (size_t)M * (size_t)N * 4;
@@ -695,7 +727,7 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
     if (in_type != BG_FP32 && in_type != BG_BF16) return fail(BG_E_INVALID, "in_type must be fp32 or bf16");
     if (out_type != BG_FP32 && out_type != BG_BF16) return fail(BG_E_INVALID, "out_type must be fp32 or bf16");
     if (M < 0 || N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
-    if (M > 0x1fffffff || N > 0x1fffffff) return fail(BG_E_UNSUPPORTED, "M and N must stay below 2^29");
+    if (!ozaki_fits(M, N)) return fail(BG_E_UNSUPPORTED, "M, N below 2^24 and M x N below 2^32 for one launch");
     const int64_t Kp = (K + 15) / 16 * 16;
     if (Kp > 133144) return fail(BG_E_UNSUPPORTED, "K above 133,144 could leave the int32 range");
     if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
@@ -724,6 +756,8 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
     bg::W8A8Plan p{};
     p.mfma = BG_MFMA_I32_32X32X32_I8;
     choose_w8a8_pipe(p, 4 * M, 4 * N);
+    if (!tiles_fit(4 * M, 4 * N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
+        return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     bg_status st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_ozaki(p, M, N, K, in_type == BG_BF16, A, lda, B, ldb, out_type == BG_BF16, C, ldc, w,
@@ -736,7 +770,7 @@ bg_status bg_quantize_act_int8(int64_t M, int64_t K, const float* X, int64_t ldx
                                float* a_scale, hipStream_t stream)
 {
     if (M < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
-    if (M > 0x7fffffff) return fail(BG_E_UNSUPPORTED, "at most 2^31 - 1 rows");
+    if (!grid_fits(M, 256)) return fail(BG_E_UNSUPPORTED, "at most 2^24 - 1 rows (a workgroup per row)");
     if (ldx < K || ldq < K) return fail(BG_E_INVALID, "leading dimension smaller than the row");
     if (M == 0) return BG_OK;
     if (!a_scale || (K > 0 && (!X || !Q))) return fail(BG_E_INVALID, "NULL tensor");
@@ -754,7 +788,7 @@ bg_status bg_requantize_weights_pow2(int64_t N, int64_t K, const int8_t* W, int6
                                      hipStream_t stream)
 {
     if (N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
-    if (N > 0x7fffffff) return fail(BG_E_UNSUPPORTED, "at most 2^31 - 1 rows");
+    if (!grid_fits((N + 1) / 2, 256)) return fail(BG_E_UNSUPPORTED, "at most 2^25 - 2 rows (a workgroup per two rows)");
     if (mode != BG_POW2_NEAREST && mode != BG_POW2_CEIL) return fail(BG_E_INVALID, "unknown mode");
     if (ldw < K || ldw2 < K) return fail(BG_E_INVALID, "leading dimension smaller than the row");
     if (N == 0) return BG_OK;
@@ -805,6 +839,8 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     for (int s = 0; s < S; s++) p.cuts.c[s] = s * span;
     p.cuts.c[S] = K;
     if (S > 1) choose_gemm_tile(p, M, N);  // the tile for the split grid
+    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
+        return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     p.atomic = S > 1;
     hipError_t e = hipSuccess;
     if (p.atomic) e = bg::launch_zero_rows(C, M, N, ldc, stream);
@@ -823,6 +859,8 @@ bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, in
     if (rows < 0 || cols < 0 || ldx < cols) return fail(BG_E_INVALID, "bad sizes");
     if (rows == 0 || cols == 0) return BG_OK;
     if (!X || !aligned16(X) || ldx % 8) return fail(BG_E_ALIGN, "X must be 16-byte aligned with ldx a multiple of 8");
+    if (!grid_fits(axis == BG_AXIS_ROW ? rows : (cols + 511) / 512, 256))
+        return fail(BG_E_UNSUPPORTED, "too many rows or columns for one launch");
     bg_status st = check_device();
     if (st != BG_OK) return st;
     int dev = 0, n_cu = 256;
@@ -838,7 +876,8 @@ bg_status bg_probe_mfma(uint32_t mfma, int64_t n_cases, const void* A, const voi
                         hipStream_t stream)
 {
     if (instruction_k(mfma) == 0) return fail(BG_E_INVALID, "unknown mfma");
-    if (n_cases < 0 || n_cases > 0x7fffffff) return fail(BG_E_INVALID, "n_cases out of range");
+    if (n_cases < 0) return fail(BG_E_INVALID, "n_cases out of range");
+    if (!grid_fits(n_cases, 64)) return fail(BG_E_UNSUPPORTED, "at most 2^26 - 1 cases per launch");
     if (n_cases == 0) return BG_OK;
     if (!A || !B || !C || !D) return fail(BG_E_INVALID, "NULL tensor");
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D))

@@ -38,6 +38,10 @@
  *   - Refusal: a descriptor the library cannot realise exactly (an unsupported
  *     field value, a profile measured on another device) is refused with
  *     BG_E_UNSUPPORTED / BG_E_PROFILE; another order is never substituted [G].
+ *   - Size: each call is one launch (or a short fixed sequence), and a
+ *     dispatch counts each grid dimension's work-items in 32 bits; a shape
+ *     whose grid would pass that is refused with BG_E_UNSUPPORTED.  Limits per
+ *     call are stated with it where they bind before memory runs out.
  *   - Alignment: tensor pointers 16-byte aligned; leading dimensions a
  *     multiple of 8 elements (bf16, fp32) or 16 (int8); else BG_E_ALIGN.
  *   - Thread safety: calls are reentrant.  Calls that share a workspace must be
@@ -276,7 +280,7 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
  * A: [M][lda], B: [N][ldb] of in_type (BG_FP32 or BG_BF16), K contiguous;
  * C: [M][ldc] of out_type.  ws: at least bg_gemm_ozaki_workspace_bytes(),
  * 16-byte aligned (slices, exponents and the 16 M N int32 products).
- * M, N < 2^29; K rounded up to 16 at most 133,144. */
+ * M, N < 2^24 and M * N < 2^32; K rounded up to 16 at most 133,144. */
 bg_status bg_gemm_ozaki_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const void* A, int64_t lda,
                         const void* B, int64_t ldb, uint32_t out_type, void* C, int64_t ldc, void* ws,
@@ -293,7 +297,7 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
  *   The maximum is exact, so the result does not depend on any order.
  * X: fp32 [M][ldx] (device, caller-owned); Q: int8 [M][ldq]; a_scale: fp32 [M].
  * Inputs are expected finite (an infinite element makes its row's scale
- * infinite and its codes 0).  M, K >= 0, M < 2^31; X and Q may be NULL when
+ * infinite and its codes 0).  M, K >= 0, M < 2^24; X and Q may be NULL when
  * K = 0 (every scale is then 1); X 4-byte aligned (16-byte X rows with
  * K % 4 == 0 take the vector path).  Errors come back synchronously with
  * nothing enqueued. */
@@ -310,7 +314,7 @@ bg_status bg_quantize_act_int8(int64_t M, int64_t K, const float* X, int64_t ldx
  *   W2[n][k] = clamp(rint(fp32(W[n][k] * w_scale[n]) / s2), -127, 127).
  *   A row whose scale is not a positive finite number is copied unchanged.
  * W, W2: int8 [N][ldw] / [N][ldw2] (may not overlap); w_scale, w_scale2:
- * fp32 [N].  N, K >= 0, N < 2^31 (W and W2 may be NULL when K = 0).  The
+ * fp32 [N].  N, K >= 0, N < 2^25 - 1 (W and W2 may be NULL when K = 0).  The
  * outputs feed bg_gemm_w8a8_pow2. */
 enum { BG_POW2_NEAREST = 0, BG_POW2_CEIL = 1 };
 bg_status bg_requantize_weights_pow2(int64_t N, int64_t K, const int8_t* W, int64_t ldw, const float* w_scale,
@@ -328,7 +332,8 @@ bg_status bg_reduce_workspace_bytes(const bg_reduce_desc* d, int64_t rows, int64
  *   (s = x0; s = s + xi; q = x0*x0; q = fma(xi, xi, q)), then a balanced tree
  *   over the leaf index.  Both outputs come from one read of X.
  * X: fp32 or bf16 [rows][ldx] per d->in_type.  out_sum / out_sumsq: fp32
- * [rows] (ROW) or [cols] (COL); NULL to skip (per d->op). */
+ * [rows] (ROW) or [cols] (COL); NULL to skip (per d->op).  Axis ROW takes
+ * rows < 2^24 (a workgroup per row). */
 bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols,
                          const void* X, int64_t ldx, float* out_sum, float* out_sumsq,
                          void* ws, size_t ws_bytes, hipStream_t stream);
@@ -357,7 +362,7 @@ bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, in
  *   i8   16x16x64: A [16][64], B [16][64] int8, C, D int32 [16][16]
  * All row-major and packed case after case.  Element k of row m of A and row
  * n of B is the instruction's k-th product slot, in the same lane/register
- * placement the GEMM kernels use. */
+ * placement the GEMM kernels use.  n_cases < 2^26. */
 bg_status bg_probe_mfma(uint32_t mfma, int64_t n_cases, const void* A, const void* B,
                         const void* C, void* D, hipStream_t stream);
 

@@ -126,3 +126,40 @@ def test_w8a8_refusals_before_any_launch(bg):
     for spec, args, want in cases:
         st = _call_w8a8(bg, bg.gemm_desc(spec), **args)
         assert st == want, (spec, args, st, bg.lib().bg_last_error())
+
+
+def test_shapes_past_one_launch_are_refused(bg):
+    """A dispatch counts each grid dimension's work-items in 32 bits: shapes
+    whose grid would pass that are refused with BG_E_UNSUPPORTED before any
+    launch (and before the pointers, never dereferenced here, are used); the
+    largest shapes that fit are not refused on that ground."""
+    L, p, big = bg.lib(), C.c_void_p(0x10000), C.c_size_t(1 << 62)
+    unsup = 2
+    # bf16 GEMM: 2^20 x 2^20 outputs in 320 x 256 tiles of 512 lanes
+    assert _call_gemm(bg, bg.gemm_desc({}), M=1 << 20, N=1 << 20, K=512) == unsup
+    # W8A8: the same outputs in 128 x 192 tiles
+    d8 = bg.gemm_desc(dict(mfma="I32_32X32X32_I8", a_type="int8", b_type="int8", acc_type="int32",
+                           out_type="bf16", epilogue="W8A8_POW2"))
+    assert _call_w8a8(bg, d8, M=1 << 20, N=1 << 20, ldy=1 << 20) == unsup
+    # reductions: a workgroup per row (2^24 rows), and the one-pass column path
+    # (2^27 fp32 columns at 64 lanes each)
+    row, col = bg.reduce_desc({"axis": "row"}), bg.reduce_desc({"axis": "col", "in_type": "fp32"})
+    full = bg.reduce_desc({"axis": "col", "in_type": "fp32", "schedule": {"leaves_per_wg": 256}})
+    red = lambda d, rows, cols: L.bg_reduce_tree(C.byref(d), rows, cols, p, cols, p, p, p, big, None)
+    assert red(row, 1 << 24, 8) == unsup
+    assert red(full, 32, 1 << 27) == unsup
+    assert red(col, 64, 1 << 32) == unsup
+    # int8 steps: a workgroup per row, per two rows
+    assert L.bg_quantize_act_int8(1 << 24, 16, p, 16, p, 16, p, None) == unsup
+    assert L.bg_requantize_weights_pow2((1 << 25) - 1, 16, p, 16, p, 0, C.c_void_p(1 << 40), 16, p, None) == unsup
+    # Ozaki: M below 2^24 (slicing) and M x N below 2^32 (combine)
+    oz = lambda M, N: L.bg_gemm_ozaki(M, N, 64, 0, p, 64, p, 64, 0, p, N, p, big, None)
+    assert oz(1 << 24, 8) == unsup
+    assert oz(1 << 16, 1 << 16) == unsup
+    size = C.c_size_t()
+    assert L.bg_gemm_ozaki_workspace_bytes(1 << 30, 1 << 30, 64, C.byref(size)) == unsup
+    assert L.bg_gemm_ozaki_workspace_bytes(1 << 12, 1 << 12, 64, C.byref(size)) == 0
+    assert L.bg_gemm_workspace_bytes(C.byref(bg.gemm_desc({"split_k": 2})), 1 << 40, 1 << 40, 512,
+                                     C.byref(size)) == unsup
+    # the probe: 64 lanes per case
+    assert L.bg_probe_mfma(0, 1 << 26, p, p, p, p, None) == unsup
