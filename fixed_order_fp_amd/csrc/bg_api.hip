@@ -558,7 +558,9 @@ static bg_status reduce_plan(const bg_reduce_desc* d, int64_t rows, int64_t cols
         if (cpw % 64 || (p.cols_per_lane != 4 && (p.cols_per_lane != 8 || !p.bf16)))
             return fail(BG_E_UNSUPPORTED, "cols_per_wg must be 256 (or 512 for bf16 input)");
         n_blocks = bg::reduce_col_blocks(rows, p.leaves_per_wg);
-        if (n_blocks > 64) return fail(BG_E_UNSUPPORTED, "too many leaf blocks: raise leaves_per_wg");
+        if (n_blocks > 64)
+            return fail(BG_E_UNSUPPORTED, d->sched.leaves_per_wg ? "too many leaf blocks: raise leaves_per_wg"
+                                                                 : "a column longer than 64 * 32 leaves (65,536 rows) is not built");
     }
     return BG_OK;
 }
@@ -729,7 +731,7 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
     if (M < 0 || N < 0 || K < 0) return fail(BG_E_INVALID, "negative size");
     if (!ozaki_fits(M, N)) return fail(BG_E_UNSUPPORTED, "M, N below 2^24 and M x N below 2^32 for one launch");
     const int64_t Kp = (K + 15) / 16 * 16;
-    if (Kp > 133144) return fail(BG_E_UNSUPPORTED, "K above 133,144 could leave the int32 range");
+    if (Kp > 133144) return fail(BG_E_UNSUPPORTED, "K rounded up to 16 above 133,144 could leave the int32 range");
     if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
     if (M == 0 || N == 0) return BG_OK;
     if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");

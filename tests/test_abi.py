@@ -161,5 +161,9 @@ def test_shapes_past_one_launch_are_refused(bg):
     assert L.bg_gemm_ozaki_workspace_bytes(1 << 12, 1 << 12, 64, C.byref(size)) == 0
     assert L.bg_gemm_workspace_bytes(C.byref(bg.gemm_desc({"split_k": 2})), 1 << 40, 1 << 40, 512,
                                      C.byref(size)) == unsup
+    # the longest row (64 blocks of 8192) and column (64 blocks of 32 leaves of 32) built
+    assert red(row, 2, 64 * 8192 + 1) == unsup
+    assert red(col, 64 * 32 * 32 + 1, 40) == unsup
+    assert b"65,536 rows" in L.bg_last_error()
     # the probe: 64 lanes per case
     assert L.bg_probe_mfma(0, 1 << 26, p, p, p, p, None) == unsup

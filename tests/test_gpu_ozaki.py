@@ -72,6 +72,15 @@ def test_wide_spread_and_zero_rows():
     check(A, B, "fp32", "fp32")
 
 
+def test_deepest_k():
+    """K = 133,133, padded to 133,136: the deepest padded k (a multiple of
+    16) whose slice products still sum exactly in int32 (K 127^2 < 2^31)."""
+    print_case("ozaki deepest k")
+    A = synth.f32_spread(51, (3, 133133), -8, 8)
+    B = synth.f32_spread(52, (5, 133133), -8, 8)
+    check(A, B, "fp32", "fp32")
+
+
 def test_k_order_does_not_move_a_bit():
     print_case("ozaki k order")
     A = synth.f32_spread(41, (64, 512), -10, 10)

@@ -89,6 +89,32 @@ def test_row_ragged(in_type, fused, rows, ld, cols):
 
 
 @pytest.mark.parametrize("in_type", ["fp32", "bf16"])
+@pytest.mark.parametrize("cols", [64 * 8192, 64 * 8192 - 5])
+def test_row_longest(in_type, cols):
+    """The longest row built: 64 blocks of 256 leaves (a full second-level
+    tree of 64 block roots), and the same with a short last leaf."""
+    print_case("row_longest", in_type, cols)
+    ld = (cols + 7) // 8 * 8
+    X = synth.f32_spread(301, (2, ld), -12, 12) if in_type == "fp32" else synth.bf16_spread(301, (2, ld), -12, 12)
+    s, q = run_reduce(X, "row", in_type, cols=cols)
+    rs, rq = oracle_reduce(X, "row", in_type, cols=cols)
+    assert same(s, rs) and same(q, rq)
+
+
+@pytest.mark.parametrize("in_type", ["fp32", "bf16"])
+@pytest.mark.parametrize("rows", [65536, 65536 - 7])
+def test_col_deepest(in_type, rows):
+    """The longest column built on the default path: 2048 leaves, 32 leaves
+    per workgroup (the default raised until 64 block roots remain), and the
+    same with a short last leaf."""
+    print_case("col_deepest", in_type, rows)
+    X = synth.f32_spread(302, (rows, 40), -12, 12) if in_type == "fp32" else synth.bf16_spread(302, (rows, 40), -12, 12)
+    s, q = run_reduce(X, "col", in_type, cols=36)
+    rs, rq = oracle_reduce(X, "col", in_type, cols=36)
+    assert same(s, rs) and same(q, rq)
+
+
+@pytest.mark.parametrize("in_type", ["fp32", "bf16"])
 @pytest.mark.parametrize("rows,ld,cols,lpw", [(1000, 304, 300, 8), (8192, 256, 256, 32), (33, 8, 5, 4),
                                               (4096 + 32 * 3 + 7, 520, 513, 16), (32, 256, 256, 8)])
 def test_col_ragged(in_type, rows, ld, cols, lpw):
