@@ -86,7 +86,7 @@ def test_small_integers_exact(instr, K):
 
 
 @pytest.mark.parametrize("instr", INSTRS)
-@pytest.mark.parametrize("K,S", [(512, 1), (512, 2), (9728, 1), (9728, 4), (9728, 16), (1000, 3)])
+@pytest.mark.parametrize("K,S", [(512, 1), (512, 2), (9728, 1), (9728, 4), (9728, 16), (1000, 3), (16400, 64)])
 def test_all_ones_count_every_k(instr, K, S):
     """All-ones operands: every output is exactly K for every split."""
     print_case("all_ones", instr, K, S)
@@ -166,6 +166,23 @@ def test_spread_parity_ragged(instr):
             print_case("spread_parity", instr, S, sched)
             got = run_gemm(dict(spec, schedule=sched) if sched else spec, A, B)
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), sched
+
+
+@pytest.mark.parametrize("instr", INSTRS)
+def test_widest_split(instr):
+    """S = 64, the most splits built: 63 spans of 256 and a last one of 272
+    (K = 16400), exponent-spread operands, a six-level balanced combine;
+    0 ULP against the oracle with fp32 and bf16 output."""
+    import oracle
+    A = synth.bf16_spread(61, (24, 16400), -20, 20)
+    B = synth.bf16_spread(62, (40, 16400), -20, 20)
+    for out in ("fp32", "bf16"):
+        print_case("widest_split", instr, out)
+        spec = {"mfma": instr, "split_k": 64}
+        ref = oracle.gemm_bf16(oracle_desc(dict(spec, out_type=out), instr), A, B)
+        got = run_gemm(spec, A, B, out=out)
+        assert np.array_equal(got.view(np.uint16 if out == "bf16" else np.uint32),
+                              ref.view(np.uint16 if out == "bf16" else np.uint32))
 
 
 # ---------------------------------------------------------------------------
