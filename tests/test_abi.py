@@ -165,5 +165,11 @@ def test_shapes_past_one_launch_are_refused(bg):
     assert red(row, 2, 64 * 8192 + 1) == unsup
     assert red(col, 64 * 32 * 32 + 1, 40) == unsup
     assert b"65,536 rows" in L.bg_last_error()
+    # the GEMM with a fused reduction: at most 1024 leaves on the reduced axis
+    dg = bg.gemm_desc({}, out_type="bf16")
+    fused = lambda axis, M, N: L.bg_gemm_bf16_reduce(C.byref(dg), C.byref(bg.reduce_desc({"in_type": "fp32",
+                                                     "axis": axis})), M, N, 64, p, 64, p, 64, p,
+                                                     (N + 7) // 8 * 8, p, p, p, big, None)
+    assert fused("col", 32769, 40) == unsup and fused("row", 3, 32769) == unsup
     # the probe: 64 lanes per case
     assert L.bg_probe_mfma(0, 1 << 26, p, p, p, p, None) == unsup

@@ -72,6 +72,20 @@ def test_against_oracle_composition(axis, M, N, K):
     assert same(s, rs) and same(q, rq)
 
 
+@pytest.mark.parametrize("axis,M,N", [("col", 32768, 40), ("col", 32761, 40), ("row", 3, 32768),
+                                     ("row", 3, 32763)])
+def test_longest_reduced_axis(axis, M, N):
+    """The longest reduced axis built: 1024 leaves (a full 32-leaf run per
+    wave of the second kernel), and the same with a short last leaf."""
+    print_case("gemm_reduce longest", axis, M, N)
+    A = synth.bf16_normal(701, (M, 64))
+    B = synth.bf16_normal(702, (N, 64), sigma=0.05)
+    C32, (rs, rq) = oracle_ref(A, B, axis)
+    C, s, q = run(A, B, axis, out="fp32")
+    assert same(C, C32), "C differs from the oracle"
+    assert same(s, rs) and same(q, rq)
+
+
 @pytest.mark.parametrize("axis", ["col", "row"])
 def test_every_tile_and_the_output_types(axis):
     """Each tile built with the reductions gives the same reductions; the bf16
