@@ -377,6 +377,16 @@ def gemm_extras(X, W, args, torch, bg, synth):
         tg_hot = graph_time(g.run, args.steps, torch)
         if free is None:
             free, free_g, free_split = free_twin_us(g, args, torch)
+        # the free-order twin at the same split count (atomic combine)
+        dF = torch.empty((g.M, g.N), dtype=torch.float32, device="cuda")
+
+        def twin_same_s(S=S, dF=dF, g=g):
+            A, B = g.rot.next()
+            bg.bench_gemm_bf16_free(A, B, dF, S)
+        same_g = graph_time(twin_same_s, args.steps, torch)
+        # the binding roof: the larger of the MFMA time and the HBM time of
+        # the algorithmic work (operands, output and the partials' round trip)
+        roof = max(g.flops() / (PEAK_BF16_TFLOPS * 1e12), g.bytes() / (PEAK_HBM_GBS * 1e9))
         out[f"splitk_S{S}"] = {"us": round(t * 1e3, 2), "graph_us": round(tg * 1e3, 2),
                                "TFLOP/s": round(g.flops() / tg / 1e9, 2),
                                "GB/s": round(g.bytes() / tg / 1e6, 1),
@@ -384,6 +394,9 @@ def gemm_extras(X, W, args, torch, bg, synth):
                                "free_us": round(free, 2),
                                "free_graph_us": round(free_g, 2), "free_split": free_split,
                                "fixed_over_free_time": round(tg * 1e3 / free_g, 3), "parity": p,
+                               "frac_binding_roof": round(roof / (tg * 1e-3), 4),
+                               "free_same_split_graph_us": round(same_g * 1e3, 2),
+                               "fixed_over_free_same_split_time": round(tg / same_g, 3),
                                "outputs_differing_from_S1": {"fp32": diff32, "after_bf16_rounding": diff16,
                                                              "of": int(g.M * g.N)}}
         if S == 16 and not args.no_cpu_baseline:
