@@ -127,3 +127,124 @@ def test_one_rounding_to_bf16():
     assert oracle.bf16_from_f64(v) == 0x3F81          # one rounding: up
     assert oracle.bf16_from_f64(float(np.float32(v))) == 0x3F80   # through fp32 it would tie down to even
     assert oracle.bf16_from_f64(3.5e38) == 0x7F80     # past the largest bf16: infinity
+
+
+# ---------------------------------------------------------------------------
+# The fp64 order of the 16 slice products.  Every row below is built from
+# chosen base-128 digits (an element is 2^e sum_s q_s 128^-(s+1) with the row
+# exponent e = 0), one nonzero digit per element, so that column k adds
+# qa_s qb_t to exactly one slice product acc[s][t].  The products are then
+# placed so that the exact dot product lies on an fp32 (or bf16) rounding
+# midpoint plus a remainder far below the fp64 precision of the partial sums:
+# which remainder survives the fp64 additions decides the final rounding,
+# so the stated order (s + t from 6 down to 0, s ascending within a level)
+# is told apart from the reversed level walk and from s descending.
+# ---------------------------------------------------------------------------
+def _digits_row(cols):
+    """Elements from digit tuples (q0, q1, q2, q3), all digits of one sign."""
+    return np.array([sum(q * 2.0 ** (-7 * (s + 1)) for s, q in enumerate(d)) for d in cols],
+                    dtype=np.float32)
+
+
+def _fill(acc_target, s, t, sign=1):
+    """Columns (digit tuple of a, digit tuple of b) whose products sum to
+    acc_target in acc[s][t]: as many 127 x 127 as fit, then 127 x r, then 1 x r."""
+    cols, left = [], acc_target
+    one = lambda pos, q: tuple(q if i == pos else 0 for i in range(4))
+    while left >= 127 * 127:
+        cols.append((one(s, 127), one(t, 127 * sign)))
+        left -= 127 * 127
+    if left >= 127:
+        cols.append((one(s, left // 127), one(t, 127 * sign)))
+        left -= (left // 127) * 127
+    if left:
+        cols.append((one(s, 1), one(t, left * sign)))
+    return cols
+
+
+def _rows(spec):
+    cols = [c for (s, t, acc) in spec for c in _fill(abs(acc), s, t, 1 if acc > 0 else -1)]
+    # an anchor column holding each row's largest magnitude 127/128 (row
+    # exponent 0) whose products land in acc[0][0] only through b = 0
+    cols.append(((127, 0, 0, 0), (0, 0, 0, 0)))
+    cols.append(((0, 0, 0, 0), (127, 0, 0, 0)))
+    a = _digits_row([c[0] for c in cols])
+    b = _digits_row([c[1] for c in cols])
+    return a, b
+
+
+def _round_bits(fr, keep):
+    """Fraction -> nearest number with `keep` significant bits, ties to even
+    (written from the definition of round-to-nearest-even)."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - keep + 1)
+    q, r = divmod(a, ulp)
+    if r * 2 > ulp or (r * 2 == ulp and q % 2 == 1):
+        q += 1
+    return sign * q * ulp
+
+
+def _order_sum(acc, order):
+    """Sequential sum of acc[s][t] 2^(-7(s+t+2)) in `order`, each add rounded
+    to 53 bits."""
+    v = Fraction(0)
+    for s, t in order:
+        v = _round_bits(v + Fraction(acc[s][t]) * Fraction(2) ** (-7 * (s + t + 2)), 53)
+    return v
+
+
+STATED = [(s, lev - s) for lev in range(6, -1, -1) for s in range(4) if 0 <= lev - s <= 3]
+LEVELS_UP = [(s, lev - s) for lev in range(0, 7) for s in range(4) if 0 <= lev - s <= 3]
+S_DESC = [(s, lev - s) for lev in range(6, -1, -1) for s in range(3, -1, -1) if 0 <= lev - s <= 3]
+
+
+def _acc_of(spec):
+    acc = [[0] * 4 for _ in range(4)]
+    for s, t, v in spec:
+        acc[s][t] += v
+    return acc
+
+
+@pytest.mark.parametrize("case", ["levels_fp32", "levels_bf16", "s_order_fp32"])
+def test_fp64_recombination_order_is_pinned(case):
+    """The stated fp64 order gives bits that the reversed level walk (case
+    levels_*) or s descending within a level (case s_order) would not."""
+    if case == "levels_fp32":
+        # 2^6 + 2^-18 (an fp32 midpoint) + 6 2^-49: the two 3 2^-49 pieces,
+        # summed first, survive the add of 2^6 (0.75 of its fp64 ulp);
+        # added one by one after it they are each lost (0.375 ulp)
+        spec, out, want = [(0, 0, 2 ** 20), (0, 1, 8), (2, 3, 3), (3, 2, 3)], "fp32", 64 + 2.0 ** -17
+    elif case == "levels_bf16":
+        # 2^6 + 2^-2 (a bf16 midpoint) + 6 2^-49, the same way to 64.5
+        spec, out, want = [(0, 0, 2 ** 20 + 2 ** 12), (2, 3, 3), (3, 2, 3)], "bf16", 64.5
+    else:
+        # T01 = 1/2, T10 = -(1/2 - 2^-21), carried 2^-45 + 3 2^-56: with T01
+        # first the 3 2^-56 is lost (0.375 of the ulp of 1/2) and the result
+        # 2^-21 + 2^-45 is an fp32 midpoint going to the even 2^-21; with T10
+        # first it is rounded up to 2^-54 (0.75 of the ulp below 1/2) and
+        # the result rounds up to 2^-21 + 2^-44
+        spec, out, want = [(0, 1, 2 ** 20), (1, 0, -(2 ** 20 - 1)), (2, 3, 16), (3, 3, 3)], "fp32", 2.0 ** -21
+    a, b = _rows(spec)
+    # the premise: the oracle cuts these rows into the designed digits
+    qa, ea = oracle.ozaki_slice_row(a)
+    qb, eb = oracle.ozaki_slice_row(b)
+    assert ea == 0 and eb == 0
+    acc = _acc_of(spec)
+    got_acc = qa.astype(np.int64) @ qb.astype(np.int64).T
+    assert got_acc.tolist() == acc
+    keep = 24 if out == "fp32" else 8
+    stated = _round_bits(_order_sum(acc, STATED), keep)
+    other = _order_sum(acc, LEVELS_UP if case.startswith("levels") else S_DESC)
+    assert stated == Fraction(want)
+    assert _round_bits(other, keep) != stated       # the order is visible here
+    res = oracle.ozaki_gemm(a[None, :], b[None, :], in_type="fp32", out_type=out)
+    if out == "fp32":
+        assert res[0, 0] == np.float32(want)
+    else:
+        assert int(res[0, 0]) == int(oracle.bf16_rne(np.array([want], np.float32))[0])
