@@ -78,6 +78,8 @@ _SYMBOLS = {
     "bg_desc_default_reduce": (C.c_int, [C.c_void_p]),
     "bg_desc_signature": (C.c_int, [C.c_void_p, C.c_void_p]),
     "bg_reduce_desc_signature": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "bg_desc_from_json": (C.c_int, [C.c_char_p, C.c_void_p, C.c_void_p]),
+    "bg_desc_to_json": (C.c_int, [C.c_void_p, C.c_void_p, C.c_char_p, C.c_size_t, C.c_void_p]),
     "bg_gemm_split_cuts": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p]),
     "bg_gemm_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p]),
     "bg_gemm_bf16": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
@@ -224,6 +226,24 @@ def reduce_desc(spec=None, **overrides):
     for k, v in (spec.get("schedule") or {}).items():
         setattr(d.sched, k, int(v))
     return d
+
+
+def desc_from_json(text):
+    """(GemmDesc, ReduceDesc) from descriptor JSON text, read by the library."""
+    g, r = GemmDesc(), ReduceDesc()
+    _check(lib().bg_desc_from_json(text.encode() if isinstance(text, str) else text, C.byref(g), C.byref(r)))
+    return g, r
+
+
+def desc_to_json(gemm=None, reduce=None):
+    """Descriptor JSON text of a GemmDesc and/or ReduceDesc, written by the library."""
+    n = C.c_size_t(0)
+    gp = C.byref(gemm) if gemm is not None else None
+    rp = C.byref(reduce) if reduce is not None else None
+    lib().bg_desc_to_json(gp, rp, None, 0, C.byref(n))   # asks for the length
+    buf = C.create_string_buffer(n.value + 1)
+    _check(lib().bg_desc_to_json(gp, rp, buf, n.value + 1, C.byref(n)))
+    return buf.value.decode()
 
 
 def signature(desc):

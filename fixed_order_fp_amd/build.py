@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libbitgemm.so")
 PROFILE = os.path.join(HERE, "profiles", "gfx950.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["bg_api.hip", "bg_probe.hip", "bg_gemm_bf16.hip", "bg_reduce.hip", "bg_w8a8.hip", "bg_quant.hip", "bg_ozaki.hip"]
+SOURCES = ["bg_api.hip", "bg_desc_json.cpp", "bg_probe.hip", "bg_gemm_bf16.hip", "bg_reduce.hip", "bg_w8a8.hip",
+           "bg_quant.hip", "bg_ozaki.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -266,6 +266,11 @@ void fused_reduce_shape(const bg_reduce_desc* rd, int64_t M, int64_t N, int64_t&
 
 }  // namespace
 
+namespace bg {
+// the descriptor JSON reader and writer report their refusals here
+bg_status json_fail(bg_status s, const std::string& msg) { return fail(s, msg); }
+}  // namespace bg
+
 extern "C" {
 
 int bg_abi_version(void) { return BG_ABI_VERSION; }
@@ -644,6 +649,9 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
     if (st != BG_OK) return st;
     if (M < 0 || N < 0 || K < 1) return fail(BG_E_INVALID, "bad sizes");
     if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    // the split is [0, K): its end is a cut point, which the kernels take in
+    // whole 16-byte chunks (as bg_gemm_bf16 requires of every cut point)
+    if (K % 8) return fail(BG_E_UNSUPPORTED, "K must be a multiple of 8 (the cut point at K)");
     if (!(rd->op & BG_RED_SUM)) out_sum = nullptr;
     if (!(rd->op & BG_RED_SUMSQ)) out_sumsq = nullptr;
     int64_t n_leaf, n_out;

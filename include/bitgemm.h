@@ -192,6 +192,28 @@ uint64_t bg_profile_hash(void);
 bg_status bg_desc_default_gemm(bg_gemm_desc* d);
 bg_status bg_desc_default_reduce(bg_reduce_desc* d);
 
+/* Descriptors as JSON text: the frozen record of [T] 4 in the form it is
+ * stored and handed between tools (the oracle reads the same text).
+ * Document: {"gemm": {...}, "reduce": {...}}, either member optional; the
+ * keys are the struct field names (the schedule as a "schedule" object),
+ * enum values by name ("bf16", "F32_32X32X16_BF16", "EXPLICIT", "row",
+ * "fused", ...), integers as plain JSON integers, mfma_profile_hash as a
+ * string "0x" + 16 hex digits, and "cuts" an array of split_k + 1 points.
+ * bg_desc_from_json: g and/or r (either may be NULL, not both) are set to
+ *   the defaults of bg_desc_default_gemm / bg_desc_default_reduce with the
+ *   document's fields applied.  A malformed document, an unknown key, a value
+ *   of the wrong type or name, or a cut table of another length is
+ *   BG_E_INVALID and leaves g and r untouched.  It reads the record only;
+ *   whether the library can realise it is decided by the call that uses it.
+ * bg_desc_to_json: writes every field of g and/or r (NULL skips it) as one
+ *   NUL-terminated document into buf (host memory, cap bytes); *len (if not
+ *   NULL) gets the text's length without the NUL.  cap too small (or buf
+ *   NULL) is BG_E_INVALID with *len set.  A field holding a value that has
+ *   no name is BG_E_INVALID.  Reading the text back gives equal order
+ *   fields, schedule and signature. */
+bg_status bg_desc_from_json(const char* json, bg_gemm_desc* g, bg_reduce_desc* r);
+bg_status bg_desc_to_json(const bg_gemm_desc* g, const bg_reduce_desc* r, char* buf, size_t cap, size_t* len);
+
 /* 128-bit signature over the order fields only (FNV-1a, two lanes).  Equal
  * signatures mean equal arithmetic ([T] 4). */
 bg_status bg_desc_signature(const bg_gemm_desc* d, uint64_t sig[2]);
@@ -253,7 +275,9 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
  * row m over its columns (norm statistics); leaves of 32 consecutive elements
  * folded in index order with no seed, then a balanced tree over the leaves.
  * The result equals bg_reduce_tree(rd) applied to the fp32 C of the same
- * GEMM.  rd->in_type must be FP32; the reduced axis holds at most 1024 leaves.
+ * GEMM.  rd->in_type must be FP32; the reduced axis holds at most 1024 leaves;
+ * K must be a multiple of 8 (BG_E_UNSUPPORTED otherwise, as bg_gemm_bf16
+ * requires of every cut point).
  * out_sum / out_sumsq: fp32 [N] (COL) or [M] (ROW), NULL where rd->op leaves
  * them out.  ws: at least bg_gemm_bf16_reduce_workspace_bytes() bytes, 4-byte
  * aligned (one fp32 node per leaf and output).  M or N = 0 enqueues nothing

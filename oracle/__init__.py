@@ -395,3 +395,87 @@ def reduce(X, axis, leaf_len=32, sq_fused=True, in_type=None, threads=None):
                     _ptr(X), cols, int(leaf_len), 1 if sq_fused else 0, _ptr(s), _ptr(q),
                     threads or default_threads())
     return s, q
+
+
+# --------------------------------------------------------------------------
+# descriptor JSON
+# --------------------------------------------------------------------------
+# The oracle reads the same descriptor text the library reads ("Taming
+# Bitwise Behavior", section 4: the descriptor is a frozen record), with its
+# own reader (Python's json module), and turns it into the specs the
+# functions above take.  Fields it does not emulate must hold the value it
+# does: a record asking for anything else is refused rather than computed in
+# another order.
+_GEMM_KEYS = {"version", "a_type", "b_type", "acc_type", "out_type", "partial_type", "merge_type", "mfma",
+              "acc_update", "k_order", "short_turn", "k_slot_layout", "split_k", "cut_rule", "cut_unit", "cuts",
+              "combine", "odd_rule", "rounding_point", "epilogue", "mfma_profile_hash", "schedule"}
+_REDUCE_KEYS = {"version", "in_type", "acc_type", "out_type", "op", "axis", "leaf_len", "leaf_order", "sq_fma",
+                "tree", "odd_rule", "schedule"}
+# the one value the oracle emulates for each field it does not vary
+_GEMM_FIXED = {"version": 1, "acc_update": "IN_MFMA", "k_order": "ASCENDING", "short_turn": "LAST",
+               "k_slot_layout": "CONTIGUOUS", "partial_type": "fp32", "merge_type": "fp32",
+               "odd_rule": "CARRY_LAST", "rounding_point": "AFTER_COMBINE_RNE"}
+_REDUCE_FIXED = {"version": 1, "acc_type": "fp32", "out_type": "fp32", "leaf_order": "SEQUENTIAL_NO_SEED",
+                 "tree": "BALANCED", "odd_rule": "CARRY_LAST"}
+
+
+def _fnv1a64(data):
+    h = 0xCBF29CE484222325
+    for b in data:
+        h = ((h ^ b) * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def profile_models_hash(profile):
+    """FNV-1a 64 of the canonical JSON of a probe profile's measured models
+    (the hash a descriptor carries as mfma_profile_hash)."""
+    import json as _json
+    canon = _json.dumps(profile.get("models", {}), sort_keys=True, separators=(",", ":"))
+    return _fnv1a64(canon.encode())
+
+
+def desc_from_json(text, profile):
+    """Descriptor JSON text -> (gemm spec or None, reduce spec or None) for
+    gemm_bf16 / w8a8_pow2 / reduce.  `profile` is the probe's profile dict:
+    its models give the instruction model, and its hash must equal the
+    record's mfma_profile_hash (when the record names one)."""
+    import json as _json
+    doc = _json.loads(text)
+    if not isinstance(doc, dict) or set(doc) - {"gemm", "reduce"}:
+        raise ValueError("the document holds 'gemm' and/or 'reduce' only")
+    g = r = None
+    if "gemm" in doc:
+        src = doc["gemm"]
+        if set(src) - _GEMM_KEYS:
+            raise ValueError(f"unknown gemm keys {sorted(set(src) - _GEMM_KEYS)}")
+        for k, v in _GEMM_FIXED.items():
+            if k in src and src[k] != v:
+                raise ValueError(f"the oracle emulates {k} = {v!r} only, not {src[k]!r}")
+        if src.get("combine", "BALANCED_NEIGHBOURS_FIRST") not in COMBINE:
+            raise ValueError(f"unknown combine {src['combine']!r}")
+        if "mfma_profile_hash" in src and int(src["mfma_profile_hash"], 16) != profile_models_hash(profile):
+            raise ValueError("the record's mfma_profile_hash is not this profile's")
+        mfma = src.get("mfma", "F32_32X32X16_BF16")
+        g = {"mfma": mfma, "split_k": int(src.get("split_k", 1)),
+             "cut_rule": src.get("cut_rule", "UNIT256_REMAINDER_LAST"), "cut_unit": int(src.get("cut_unit", 256)),
+             "combine": src.get("combine", "BALANCED_NEIGHBOURS_FIRST"), "out_type": src.get("out_type", "bf16"),
+             "epilogue": src.get("epilogue", "NONE")}
+        if g["cut_rule"] not in ("UNIT256_REMAINDER_LAST", "EXPLICIT"):
+            raise ValueError(f"unknown cut_rule {g['cut_rule']!r}")
+        if "cuts" in src:
+            g["cuts"] = [int(c) for c in src["cuts"]]
+        if mfma in INSTR_K:   # the bf16 instructions: the measured model of one instruction
+            g["mfma_model"] = profile["models"][mfma]
+    if "reduce" in doc:
+        src = doc["reduce"]
+        if set(src) - _REDUCE_KEYS:
+            raise ValueError(f"unknown reduce keys {sorted(set(src) - _REDUCE_KEYS)}")
+        for k, v in _REDUCE_FIXED.items():
+            if k in src and src[k] != v:
+                raise ValueError(f"the oracle emulates {k} = {v!r} only, not {src[k]!r}")
+        r = {"in_type": src.get("in_type", "fp32"), "op": src.get("op", "sum_and_sumsq"),
+             "axis": src.get("axis", "row"), "leaf_len": int(src.get("leaf_len", 32)),
+             "sq_fused": src.get("sq_fma", "fused") == "fused"}
+        if src.get("sq_fma", "fused") not in ("fused", "unfused"):
+            raise ValueError(f"unknown sq_fma {src['sq_fma']!r}")
+    return g, r

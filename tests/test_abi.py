@@ -173,3 +173,114 @@ def test_shapes_past_one_launch_are_refused(bg):
     assert fused("col", 32769, 40) == unsup and fused("row", 3, 32769) == unsup
     # the probe: 64 lanes per case
     assert L.bg_probe_mfma(0, 1 << 26, p, p, p, p, None) == unsup
+
+
+def test_fused_reduce_refuses_k_off_the_chunk_grid(bg):
+    """K is the split's end, a cut point: like bg_gemm_bf16 the fused call takes
+    it only on the 8-element chunk grid, even where lda leaves room for the
+    chunk (a sliced view K = 20 of rows of 24): refused before any launch."""
+    L, p, big = bg.lib(), C.c_void_p(0x10000), C.c_size_t(1 << 40)
+    dg = bg.gemm_desc({}, out_type="fp32")
+    rd = bg.reduce_desc({"in_type": "fp32", "axis": "col"})
+    call = lambda K, ld: L.bg_gemm_bf16_reduce(C.byref(dg), C.byref(rd), 64, 64, K, p, ld, p, ld, p, 64,
+                                               p, p, p, big, None)
+    assert call(20, 24) == 2
+    assert b"multiple of 8" in L.bg_last_error()
+    assert _call_gemm(bg, bg.gemm_desc({}), K=20, lda=24) == 2   # the plain GEMM alike
+
+
+# ---------------------------------------------------------------------------
+# descriptors as JSON text
+# ---------------------------------------------------------------------------
+def _struct_bytes(d):
+    return bytes(memoryview(d))
+
+
+JSON_DOCS = [
+    '{"gemm": {}}',
+    '{"gemm": {"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 256, 512], "out_type": "fp32"}}',
+    '{"gemm": {"split_k": 16, "out_type": "fp32", "schedule": {"bm": 128, "bn": 64, "bk": 32, '
+    '"waves_m": 2, "waves_n": 2, "load_path": 2, "stages": 8}}}',
+    '{"gemm": {"mfma": "F32_16X16X32_BF16", "combine": "SEQUENTIAL", "cut_unit": 128, "split_k": 3}}',
+    '{"gemm": {"mfma": "I32_32X32X32_I8", "a_type": "int8", "b_type": "int8", "acc_type": "int32", '
+    '"out_type": "bf16", "epilogue": "W8A8_POW2"}}',
+    '{"reduce": {"axis": "col", "in_type": "bf16", "op": "sum", "sq_fma": "unfused", '
+    '"schedule": {"leaves_per_wg": 8}}}',
+    '{"gemm": {"acc_update": "SEPARATE_ADD", "short_turn": "FIRST", "k_slot_layout": "STRIDED"}, '
+    '"reduce": {"op": "sumsq"}}',
+]
+
+
+@pytest.mark.parametrize("text", JSON_DOCS)
+def test_json_round_trip_keeps_the_record(bg, text):
+    """[T] section 4: the descriptor is a frozen record.  Text read by the
+    library, written back and read again gives the same bytes (order fields
+    and schedule) and the same signature."""
+    g1, r1 = bg.desc_from_json(text)
+    back = bg.desc_to_json(g1, r1)
+    g2, r2 = bg.desc_from_json(back)
+    assert _struct_bytes(g1) == _struct_bytes(g2) and _struct_bytes(r1) == _struct_bytes(r2)
+    assert bg.signature(g1) == bg.signature(g2) and bg.signature(r1) == bg.signature(r2)
+    assert bg.desc_to_json(g2, r2) == back          # the writer is canonical
+
+
+def test_json_agrees_with_field_by_field_construction(bg):
+    spec = {"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 256, 512], "out_type": "fp32"}
+    g, _ = bg.desc_from_json('{"gemm": %s}' % __import__("json").dumps(spec))
+    d = bg.gemm_desc(spec)
+    assert bg.signature(g) == bg.signature(d) and _struct_bytes(g) == _struct_bytes(d)
+    # an absent member leaves the defaults, including the library's profile hash
+    g0, r0 = bg.desc_from_json("{}")
+    assert _struct_bytes(g0) == _struct_bytes(bg.gemm_desc({}))
+    assert _struct_bytes(r0) == _struct_bytes(bg.reduce_desc({}))
+    assert g0.mfma_profile_hash == bg.profile_hash()
+    # the hash is part of the record: another profile is another signature
+    g1, _ = bg.desc_from_json('{"gemm": {"mfma_profile_hash": "0x0000000000000001"}}')
+    assert g1.mfma_profile_hash == 1 and bg.signature(g1) != bg.signature(g0)
+
+
+@pytest.mark.parametrize("text, why", [
+    ('{"gemm": {"split_k": 2,}}', "malformed"),
+    ('{"gemm": {"split_k": 2}', "malformed"),
+    ('{"gemm": {"split_k": 2}} x', "after the document"),
+    ('[1, 2]', "must be an object"),
+    ('{"gemm": {"splitk": 2}}', "unknown gemm key"),
+    ('{"gemm": {"split_k": "2"}}', "must be an integer"),
+    ('{"gemm": {"split_k": 2.0}}', "integers"),
+    ('{"gemm": {"split_k": -1}}', "must be an integer"),
+    ('{"gemm": {"mfma": "F32_32X32X8_BF16"}}', "unknown value"),
+    ('{"gemm": {"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 512]}}', "split_k + 1"),
+    ('{"gemm": {"cuts": [0, "256"]}}', "array of integers"),
+    ('{"gemm": {"mfma_profile_hash": 123}}', "hex"),
+    ('{"gemm": {"mfma_profile_hash": "0x12345"}}', "hex"),
+    ('{"gemm": {"split_k": 2, "split_k": 4}}', "duplicate"),
+    ('{"gemm": {"schedule": {"tile": 3}}}', "unknown gemm schedule key"),
+    ('{"reduce": {"axis": "diagonal"}}', "unknown value"),
+    ('{"gemm": {}, "profile": {}}', "unknown top-level key"),
+    ('', "malformed"),
+])
+def test_json_refusals(bg, text, why):
+    """A document that is not exactly a descriptor record is refused with
+    BG_E_INVALID, and the output structs are left as they were."""
+    L = bg.lib()
+    g, r = bg.gemm_desc({"split_k": 5}), bg.reduce_desc({"axis": "col"})
+    before = (_struct_bytes(g), _struct_bytes(r))
+    st = L.bg_desc_from_json(text.encode(), C.byref(g), C.byref(r))
+    assert st == 1, (text, st)
+    assert why.encode() in L.bg_last_error(), L.bg_last_error()
+    assert (_struct_bytes(g), _struct_bytes(r)) == before
+
+
+def test_json_writer_buffer_and_names(bg):
+    L = bg.lib()
+    g = bg.gemm_desc({})
+    n = C.c_size_t(0)
+    assert L.bg_desc_to_json(C.byref(g), None, None, 0, C.byref(n)) == 1 and n.value > 100
+    small = C.create_string_buffer(n.value)          # one byte short of the NUL
+    assert L.bg_desc_to_json(C.byref(g), None, small, n.value, C.byref(n)) == 1
+    assert b"buffer too small" in L.bg_last_error()
+    g.mfma = 99                                      # a value with no name
+    big = C.create_string_buffer(4096)
+    assert L.bg_desc_to_json(C.byref(g), None, big, 4096, C.byref(n)) == 1
+    assert L.bg_desc_to_json(None, None, big, 4096, C.byref(n)) == 1
+    assert L.bg_desc_from_json(None, C.byref(g), None) == 1

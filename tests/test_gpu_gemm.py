@@ -266,3 +266,33 @@ def test_two_rounds_of_large_tiles_match_one_round_tiles():
     ni = rng.integers(0, 8000, 96)
     ref = oracle.gemm_bf16_points(oracle_desc({"out_type": "bf16"}, "F32_32X32X16_BF16"), A, B, mi, ni)
     assert np.array_equal(walk[mi, ni], ref)
+
+
+@pytest.mark.parametrize("text", [
+    '{"gemm": {"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 256, 512], "out_type": "fp32"}}',
+    '{"gemm": {"split_k": 3, "cut_unit": 64, "out_type": "bf16"}}',
+    '{"gemm": {"mfma": "F32_16X16X32_BF16", "split_k": 4, "cut_unit": 128, "out_type": "fp32", '
+    '"schedule": {"bm": 64, "bn": 64, "bk": 64, "waves_m": 2, "waves_n": 2}}}',
+])
+def test_one_json_record_drives_both_sides(text):
+    """[T] section 4: one frozen record.  The same descriptor text is read by
+    the library (bg_desc_from_json) and by the oracle (its own reader); the
+    outputs are bit-identical."""
+    import torch
+    import fixed_order_fp_amd as bg
+    import oracle
+    from gpu_util import profile
+    print_case("json record", text)
+    g, _ = bg.desc_from_json(text)
+    spec, _ = oracle.desc_from_json(text, profile())
+    A = synth.bf16_spread(71, (70, 512), -20, 20)
+    B = synth.bf16_spread(72, (136, 512), -20, 20)
+    out = spec["out_type"]
+    dC = torch.empty((70, 136), dtype=torch.float32 if out == "fp32" else torch.int16, device="cuda")
+    nws = bg.gemm_workspace_bytes(g, 70, 136, 512)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    bg.gemm_bf16(g, to_dev_u16(A), to_dev_u16(B), dC, ws)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy().view(np.uint32 if out == "fp32" else np.uint16)
+    ref = oracle.gemm_bf16(spec, A, B)
+    assert np.array_equal(got, ref.view(np.uint32 if out == "fp32" else np.uint16))

@@ -243,3 +243,37 @@ def test_points_match_full_output():
     ni = rng.integers(0, 64, 50)
     pts = oracle.gemm_bf16_points(desc(model, S=2, cuts=[0, 256, 512]), A, B, mi, ni)
     assert np.array_equal(pts, full[mi, ni])
+
+
+# ---------------------------------------------------------------------------
+# the oracle reads the descriptor JSON the library reads
+# ---------------------------------------------------------------------------
+def _profile():
+    import json as _json
+    import os as _os
+    path = _os.path.join(_os.path.dirname(_os.path.dirname(_os.path.abspath(__file__))),
+                         "fixed_order_fp_amd", "profiles", "gfx950.json")
+    with open(path) as f:
+        return _json.load(f)
+
+
+def test_oracle_reads_descriptor_json():
+    """The same record text gives the oracle the spec it is otherwise handed
+    as a dict: equal results on a small split GEMM; refusals of what it does
+    not emulate and of another profile's hash."""
+    prof = _profile()
+    text = ('{"gemm": {"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 256, 512], "out_type": "fp32", '
+            '"mfma_profile_hash": "0x%016x"}}' % oracle.profile_models_hash(prof))
+    g, r = oracle.desc_from_json(text, prof)
+    assert r is None and g["split_k"] == 2 and g["cuts"] == [0, 256, 512]
+    A, B = synth.gemm_small()
+    direct = {"mfma": "F32_32X32X16_BF16", "mfma_model": prof["models"]["F32_32X32X16_BF16"], "split_k": 2,
+              "cut_rule": "EXPLICIT", "cuts": [0, 256, 512], "out_type": "fp32"}
+    assert np.array_equal(oracle.gemm_bf16(g, A, B).view(np.uint32), oracle.gemm_bf16(direct, A, B).view(np.uint32))
+    _, rd = oracle.desc_from_json('{"reduce": {"axis": "col", "sq_fma": "unfused"}}', prof)
+    assert rd["axis"] == "col" and rd["sq_fused"] is False
+    for bad in ('{"gemm": {"acc_update": "SEPARATE_ADD"}}', '{"gemm": {"k_slot_layout": "STRIDED"}}',
+                '{"gemm": {"mfma_profile_hash": "0x0000000000000001"}}', '{"gemm": {"tile": 1}}',
+                '{"reduce": {"tree": "SEQUENTIAL"}}', '{"other": {}}'):
+        with pytest.raises(ValueError):
+            oracle.desc_from_json(bad, prof)
