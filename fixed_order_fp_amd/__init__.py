@@ -85,6 +85,8 @@ _SYMBOLS = {
     "bg_gemm_bf16": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_size_t,
                                C.c_void_p]),
+    "bg_gemm_bf16_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
+                                       C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p]),
     "bg_gemm_w8a8_pow2": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                     C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                     C.c_void_p, C.c_int64, C.c_void_p]),
@@ -287,6 +289,15 @@ def gemm_bf16(desc, A, B, C_out, ws=None, stream=None):
     _check(lib().bg_gemm_bf16(C.byref(desc), M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0),
                               _ptr(C_out), C_out.stride(0), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gemm_bf16_noalloc(desc, A, B, C_out, stream=None):
+    """C_out = A B^T under desc with the library's static scratch for split-K
+    partials (no workspace argument)."""
+    M, K = A.shape
+    N = B.shape[0]
+    _check(lib().bg_gemm_bf16_noalloc(C.byref(desc), M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                                      _ptr(C_out), C_out.stride(0), _stream(stream)))
 
 
 def gemm_w8a8_pow2(desc, A, W, a_scale, w_scale, Y, acc_out=None, stream=None):

@@ -264,6 +264,36 @@ void fused_reduce_shape(const bg_reduce_desc* rd, int64_t M, int64_t N, int64_t&
     bytes = (size_t)n_leaf * (size_t)n_out * sizeof(float) * (size_t)arrays;
 }
 
+// ---- the static scratch of bg_gemm_bf16_noalloc -----------------------------
+// Split-K partials of the allocation-free entry point live here: one copy per
+// GPU, allocated with the library's code object when it is loaded on that GPU
+// and held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is taken once per
+// device with hipGetSymbolAddress (that device current) and only that address
+// is handed to kernels.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device; nullptr until taken
+
+bg_status scratch_for_current_device(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BG_E_HIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(BG_E_HIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BG_OK;
+}
+
 }  // namespace
 
 namespace bg {
@@ -467,6 +497,28 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
                                         (float*)ws, stream);
     if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
     return BG_OK;
+}
+
+bg_status bg_gemm_bf16_noalloc(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, const void* A,
+                               int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream)
+{
+    size_t need = 0;
+    bg_status st = bg_gemm_workspace_bytes(d, M, N, K, &need);
+    if (st != BG_OK) return st;
+    if (need > kNoallocScratchBytes)
+        return fail(BG_E_WORKSPACE, "bg_gemm_bf16_noalloc: the split partials need " + std::to_string(need) +
+                                        " bytes; the static scratch holds " + std::to_string(kNoallocScratchBytes));
+    void* ws = nullptr;
+    if (need > 0 && M > 0 && N > 0) {
+        st = check_device();  // the scratch exists only where the gfx950 code object is loaded
+        if (st != BG_OK) return st;
+        st = scratch_for_current_device(&ws);
+        if (st != BG_OK) return st;
+    }
+    // the same validation, plan and kernels as bg_gemm_bf16, with the
+    // scratch as the workspace (every partial is written before it is read,
+    // so nothing is cleared)
+    return bg_gemm_bf16(d, M, N, K, A, lda, B, ldb, C, ldc, ws, ws ? kNoallocScratchBytes : 0, stream);
 }
 
 bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, const int8_t* A,

@@ -249,6 +249,23 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K,
                        void* C, int64_t ldc, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* bg_gemm_bf16 for callers that cannot allocate device memory or hand in a
+ * workspace (code under stream or graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same descriptor, arguments, order,
+ * kernels and bits as bg_gemm_bf16, with the split-K partials kept in a
+ * static scratch inside the library instead of a caller workspace.
+ * The scratch is 64 MiB per GPU (S * M * N * 4 bytes at most; e.g. split-K 16
+ * at 256 x 2560 takes 42 MB), allocated with the library's code object on
+ * each GPU it runs on and held until the process ends; a call that needs
+ * more is refused with BG_E_WORKSPACE before anything is enqueued.  The call
+ * itself allocates nothing.  Every call on one GPU shares that GPU's scratch:
+ * calls that can overlap in time on one GPU (different streams without
+ * ordering) race on it and must be ordered by the caller.  S = 1 uses no
+ * scratch. */
+bg_status bg_gemm_bf16_noalloc(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               void* C, int64_t ldc, hipStream_t stream);
+
 /* W8A8 with power-of-two weight scales ([W] section II):
  *   acc[m][n] = sum_k A[m][k] * W[n][k] in exact int32 (order-free: |acc| <=
  *   K * 127^2 must stay below 2^31, so K <= 133,144);
