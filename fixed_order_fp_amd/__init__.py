@@ -109,6 +109,8 @@ _SYMBOLS = {
     "bg_bench_gemm_bf16_free": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                           C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int32,
                                           C.c_void_p]),
+    "bg_bench_gemm_w8a8_free": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
+                                          C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
     "bg_bench_reduce_free": (C.c_int, [C.c_uint32, C.c_uint32, C.c_int64, C.c_int64, C.c_void_p,
                                        C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "bg_probe_mfma": (C.c_int, [C.c_uint32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -368,6 +370,13 @@ def bench_gemm_bf16_free(A, B, C_out, split_k=0, stream=None):
     N = B.shape[0]
     _check(lib().bg_bench_gemm_bf16_free(M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0),
                                          _ptr(C_out), C_out.stride(0), int(split_k), _stream(stream)))
+
+
+def bench_gemm_w8a8_free(A, W, a_scale, w_scale, Y, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().bg_bench_gemm_w8a8_free(M, N, K, _ptr(A), A.stride(0), _ptr(W), W.stride(0), _ptr(a_scale),
+                                         _ptr(w_scale), _ptr(Y), Y.stride(0), _stream(stream)))
 
 
 def bench_reduce_free(axis, in_type, X, out_sum=None, out_sumsq=None, stream=None):

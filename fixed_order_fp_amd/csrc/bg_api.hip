@@ -913,6 +913,29 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     return BG_OK;
 }
 
+bg_status bg_bench_gemm_w8a8_free(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
+                                  int64_t ldw, const float* a_scale, const float* w_scale, void* Y, int64_t ldy,
+                                  hipStream_t stream)
+{
+    if (M < 0 || N < 0 || K < 1 || K > 131071) return fail(BG_E_INVALID, "bad sizes");
+    if (lda < K || ldw < K || ldy < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !W || !a_scale || !w_scale || !Y) return fail(BG_E_INVALID, "NULL tensor");
+    if (!aligned16(A) || !aligned16(W) || lda % 16 || ldw % 16 || !aligned16(Y) || ldy % 8 ||
+        ((uintptr_t)a_scale & 3u) || ((uintptr_t)w_scale & 3u))
+        return fail(BG_E_ALIGN, "pointers must be aligned and leading dimensions multiples of 16 (int8) / 8");
+    bg::W8A8Plan p{};
+    p.mfma = BG_MFMA_I32_32X32X32_I8;
+    choose_w8a8_pipe(p, M, N);  // the same tile and main loop as bg_gemm_w8a8_pow2
+    p.free_epilogue = true;
+    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n)) return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_w8a8(p, M, N, K, A, lda, W, ldw, a_scale, w_scale, (uint16_t*)Y, ldy, nullptr, 0, stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
 bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, int64_t cols, const void* X,
                                int64_t ldx, float* out_sum, float* out_sumsq, hipStream_t stream)
 {

@@ -85,6 +85,7 @@ struct W8A8Plan {
     int bm, bn, waves_m, waves_n, group_m;
     int path;    // 1: direct-to-LDS double buffer; 2: pipelined (32x32x32 only)
     int stages;  // k tiles in LDS (pipelined path; 0 = the tile's default)
+    bool free_epilogue;  // free-order twin (bench only): y = fp32(acc) * (a_scale * w_scale)
 };
 
 bool w8a8_has_tile(int mfma, int bm, int bn, int waves_m, int waves_n, int path, int stages);

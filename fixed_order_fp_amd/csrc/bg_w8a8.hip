@@ -206,7 +206,8 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
 // stores.  A short last k tile (K not a multiple of 64) is copied
 // through registers with zeros past K.
 // MODE 0: Y; 1: Y and the int32 accumulators; 2: the accumulators only (no
-// scales, no Y: the integer products other paths build on)
+// scales, no Y: the integer products other paths build on); 3: Y with the
+// epilogue's order left free (the bench's free-order twin)
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
     PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU)))
@@ -380,7 +381,9 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
 
     // epilogue: block (j, i), element 4q+u of lane l is row m = wm*WTM + 32i +
     // l%32, column n = wn*WTN + 32j + 8q + 4(l/32) + u
-    constexpr bool WANT_Y = MODE != 2, WANT_ACC = MODE != 0;
+    // MODE 3 (free-order twin, bench only): Y with the epilogue's order left
+    // free -- one combined scale a_scale * w_scale multiplied in once
+    constexpr bool WANT_Y = MODE != 2, WANT_ACC = MODE == 1 || MODE == 2;
     __syncthreads();  // every wave is done with the operand stages
     unsigned char* cl = (unsigned char*)lds;
 #pragma unroll
@@ -401,8 +404,12 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
                     for (int u = 0; u < 4; u++) {
                         const float ws = w_scale[gn + u < N ? gn + u : N - 1];
                         const float f = (float)acc[j][i][4 * q + u];  // v_cvt_f32_i32: round to nearest even
-                        const float tt = f * ws;                       // exact: a power of two
-                        y[u] = tt * as;                                // the one rounding
+                        if constexpr (MODE == 3) {
+                            y[u] = f * (as * ws);
+                        } else {
+                            const float tt = f * ws;  // exact: a power of two
+                            y[u] = tt * as;           // the one rounding
+                        }
                     }
                     uint2 w;
                     w.x = bf16x2_rne(y[0], y[1]);
@@ -448,7 +455,10 @@ hipError_t launch_pipe(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
     dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
-    if (!Y)
+    if (p.free_epilogue)  // free-order twin (bench only)
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 3>), grid, block, 0, stream, A, lda, W, ldw,
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+    else if (!Y)
         hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, stream, A, lda, W, ldw,
                            a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
     else if (acc_out)

@@ -388,6 +388,15 @@ bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols,
 bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                   const void* B, int64_t ldb, float* C, int64_t ldc,
                                   int32_t split_k, hipStream_t stream);
+/* W8A8 with the epilogue's order left free: the same tile, main loop and
+ * exact int32 sums as bg_gemm_w8a8_pow2, then y = bf16(fp32(acc) *
+ * (a_scale[m] * w_scale[n])) -- the two scales combined first, as an
+ * implementation free to reorder would.  With power-of-two w_scale this gives
+ * the same bits ([W] section II: power-of-two commutation); it is the
+ * denominator of what holding the epilogue's order costs. */
+bg_status bg_bench_gemm_w8a8_free(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                                  const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale,
+                                  void* Y, int64_t ldy, hipStream_t stream);
 bg_status bg_bench_reduce_free(uint32_t axis, uint32_t in_type, int64_t rows, int64_t cols,
                                const void* X, int64_t ldx, float* out_sum, float* out_sumsq,
                                hipStream_t stream);

@@ -153,3 +153,23 @@ def test_batch_invariance():
         print_case("w8a8 batch", m)
         part, _ = run_w8a8(a_q[:m], w_q, a_s[:m], w_s, want_acc=False)
         assert np.array_equal(part, full[:m])
+
+
+def test_free_order_epilogue_twin_gives_the_same_bits():
+    """The bench's free-order twin (same main loop, the two scales combined
+    before the multiply) returns the fixed epilogue's bits when the weight
+    scales are powers of two ([W] section II: power-of-two commutation)."""
+    import torch
+    import fixed_order_fp_amd as bg
+    a_q, w_q, a_s, w_s = synth.w8a8_input(M=200, N=320, K=512)
+    print_case("w8a8 free twin 200x320x512")
+    d = bg.gemm_desc(dict(mfma="I32_32X32X32_I8", a_type="int8", b_type="int8", acc_type="int32",
+                          out_type="bf16", epilogue="W8A8_POW2"))
+    dA, dW = torch.from_numpy(a_q).cuda(), torch.from_numpy(w_q).cuda()
+    sa, sw = torch.from_numpy(a_s).cuda(), torch.from_numpy(w_s).cuda()
+    Y = torch.empty((200, 320), dtype=torch.int16, device="cuda")
+    Yf = torch.full((200, 320), 7, dtype=torch.int16, device="cuda")
+    bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, Y)
+    bg.bench_gemm_w8a8_free(dA, dW, sa, sw, Yf)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Yf)
