@@ -18,9 +18,17 @@ without evaluating addresses:
     many accumulators as the wave owns output blocks.
 
 The k order itself (which k block each instruction reads) comes from LDS
-addresses and is checked at run time, bit for bit against the oracle."""
+addresses and is checked at run time, bit for bit against the oracle.
+
+Canonical dependence-tree signatures (further below) read the tree of one
+output back from the code of the split-K combine (the partials' loads
+resolved to their plane index, then the adds) and of the row reduction (the
+leaf's loads numbered by offset, the fold, the DPP steps and the readlanes),
+so that variants and builds can be compared with each other and with the
+tree the definition gives."""
 import hashlib
 import os
+from fractions import Fraction
 import re
 import subprocess
 import sys
@@ -38,9 +46,10 @@ STORES = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store
           "global_load_lds", "buffer_load_dword lds", "global_atomic", "buffer_atomic", "ds_add", "s_")
 
 
-def device_asm(src):
+def device_asm(src, opt="-O3"):
     """AMDGCN text of one source file, compiled as the library is (cached by
-    the source's and its headers' contents)."""
+    the source's and its headers' contents); `opt` replaces the optimisation
+    level, for a second build to compare with the library's."""
     sys.path.insert(0, ROOT)
     from fixed_order_fp_amd import build as B
     h = hashlib.sha256()
@@ -51,9 +60,9 @@ def device_asm(src):
     with open(os.path.join(ROOT, "include", "bitgemm.h"), "rb") as fh:
         h.update(fh.read())
     os.makedirs(CACHE, exist_ok=True)
-    out = os.path.join(CACHE, f"{os.path.splitext(src)[0]}.{h.hexdigest()[:16]}.s")
+    out = os.path.join(CACHE, f"{os.path.splitext(src)[0]}.{opt.lstrip('-')}.{h.hexdigest()[:16]}.s")
     if not os.path.exists(out):
-        flags = [f for f in B.FLAGS if f != "-fPIC"]
+        flags = [opt if f == "-O3" else f for f in B.FLAGS if f != "-fPIC"]
         cmd = [B.HIPCC, *flags, f"-DBG_PROFILE_HASH=0x{B.profile_hash():016x}ull", "--cuda-device-only", "-S",
                os.path.join(CSRC, src), "-o", out + ".tmp"]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -219,3 +228,268 @@ def w8a8_variants(asm):
             e = BLOCK[i]
             out.append((name, lines, i, 128 // INSTR_K[i], (bm // wm // e) * (bn // wn // e)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Canonical dependence-tree signatures ("Taming Bitwise Behavior", section 6:
+# the reduction tree read back from the compiled code, so that two variants
+# or two builds can be compared; Table 3 lists an AMDGCN checker).  Each
+# signature is a string that names the floating-point operations of one
+# output's reduction and how they nest, with the registers renamed away:
+# equal strings mean the same tree, whatever the schedule or the build.
+# fp32 addition is commutative bit for bit on non-NaN operands, so the two
+# operands of an add are put in a canonical order; association is kept.
+# ---------------------------------------------------------------------------
+def balanced_tree(leaves):
+    """The balanced tree over `leaves` (strings), neighbours first, an odd
+    last node carried up, written as nested sums with commutative operands
+    sorted -- built from the definition, independently of any kernel."""
+    nodes = list(leaves)
+    while len(nodes) > 1:
+        nxt = [canon_add(nodes[i], nodes[i + 1]) for i in range(0, len(nodes) - 1, 2)]
+        if len(nodes) % 2:
+            nxt.append(nodes[-1])
+        nodes = nxt
+    return nodes[0]
+
+
+def canon_add(a, b):
+    return "(" + " + ".join(sorted((a, b))) + ")"
+
+
+def gemm_chain_signature(lines, instr, k_per_turn):
+    """The tree of one GEMM output inside one split, as the ISA shows it: a
+    single chain of the descriptor's matrix instruction accumulating in place,
+    one instruction per instruction_k of k.  Returns None when the kernel
+    does not have that shape (check_kernel then names the problem)."""
+    ins = instructions(lines)
+    accs = {}
+    for head, idx in loops(lines).items():
+        keep = set(idx)
+        for i, op, ops in ins:
+            if i in keep and op.startswith("v_mfma"):
+                if len(ops) != 4 or regs(ops[0]) != regs(ops[3]):
+                    return None
+                accs.setdefault(head, {}).setdefault(regs(ops[0]), []).append(op)
+    if not accs:
+        return None
+    shapes = set()
+    for head, per in accs.items():
+        for r, ops in per.items():
+            if len(set(ops)) != 1:
+                return None
+            shapes.add((ops[0], len(ops)))
+    if len({s[0] for s in shapes}) != 1:
+        return None
+    mnem = next(iter(shapes))[0]
+    # per turn of k_per_turn, one instruction per instruction_k
+    per_turn = {n for _, n in shapes}
+    if per_turn != {k_per_turn // INSTR_K[instr]}:
+        return None
+    return f"chain[{mnem}, in place, k step {INSTR_K[instr]}, ascending]"
+
+
+def _pair(op):
+    m = re.match(r"s\[(\d+):(\d+)\]$", op)
+    return (int(m.group(1)), int(m.group(2))) if m else None
+
+
+def _sym_loads(ins):
+    """Plane index of each dword load of a split-K combine kernel: partial s
+    sits at base + s * plane elements, the base being (idx << 2) + the
+    workspace pointer and the plane count a scalar pair, the offset formed as
+    (plane << shift), as a 64-bit multiply by a constant (low half from the
+    pair's low register) or as a shifted scalar pair.  Returns {instruction
+    index: (loaded register, plane)} or None when an address is not of that form or two
+    loads use different plane counts."""
+    val = {}      # low VGPR of an address pair -> (plane multiple, plane pair)
+    sval = {}     # scalar pair -> (plane multiple, plane pair)
+    loads = {}
+    planes = set()
+    for i, op, ops in ins:
+        if op == "s_lshl_b64" and len(ops) == 3 and _pair(ops[0]) and _pair(ops[1]) and ops[2].isdigit():
+            sval[_pair(ops[0])] = (Fraction(2 ** int(ops[2]), 4), _pair(ops[1]))
+        elif op == "v_lshl_add_u64" and len(ops) == 4:
+            d, a, sh, b = ops
+            dr = regs(d)
+            if a.startswith("v[") and _pair(b) and sh == "2" and regs(a)[1] not in val:
+                val[dr[1]] = (Fraction(0), None)                      # (idx << 2) + workspace
+            elif _pair(a) and b.startswith("v[") and regs(b)[1] in val and sh.isdigit():
+                k, q = val[regs(b)[1]]
+                val[dr[1]] = (k + Fraction(2 ** int(sh), 4), _pair(a))
+                planes.add(_pair(a))
+            elif a.startswith("v[") and regs(a)[1] in val and sh == "0" and _pair(b) in sval:
+                k, q = val[regs(a)[1]]
+                k2, q2 = sval[_pair(b)]
+                val[dr[1]] = (k + k2, q2)
+                planes.add(q2)
+            else:
+                val.pop(dr[1], None)
+        elif op == "v_mad_u64_u32" and len(ops) == 5:
+            d, _, a, c, b = ops
+            dr = regs(d)
+            if re.match(r"s\d+$", a) and any(int(a[1:]) == q[1] for q in planes):
+                pass                                                  # the high half of a product below
+            elif re.match(r"s\d+$", a) and c.isdigit() and b.startswith("v[") and regs(b)[1] in val:
+                k, q = val[regs(b)[1]]
+                lo = int(a[1:])
+                val[dr[1]] = (k + Fraction(int(c), 4), (lo, lo + 1))   # low half: base + c * plane
+                planes.add((lo, lo + 1))
+            else:
+                val.pop(dr[1], None)
+        elif op == "global_load_dword" and len(ops) >= 2:
+            r = regs(ops[1])
+            if r is None or r[1] not in val or val[r[1]][0].denominator != 1:
+                return None
+            loads[i] = (regs(ops[0])[1], int(val[r[1]][0]))
+    if len(planes) > 1:
+        return None
+    return loads
+
+
+def combine_tree_signature(lines):
+    """The tree a split-K combine kernel applies to the partials P0..P(S-1)
+    of one output, read from its adds, and the planes it loads (None if it
+    cannot be read).  Any other instruction writing a register that held a
+    partial sum passes it on as an opaque function of it (the rounding to
+    bf16 is integer code), so the stored value shows the sum it came from;
+    a register it writes from nothing tracked is dropped."""
+    ins = instructions(lines)
+    loads = _sym_loads(ins)
+    if not loads:
+        return None
+    expr = {}
+    last = None
+    for i, op, ops in ins:
+        if i in loads:
+            r, plane = loads[i]
+            expr[r] = f"P{plane}"
+        elif op.startswith("v_add_f32") and len(ops) == 3:
+            a, b = regs(ops[1]), regs(ops[2])
+            d = regs(ops[0])[1]
+            if a is None or b is None or a[1] not in expr or b[1] not in expr:
+                expr.pop(d, None)
+                continue
+            expr[d] = canon_add(expr[a[1]].split("cvt:")[-1], expr[b[1]].split("cvt:")[-1])
+        elif op.startswith(("global_store_dword", "global_store_short")):
+            r = regs(ops[1])
+            if r is not None and r[1] in expr:
+                last = expr[r[1]].split("cvt:")[-1]
+        elif op.startswith("v_") and ops and regs(ops[0]) and regs(ops[0])[0] == "v":
+            d = regs(ops[0])
+            srcs = [expr[regs(o)[1]] for o in ops[1:] if regs(o) and regs(o)[0] == "v" and regs(o)[1] in expr]
+            for k in range(d[1], d[2] + 1):
+                if srcs and k == d[1]:
+                    expr[k] = "cvt:" + max(srcs, key=len)
+                else:
+                    expr.pop(k, None)
+    return last, sorted(p for _, p in loads.values())
+
+
+def leaf_chain(n, fused=True):
+    """The leaf fold of n elements e0.. in index order with no seed, from
+    the definition: (sum, sum of squares) as canonical expression strings."""
+    sm = "e0"
+    sq = "(e0*e0)"
+    for i in range(1, n):
+        sm = canon_add(sm, f"e{i}")
+        sq = f"fma(e{i},e{i},{sq})" if fused else canon_add(sq, f"(e{i}*e{i})")
+    return sm, sq
+
+
+def wave_tree(x):
+    """The count-up wave tree over one value per lane, from the definition:
+    DPP row shifts 1, 2, 4, 8 (each lane at the end of a run of 2d lanes adds
+    the run's left half), then the four row roots as (r0 + r1) + (r2 + r3)."""
+    t = x
+    for d in (1, 2, 4, 8):
+        t = f"S{d}({t})"
+    return canon_add(canon_add(f"L15[{t}]", f"L31[{t}]"), canon_add(f"L47[{t}]", f"L63[{t}]"))
+
+
+def _src(expr, o):
+    r = regs(o)
+    if r is not None and r[0] == "v":
+        return expr.get(("v", r[1]))
+    m = re.match(r"s(\d+)$", o)
+    if m:
+        return expr.get(("s", int(m.group(1))))
+    return None
+
+
+def row_tree_signature(lines, bf16):
+    """The row reduction's tree for one row block, read from the kernel's
+    whole-leaf path: the straight-line code from the first vector load of
+    the leaf through the readlanes that finish the wave tree.  Loaded dwords
+    are numbered from the leaf's start (offset / 4), a bf16 pair unpacked by
+    the shift and the mask becomes elements 2n and 2n + 1, and adds, fused
+    multiply-adds, multiplies, DPP-shifted adds with their lane selects and
+    readlanes build expressions.  Returns the expressions of the two wave
+    roots (sum, sum of squares), or None."""
+    ins = instructions(lines)
+    k0 = next((k for k, (i, op, ops) in enumerate(ins) if op == "global_load_dwordx4"), None)
+    if k0 is None:
+        return None
+    expr = {}
+    roots = []
+    for i, op, ops in ins[k0:]:
+        if op == "global_load_dwordx4":
+            d = regs(ops[0])
+            m = re.search(r"offset:(\d+)", " ".join(ops))
+            base = (int(m.group(1)) if m else 0) // 4
+            for j in range(4):
+                expr[("v", d[1] + j)] = ("w", base + j)
+            continue
+        if op.startswith(("s_waitcnt", "s_nop", "v_cmp", "s_cmp")) or op.startswith("s_and_b64"):
+            continue
+        if op.startswith(("s_barrier", "ds_write", "ds_store", "s_cbranch", "s_branch", "global_store")):
+            break
+        d = regs(ops[0]) if ops else None
+        if op == "v_lshlrev_b32_e32" and ops[1] == "16":
+            w = _src(expr, ops[2])
+            val = f"e{2 * w[1]}" if isinstance(w, tuple) and bf16 else None
+        elif op == "v_and_b32_e32" and ops[1].lower() == "0xffff0000":
+            w = _src(expr, ops[2])
+            val = f"e{2 * w[1] + 1}" if isinstance(w, tuple) and bf16 else None
+        elif op.startswith("v_add_f32_dpp"):
+            sh = re.search(r"row_shr:(\d+)", ",".join(ops))
+            a = _src(expr, ops[1])
+            val = ("dpp", int(sh.group(1)) if sh else 0, a)
+        elif op.startswith("v_cndmask_b32"):
+            x, y = _src(expr, ops[1]), _src(expr, ops[2])
+            val = None
+            for new, old in ((x, y), (y, x)):
+                if isinstance(new, tuple) and new[0] == "dpp" and new[2] == old:
+                    val = f"S{new[1]}({old})"
+        elif op == "v_readlane_b32":
+            m = re.match(r"s(\d+)$", ops[0])
+            v = _src(expr, ops[1])
+            if m:
+                expr[("s", int(m.group(1)))] = f"L{ops[2]}[{v}]" if isinstance(v, str) else None
+            continue
+        elif op.startswith(("v_mov_b32", "v_mov_b32_e32")):
+            val = _src(expr, ops[1])
+        elif op.startswith("v_add_f32") or op.startswith("v_mul_f32") or op.startswith("v_fmac_f32"):
+            a, b = _src(expr, ops[1]), _src(expr, ops[2])
+            if not bf16:
+                a = f"e{a[1]}" if isinstance(a, tuple) and a[0] == "w" else a
+                b = f"e{b[1]}" if isinstance(b, tuple) and b[0] == "w" else b
+            if not (isinstance(a, str) and isinstance(b, str)):
+                val = None
+            elif op.startswith("v_add_f32"):
+                val = canon_add(a, b)
+            elif op.startswith("v_mul_f32"):
+                val = f"({a}*{b})"
+            else:
+                acc = _src(expr, ops[0])
+                acc = f"e{acc[1]}" if isinstance(acc, tuple) and acc[0] == "w" and not bf16 else acc
+                val = f"fma({a},{b},{acc})" if isinstance(acc, str) else None
+        else:
+            val = None
+        if d is not None and d[0] == "v":
+            for k in range(d[1], d[2] + 1):
+                expr[("v", k)] = val if k == d[1] else None
+    for v in expr.values():
+        if isinstance(v, str) and v.startswith("((L") and v.count("L") == 4:
+            roots.append(v)
+    return sorted(set(roots)) or None
