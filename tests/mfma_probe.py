@@ -18,9 +18,16 @@ Test infrastructure: it drives the GPU library and the oracle side by side.
 The captured bytes are measurements used to choose the descriptor; they are
 never stored as expected values for a parity test.
 
+  compact  (CPU)  keep only the captured cases that decide the fit (for each
+                  other member of the grid, one case it gets wrong), as a
+                  small JSON fixture of measured output bits; the inputs are
+                  regenerated from their seeds, so the fit can be re-run from
+                  the repository alone (tests/test_oracle_mfma_model.py).
+
 Usage:
   python tests/mfma_probe.py collect OUT.npz     (on the GPU)
   python tests/mfma_probe.py fit OUT.npz [--write]
+  python tests/mfma_probe.py compact OUT.npz [--out tests/golden/mfma_probe_decisive_cases.json]
 """
 import argparse
 import itertools
@@ -336,18 +343,118 @@ def fit(npz_path, instr, sample=512, verbose=True):
     return {"layout_ok": layout_ok, "fits": full, "n_cases": n_cases, "best": scores[:8]}
 
 
+def compact(npz_path, out_path, per_model_sample=4096, seed=7):
+    """Reduce a full capture to the cases that decide the fit: for every
+    member of the model grid except the one that fits, one captured case it
+    gets wrong (searched first in a seeded sample of every category, then in
+    all cases), plus the small-integer placement cases.  The inputs are not
+    stored -- make_cases(instr, 0) regenerates them from their seeds -- only
+    each chosen case's category, flat index and measured output bits.
+    Returns the fixture dict (also written to out_path as JSON)."""
+    import oracle
+    data = np.load(npz_path)
+    fixture = {"note": "black-box MFMA probe: measured outputs of the cases that single out the "
+                       "fitted model; inputs are make_cases(instr, seed) of tests/mfma_probe.py",
+               "seed": 0, "instructions": {}}
+    rng = np.random.default_rng(seed)
+    for instr in SHAPES:
+        R, K = SHAPES[instr]
+        cats = make_cases(instr, 0)
+        cases = {}
+        for c, (A, B, Cm) in cats.items():
+            acc, a, b = expand(A, B, Cm)
+            D = data[f"{instr}/{c}/D"].reshape(-1)
+            assert np.array_equal(data[f"{instr}/{c}/A"], A), "capture made from other inputs"
+            cases[c] = (acc, a, b, D)
+        res = fit(npz_path, instr, verbose=False)
+        assert res["layout_ok"] and len(res["fits"]) == 1, (instr, len(res["fits"]))
+        winner = {k: v for k, v in res["fits"][0].items() if k != "slot_order_name"}
+        chosen = {("layout_int", i) for i in range(len(cases["layout_int"][0]))}
+        samp = {c: rng.choice(len(v[0]), size=min(per_model_sample, len(v[0])), replace=False)
+                for c, v in cases.items()}
+        n_models = 0
+        for model in model_grid(K):
+            m = {k: v for k, v in model.items() if k != "slot_order_name"}
+            if m == winner:
+                continue
+            n_models += 1
+            # a case already chosen may rule this member out
+            hit = None
+            for (c, i) in sorted(chosen):
+                acc, a, b, d = cases[c]
+                if mismatches(oracle.mfma_bf16_batch(m, acc[i:i + 1], a[i:i + 1], b[i:i + 1]), d[i:i + 1]):
+                    hit = (c, i)
+                    break
+            if hit:
+                continue
+            for pool in ("sample", "all"):
+                for c, (acc, a, b, d) in cases.items():
+                    idx = samp[c] if pool == "sample" else np.arange(len(acc))
+                    got = oracle.mfma_bf16_batch(m, acc[idx], a[idx], b[idx])
+                    bad = (got.view(np.uint32) != d[idx].view(np.uint32)) & ~(np.isnan(got) & np.isnan(d[idx]))
+                    if bad.any():
+                        hit = (c, int(idx[int(np.argmax(bad))]))
+                        break
+                if hit:
+                    break
+            assert hit, f"{instr}: {model} matches every captured case"
+            chosen.add(hit)
+        entries = [[c, i, f"{int(cases[c][3][i:i + 1].view(np.uint32)[0]):08x}"] for c, i in sorted(chosen)]
+        # keep every 64th placement case (they were all taken in to rule
+        # members out cheaply) if the whole grid still leaves one member
+        lay = [e for e in entries if e[0] == "layout_int"]
+        thin = lay[::64] + [e for e in entries if e[0] != "layout_int"]
+        trial = {"seed": 0, "instructions": {instr: {"cases": thin}}}
+        if refit_fixture(trial)[instr] == [winner]:
+            entries = thin
+        fixture["instructions"][instr] = {"model": winner, "grid_members_ruled_out": n_models,
+                                          "cases": entries}
+        print(f"{instr}: {len(entries)} cases rule out all {n_models} other members", flush=True)
+    with open(out_path, "w") as f:
+        json.dump(fixture, f, indent=1)
+        f.write("\n")
+    return fixture
+
+
+def refit_fixture(fixture):
+    """Re-run the fit on a compact fixture: every member of the model grid on
+    the stored cases (inputs regenerated from their seeds).  Returns {instr:
+    [members with zero mismatches]}."""
+    import oracle
+    out = {}
+    for instr, spec in fixture["instructions"].items():
+        R, K = SHAPES[instr]
+        cats = make_cases(instr, fixture["seed"])
+        expanded = {c: expand(*v) for c, v in cats.items()}
+        acc = np.array([expanded[c][0][i] for c, i, _ in spec["cases"]], dtype=np.float32)
+        a = np.array([expanded[c][1][i] for c, i, _ in spec["cases"]], dtype=np.uint16)
+        b = np.array([expanded[c][2][i] for c, i, _ in spec["cases"]], dtype=np.uint16)
+        d = np.array([int(h, 16) for _, _, h in spec["cases"]], dtype=np.uint32).view(np.float32)
+        fits = []
+        for model in model_grid(K):
+            m = {k: v for k, v in model.items() if k != "slot_order_name"}
+            if mismatches(oracle.mfma_bf16_batch(m, acc, a, b), d) == 0:
+                fits.append(m)
+        out[instr] = fits
+    return out
+
+
 def _short(m):
     return " ".join(f"{k}={v}" for k, v in m.items() if k != "slot_order")
 
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("cmd", choices=["collect", "fit"])
+    ap.add_argument("cmd", choices=["collect", "fit", "compact"])
     ap.add_argument("npz")
     ap.add_argument("--write", action="store_true")
+    ap.add_argument("--out", default=os.path.join(ROOT, "tests", "golden", "mfma_probe_decisive_cases.json"))
     args = ap.parse_args()
     if args.cmd == "collect":
         collect(args.npz)
+        return
+    if args.cmd == "compact":
+        compact(args.npz, args.out)
         return
     results = {}
     for instr in SHAPES:

@@ -93,3 +93,41 @@ def test_int8_instructions_are_exact(instr, R, K):
     torch.cuda.synchronize()
     exact = Cm.astype(np.int64) + np.einsum("wmk,wnk->wmn", A.astype(np.int64), B.astype(np.int64))
     assert np.array_equal(dD.cpu().numpy().astype(np.int64), exact)
+
+
+@pytest.mark.parametrize("instr", list(SHAPES))
+def test_zero_products_leave_tiny_accumulators_alone(instr):
+    """The short last turn of a walk, and the extra k-steps of the 64-deep
+    register and direct-load kernels' last turn, issue instructions whose
+    every product is +0 or -0.  Fresh draws of such instructions against
+    accumulators at the bottom of the fp32 range -- subnormals of every
+    size, near-underflow normals, signed zeros -- must match the profile
+    (which returns the accumulator unchanged) bit for bit."""
+    import oracle
+    model = measured_model(instr)
+    R, K = SHAPES[instr]
+    rng = np.random.default_rng(9100 + K)
+    W = 512
+    # products of +-0 with anything finite, and of anything with +-0
+    A = np.where(rng.random((W, R, K)) < 0.5, 0x8000, 0x0000).astype(np.uint16)
+    B = synth.bf16_spread(9101 + K, (W, R, K), -60, 60)
+    half = W // 2
+    A[half:], B[half:] = B[half:].copy(), np.where(rng.random((W - half, R, K)) < 0.5, 0x8000, 0x0000).astype(np.uint16)
+    sub = (rng.integers(1, 1 << 23, size=(W, R, R)).astype(np.uint32)
+           | (rng.integers(0, 2, size=(W, R, R)).astype(np.uint32) << 31))
+    near = synth.f32_spread(9102 + K, (W, R, R), -126, -110)
+    zeros = np.where(rng.random((W, R, R)) < 0.5, -0.0, 0.0).astype(np.float32)
+    pick = rng.integers(0, 3, size=(W, R, R))
+    Cm = np.where(pick == 0, sub.view(np.float32), np.where(pick == 1, near, zeros)).astype(np.float32)
+    print_case("probe_zero_products", instr, A.shape)
+    D = _run_probe(instr, A, B, Cm)
+    acc = Cm.reshape(-1)
+    a = np.repeat(A[:, :, None, :], R, axis=2).reshape(-1, K)
+    b = np.repeat(B[:, None, :, :], R, axis=1).reshape(-1, K)
+    ref = oracle.mfma_bf16_batch(model, acc, a, b)
+    assert np.array_equal(ref.view(np.uint32), D.reshape(-1).view(np.uint32))
+    # and the profile's reading: the accumulator passes through unchanged,
+    # except that -0 plus a +0 product is +0 (IEEE round-to-nearest)
+    moved = D.reshape(-1).view(np.uint32) != acc.view(np.uint32)
+    assert np.all(acc[moved] == 0)
+
