@@ -168,12 +168,16 @@ def host_cost(head, torch, bg, n=100, reps=5):
                     f"{reps} batches; the plan is derived on every call, no cache"}
 
 
-def time_steps(fn, steps, warmup, torch):
-    """Warm up, then time exactly `steps` calls between synchronisations with
-    HIP events recorded on the stream the kernels are launched on."""
+def time_steps(fn, steps, warmup, torch, settle_ms=100.0):
+    """Warm up (`warmup` calls, then the same call for `settle_ms` of wall
+    time: after host-side work the clock takes tens of milliseconds to come
+    back), then time exactly `steps` calls between synchronisations with HIP
+    events recorded on the stream the kernels are launched on."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if settle_ms:
+        settle(fn, torch, settle_ms)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -626,7 +630,6 @@ def gemm_reduce_extras(X, W, args, torch, bg, ms_plain):
     N = W.shape[0]
     g = Gemm("gemm_bf16 M=4000 (fused reductions)", X, W, {"mfma": "F32_32X32X16_BF16", "out_type": "bf16"},
              torch, bg)
-    t_plain = ms_plain  # the headline's own timed launches: the same kernel on the same rotated inputs
     dF = torch.empty((M, N), dtype=torch.float32, device="cuda")
     d32 = bg.gemm_desc({"mfma": "F32_32X32X16_BF16"}, out_type="fp32")
     spec = dict(g.spec, out_type="fp32", mfma_model=bg.load_profile()["models"]["F32_32X32X16_BF16"])
@@ -657,7 +660,6 @@ def gemm_reduce_extras(X, W, args, torch, bg, ms_plain):
         bad = int(np.sum(s.cpu().numpy()[idx].view(np.uint32) != rs.view(np.uint32)))
         if q is not None:
             bad += int(np.sum(q.cpu().numpy()[idx].view(np.uint32) != rq.view(np.uint32)))
-        t_f, _ = time_steps(fused, args.steps, args.warmup, torch)
         rdu = bg.reduce_desc({"in_type": "fp32", "axis": axis, "op": op})
         nwu = bg.reduce_workspace_bytes(rdu, M, N)
         wsu = torch.empty(max(nwu, 16), dtype=torch.uint8, device="cuda")
@@ -667,12 +669,16 @@ def gemm_reduce_extras(X, W, args, torch, bg, ms_plain):
             bg.gemm_bf16(d32, A, B, dF, None)
             bg.reduce_tree(rdu, dF, s, q, wsu)
 
-        t_u, _ = time_steps(unfused, args.steps, args.warmup, torch)
+        # fused, unfused and the plain GEMM timed in interleaved rounds after
+        # the host-side oracle work above (medians over rounds)
+        settle(fused, torch, 200.0)
+        il = interleaved_ms({"fused": fused, "unfused": unfused, "plain": g.run_rot}, max(10, args.steps), torch)
+        t_f, t_u, t_plain = il["fused"], il["unfused"], il["plain"]
         out[f"gemm_reduce_{axis}_{op}"] = {
             "us": round(t_f * 1e3, 2), "plain_gemm_us": round(t_plain * 1e3, 2),
             "unfused_us": round(t_u * 1e3, 2), "fused_over_plain_time": round(t_f / t_plain, 4),
             "fused_over_unfused_time": round(t_f / t_u, 4), "TFLOP/s": round(g.flops() / t_f / 1e9, 2),
-            "inputs": g.rot.note(),
+            "inputs": g.rot.note(), "timing": "fused, unfused and plain interleaved over 5 rounds (medians)",
             "parity": {"sampled_outputs": int(len(idx)), "mismatches": bad}}
         log(f"bench: GEMM + {axis} {op}: fused {t_f * 1e3:.1f} us, plain GEMM {t_plain * 1e3:.1f} us, "
             f"unfused {t_u * 1e3:.1f} us")

@@ -262,7 +262,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
     tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    const int split = blockIdx.y;
+    // the last split (which takes the remainder, so it is the deepest) is
+    // dispatched first: longest work first balances the CUs (a schedule
+    // choice; each split's chain and the combine are unchanged)
+    const int split = (int)gridDim.y - 1 - (int)blockIdx.y;
     const int64_t k_begin = cuts.c[split];
     const int64_t k_end = cuts.c[split + 1];
     const int n_full = (int)((k_end - k_begin) / BK);
@@ -442,7 +445,10 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
     tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    const int split = blockIdx.y;
+    // the last split (which takes the remainder, so it is the deepest) is
+    // dispatched first: longest work first balances the CUs (a schedule
+    // choice; each split's chain and the combine are unchanged)
+    const int split = (int)gridDim.y - 1 - (int)blockIdx.y;
     const int64_t k_begin = cuts.c[split];
     const int64_t k_end = cuts.c[split + 1];
     const int n_full = (int)((k_end - k_begin) / BK);
