@@ -34,7 +34,9 @@ STATUS = {0: "BG_OK", 1: "BG_E_INVALID", 2: "BG_E_UNSUPPORTED", 3: "BG_E_WORKSPA
 class GemmSchedule(C.Structure):
     _fields_ = [("bm", C.c_int32), ("bn", C.c_int32), ("bk", C.c_int32),
                 ("waves_m", C.c_int32), ("waves_n", C.c_int32), ("load_path", C.c_int32),
-                ("group_m", C.c_int32), ("stages", C.c_int32)]
+                ("group_m", C.c_int32), ("stages", C.c_int32), ("last_bm", C.c_int32),
+                ("last_bn", C.c_int32), ("last_waves_m", C.c_int32), ("last_waves_n", C.c_int32),
+                ("last_stages", C.c_int32)]
 
 
 class GemmDesc(C.Structure):
@@ -85,6 +87,7 @@ _SYMBOLS = {
     "bg_gemm_bf16": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p, C.c_size_t,
                                C.c_void_p]),
+    "bg_gemm_bf16_plan": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p]),
     "bg_gemm_bf16_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p]),
     "bg_gemm_w8a8_pow2": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
@@ -178,7 +181,9 @@ def gemm_desc(spec=None, **overrides):
     """Build a GemmDesc from a descriptor dict (the JSON format the tests and
     the oracle share): mfma, split_k, cut_rule, cuts, cut_unit, combine,
     out_type, epilogue, a_type/b_type/acc_type, and an optional 'schedule'
-    dict (bm, bn, bk, waves_m, waves_n).  Unset fields keep the library
+    dict (bm, bn, bk, waves_m, waves_n, load_path, group_m, stages and the
+    last split's last_bm, last_bn, last_waves_m, last_waves_n, last_stages).
+    Unset fields keep the library
     defaults; the profile hash is the library's."""
     spec = dict(spec or {}, **overrides)
     d = GemmDesc()
@@ -291,6 +296,14 @@ def gemm_bf16(desc, A, B, C_out, ws=None, stream=None):
     _check(lib().bg_gemm_bf16(C.byref(desc), M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0),
                               _ptr(C_out), C_out.stride(0), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gemm_bf16_plan(desc, M, N, K):
+    """The tiles bg_gemm_bf16 would launch for desc at M x N x K, as a
+    schedule dict (host only)."""
+    s = GemmSchedule()
+    _check(lib().bg_gemm_bf16_plan(C.byref(desc), M, N, K, C.byref(s)))
+    return {f: int(getattr(s, f)) for f, _ in GemmSchedule._fields_}
 
 
 def gemm_bf16_noalloc(desc, A, B, C_out, stream=None):

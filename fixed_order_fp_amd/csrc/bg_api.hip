@@ -176,6 +176,143 @@ void choose_w8a8_pipe(bg::W8A8Plan& p, int64_t M, int64_t N)
     }
 }
 
+// ---- tiles for split-K ---------------------------------------------------
+// Time of one pipelined workgroup over `turns` k tiles of 32, in us: a
+// per-turn cost measured on MI355X for each tile (the deep split of a
+// 256 x 2560 x 9728 product, one workgroup per CU, at the clock these kernels
+// settle at; the 8-wave 256 x 256 tile measured ahead of the 4-wave one once
+// every CU is busy), plus 0.5 us, one turn per stage for the pipeline fill,
+// and the fp32 partial tile's store at 30 GB/s per CU.  Workgroups that share
+// a CU (as many as its LDS holds, while there are more workgroups than CUs)
+// each run that much slower.  The constants were fitted to the split sweep of
+// that product (S = 2 .. 16, the tiles and pairs below); the model ranks
+// tiles, it does not predict times.
+struct PipeTileCost {
+    int bm, bn, wm, wn, ns;
+    double turn_us;
+};
+const PipeTileCost kPipeCosts[] = {
+    {256, 256, 2, 4, 4, 0.858}, {256, 256, 2, 2, 4, 0.900}, {192, 256, 2, 4, 4, 0.613}, {256, 128, 2, 2, 4, 0.510},
+    {192, 128, 2, 2, 4, 0.407}, {128, 128, 2, 2, 4, 0.333}, {128, 128, 2, 2, 8, 0.327}, {128, 64, 2, 2, 4, 0.293},
+    {128, 64, 2, 2, 8, 0.259},  {64, 128, 2, 2, 4, 0.293},  {64, 128, 2, 2, 8, 0.267},  {64, 64, 2, 2, 8, 0.189},
+    {128, 64, 4, 2, 8, 0.259},  {64, 128, 2, 4, 8, 0.267}};
+
+const PipeTileCost* pipe_cost(int bm, int bn, int wm, int wn, int ns)
+{
+    for (const PipeTileCost& c : kPipeCosts)
+        if (c.bm == bm && c.bn == bn && c.wm == wm && c.wn == wn && c.ns == ns) return &c;
+    return nullptr;
+}
+
+double wg_us(const PipeTileCost& c, int64_t turns)
+{
+    return 0.5 + (double)(turns + c.ns) * c.turn_us + (double)c.bm * c.bn * 4.0 / 30e3;
+}
+
+int pipe_lds_bytes(const PipeTileCost& c) { return c.ns * (c.bm + c.bn) * 64; }
+
+// Longest-first list schedule of two kinds of workgroups on n_cu slots, one
+// at a time per slot: the longer kind is dealt out first (some slots take
+// one more of them), then each shorter workgroup goes to the slot that frees
+// up first.  Returns the time the last slot finishes.
+double lpt_slots(int64_t na, double ta, int64_t nb, double tb, int64_t n_cu)
+{
+    if (tb > ta) std::swap(na, nb), std::swap(ta, tb);
+    const int64_t q = na / n_cu, r = na % n_cu;
+    const double lo = (double)q * ta, hi = (double)(q + (r ? 1 : 0)) * ta;
+    if (nb <= 0) return hi;
+    if (tb <= 0.0) return hi;
+    // the earliest time T by which the CUs at `lo` (n_cu - r of them) and at
+    // `hi` (r) have room for nb shorter workgroups
+    auto fits = [&](double T) {
+        const int64_t a = T >= lo ? (int64_t)((T - lo) / tb + 1e-9) : 0;
+        const int64_t b = T >= hi ? (int64_t)((T - hi) / tb + 1e-9) : 0;
+        return (n_cu - r) * a + r * b >= nb;
+    };
+    // fits() grows with T, and a CU's load changes only at lo + k tb or
+    // hi + k tb: the answer is the first of either family that fits
+    auto first_k = [&](double base) {  // smallest k >= 1 with fits(base + k tb), by bisection
+        int64_t a = 1, b = nb + 1;         // fits(base + (nb + 1) tb) always holds
+        while (a < b) {
+            const int64_t m = a + (b - a) / 2;
+            if (fits(base + (double)m * tb)) b = m;
+            else a = m + 1;
+        }
+        return a;
+    };
+    return std::min(std::max(lo + (double)first_k(lo) * tb, hi), hi + (double)first_k(hi) * tb);
+}
+
+// lpt_slots with `lds` bytes per workgroup: a CU holds 160 KiB / lds of
+// them, and while there are more workgroups than CUs it runs up to that many
+// at once, each proportionally slower
+double lpt2(int64_t na, double ta, int64_t nb, double tb, int64_t n_cu, int lds)
+{
+    const double per_cu = std::max(1, (160 * 1024) / std::max(lds, 1));
+    const double share = std::min(per_cu, std::max(1.0, (double)(na + nb) / (double)n_cu));
+    return lpt_slots(na, ta * share, nb, tb * share, (int64_t)((double)n_cu * share));
+}
+
+struct DualPair {
+    int bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2;
+};
+// must list exactly the pairs bg_gemm_bf16.hip compiles in
+const DualPair kDualPairs[] = {{256, 256, 2, 2, 4, 64, 64, 2, 2, 8},  {256, 256, 2, 2, 4, 128, 64, 2, 2, 4},
+                               {256, 128, 2, 2, 4, 64, 64, 2, 2, 8},  {192, 128, 2, 2, 4, 64, 64, 2, 2, 8},
+                               {128, 128, 2, 2, 4, 64, 64, 2, 2, 8},  {256, 256, 2, 4, 4, 128, 64, 4, 2, 8},
+                               {256, 256, 2, 4, 4, 64, 128, 2, 4, 8}};
+
+// The split grid's tiles (S > 1): every single tile of the cost table and
+// every compiled (other splits, last split) pair is scored by lpt2 over the
+// splits' depths; the cheapest wins, a single tile on a tie.
+void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
+{
+    const int64_t n_cu = 256;
+    int64_t body = 0;
+    for (int s = 0; s + 1 < p.S; s++) body = std::max<int64_t>(body, p.cuts.c[s + 1] - p.cuts.c[s]);
+    const int64_t last = p.cuts.c[p.S] - p.cuts.c[p.S - 1];
+    const int64_t tb = (body + 31) / 32, tl = (last + 31) / 32;
+    auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
+    double best = 0.0;
+    bool have = false;
+    for (const PipeTileCost& c : kPipeCosts) {
+        if (c.bm > 64 && M <= 64) continue;
+        const int64_t n = tiles(c.bm, c.bn);
+        const double t = lpt2(n * (p.S - 1), wg_us(c, tb), n, wg_us(c, tl), n_cu, pipe_lds_bytes(c));
+        if (!have || t < best) {
+            have = true, best = t;
+            p.bm = c.bm, p.bn = c.bn, p.bk = 32, p.waves_m = c.wm, p.waves_n = c.wn, p.direct = 2, p.stages = c.ns;
+            p.bm2 = 0, p.bn2 = 0, p.waves_m2 = 0, p.waves_n2 = 0, p.stages2 = 0;
+        }
+    }
+    for (const DualPair& d : kDualPairs) {
+        const PipeTileCost* a = pipe_cost(d.bm, d.bn, d.wm, d.wn, d.ns);
+        const PipeTileCost* b = pipe_cost(d.bm2, d.bn2, d.wm2, d.wn2, d.ns2);
+        if (!a || !b) continue;
+        const double ta = wg_us(*a, tb), tl2 = wg_us(*b, tl);
+        const double t = lpt2(tiles(d.bm, d.bn) * (p.S - 1), ta, tiles(d.bm2, d.bn2), tl2, n_cu,
+                              std::max(pipe_lds_bytes(*a), pipe_lds_bytes(*b)));
+        if (t < best) {
+            best = t;
+            p.bm = d.bm, p.bn = d.bn, p.bk = 32, p.waves_m = d.wm, p.waves_n = d.wn, p.direct = 2, p.stages = d.ns;
+            p.bm2 = d.bm2, p.bn2 = d.bn2, p.waves_m2 = d.wm2, p.waves_n2 = d.wn2, p.stages2 = d.ns2;
+            p.last_first = tl2 >= ta;
+        }
+    }
+}
+
+// whether the last split's workgroups go first (the longer kind first)
+bool dual_last_first(const bg::GemmPlan& p)
+{
+    const PipeTileCost* a = pipe_cost(p.bm, p.bn, p.waves_m, p.waves_n, p.stages);
+    const PipeTileCost* b = pipe_cost(p.bm2, p.bn2, p.waves_m2, p.waves_n2, p.stages2);
+    if (!a || !b) return true;
+    int64_t body = 0;
+    for (int s = 0; s + 1 < p.S; s++) body = std::max<int64_t>(body, p.cuts.c[s + 1] - p.cuts.c[s]);
+    const int64_t last = p.cuts.c[p.S] - p.cuts.c[p.S - 1];
+    return wg_us(*b, (last + 31) / 32) >= wg_us(*a, (body + 31) / 32);
+}
+
 void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
 {
     auto set = [&](int bm, int bn, int bk, int wm, int wn, int direct, int stages) {
@@ -206,6 +343,17 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
     if (M <= 64) {
         set(64, 64, 32, 2, 2, 2, 8);
         return;
+    }
+    if (p.S > 1) {
+        // a remainder split at least twice as deep as the others: score the
+        // pairs of tiles too (the longest-first model below); otherwise the
+        // splits are about even and the copy-time model below picks one tile
+        int64_t body = 0;
+        for (int s = 0; s + 1 < p.S; s++) body = std::max<int64_t>(body, p.cuts.c[s + 1] - p.cuts.c[s]);
+        if (p.cuts.c[p.S] - p.cuts.c[p.S - 1] >= 2 * body) {
+            choose_split_tiles(p, M, N);
+            return;
+        }
     }
     // deep splits: the tile whose busiest CU finishes first.  Each CU moves
     // operands at ~38 GB/s and multiplies at ~8.1 TFLOP/s (both measured on
@@ -441,9 +589,13 @@ bg_status bg_gemm_workspace_bytes(const bg_gemm_desc* d, int64_t M, int64_t N, i
     return BG_OK;
 }
 
-bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                       const void* B, int64_t ldb, void* C, int64_t ldc, void* ws, size_t ws_bytes,
-                       hipStream_t stream)
+}  // extern "C"
+
+namespace {
+// bg_gemm_bf16's descriptor and size checks and its cut points (plan p: S
+// and cuts set); nothing here reads memory or the device
+bg_status check_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                          int64_t ldc, bg::GemmPlan& p)
 {
     bg_status st = check_common_order(d);
     if (st != BG_OK) return st;
@@ -460,13 +612,84 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
     if (d->epilogue != BG_EPI_NONE) return fail(BG_E_INVALID, "bg_gemm_bf16 has no epilogue");
     if (M < 0 || N < 0) return fail(BG_E_INVALID, "negative size");
     if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
-
-    bg::GemmPlan p{};
+    p = bg::GemmPlan{};
     p.S = (int)d->split_k;
     st = make_cuts(d, K, p.cuts.c);
     if (st != BG_OK) return st;
     for (int s = 0; s <= p.S; s++)
         if (p.cuts.c[s] % 8) return fail(BG_E_UNSUPPORTED, "cut points must be multiples of 8");
+    p.mfma = (int)d->mfma;
+    p.out_bf16 = d->out_type == BG_BF16;
+    return BG_OK;
+}
+
+// the tiles of plan p (M, N > 0): the descriptor's schedule, or the
+// library's choice for the shape
+bg_status resolve_gemm_schedule(const bg_gemm_desc* d, int64_t M, int64_t N, bg::GemmPlan& p)
+{
+    const bg_gemm_schedule& s = d->sched;
+    p.group_m = s.group_m;
+    if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
+        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path, s.stages))
+            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path, stages) is not compiled in");
+        p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
+        p.direct = s.load_path;
+        p.stages = s.stages;
+        if (s.last_bm || s.last_bn || s.last_waves_m || s.last_waves_n || s.last_stages) {
+            if (p.S < 2) return fail(BG_E_UNSUPPORTED, "a last-split tile needs split_k > 1");
+            if (s.load_path != 2 || s.bk != 32 || p.mfma != BG_MFMA_F32_32X32X16_BF16 ||
+                !bg::gemm_bf16_has_dual_tile(s.bm, s.bn, s.waves_m, s.waves_n, s.stages, s.last_bm, s.last_bn,
+                                             s.last_waves_m, s.last_waves_n, s.last_stages))
+                return fail(BG_E_UNSUPPORTED, "the (tile, last-split tile) pair is not compiled in");
+            p.bm2 = s.last_bm, p.bn2 = s.last_bn, p.waves_m2 = s.last_waves_m, p.waves_n2 = s.last_waves_n;
+            p.stages2 = s.last_stages;
+            for (const DualPair& dp : kDualPairs)  // the pair's compiled stage counts where left 0
+                if (dp.bm == p.bm && dp.bn == p.bn && dp.wm == p.waves_m && dp.wn == p.waves_n &&
+                    (!p.stages || dp.ns == p.stages) && dp.bm2 == p.bm2 && dp.bn2 == p.bn2 && dp.wm2 == p.waves_m2 &&
+                    dp.wn2 == p.waves_n2 && (!p.stages2 || dp.ns2 == p.stages2)) {
+                    p.stages = dp.ns, p.stages2 = dp.ns2;
+                    break;
+                }
+            p.last_first = dual_last_first(p);
+        }
+    } else {
+        if (s.last_bm || s.last_bn || s.last_waves_m || s.last_waves_n || s.last_stages)
+            return fail(BG_E_UNSUPPORTED, "a last-split tile needs the other splits' tile (bm .. waves_n) set");
+        choose_gemm_tile(p, M, N);
+    }
+    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n) || (p.S > 1 && !grid_fits((M * N + 255) / 256, 256)))
+        return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
+    return BG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+bg_status bg_gemm_bf16_plan(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, bg_gemm_schedule* out)
+{
+    if (!d || !out) return fail(BG_E_INVALID, "NULL argument");
+    bg::GemmPlan p{};
+    bg_status st = check_gemm_bf16(d, M, N, K, K, K, N, p);
+    if (st != BG_OK) return st;
+    if (M == 0 || N == 0) return fail(BG_E_INVALID, "an empty product launches nothing");
+    st = resolve_gemm_schedule(d, M, N, p);
+    if (st != BG_OK) return st;
+    bg_gemm_schedule s{};
+    s.bm = p.bm, s.bn = p.bn, s.bk = p.bk, s.waves_m = p.waves_m, s.waves_n = p.waves_n, s.load_path = p.direct;
+    s.group_m = p.group_m, s.stages = p.stages;
+    s.last_bm = p.bm2, s.last_bn = p.bn2, s.last_waves_m = p.waves_m2, s.last_waves_n = p.waves_n2;
+    s.last_stages = p.stages2;
+    *out = s;
+    return BG_OK;
+}
+
+bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, void* C, int64_t ldc, void* ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    bg::GemmPlan p{};
+    bg_status st = check_gemm_bf16(d, M, N, K, lda, ldb, ldc, p);
+    if (st != BG_OK) return st;
     if (M == 0 || N == 0) return BG_OK;
     if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 8 || ldb % 8 || ldc % 8)
@@ -476,21 +699,8 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
         if (!ws || ws_bytes < need) return fail(BG_E_WORKSPACE, "split-K needs S*M*N*4 bytes of workspace");
         if (!aligned16(ws)) return fail(BG_E_ALIGN, "workspace must be 16-byte aligned");
     }
-    p.mfma = (int)d->mfma;
-    p.out_bf16 = d->out_type == BG_BF16;
-    const bg_gemm_schedule& s = d->sched;
-    p.group_m = s.group_m;
-    if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
-        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path, s.stages))
-            return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path, stages) is not compiled in");
-        p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
-        p.direct = s.load_path;
-        p.stages = s.stages;
-    } else {
-        choose_gemm_tile(p, M, N);
-    }
-    if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n) || (p.S > 1 && !grid_fits((M * N + 255) / 256, 256)))
-        return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
+    st = resolve_gemm_schedule(d, M, N, p);
+    if (st != BG_OK) return st;
     st = check_device();
     if (st != BG_OK) return st;
     hipError_t e = bg::launch_gemm_bf16(p, M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc,
@@ -900,7 +1110,8 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     p.S = S;
     for (int s = 0; s < S; s++) p.cuts.c[s] = s * span;
     p.cuts.c[S] = K;
-    if (S > 1) choose_gemm_tile(p, M, N);  // the tile for the split grid
+    p.atomic = S > 1;
+    if (S > 1) choose_gemm_tile(p, M, N);  // the tile (or pair of tiles) for the split grid
     if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
         return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     p.atomic = S > 1;

@@ -21,7 +21,8 @@
 //           ("CARRY_LAST"), rounding_point ("AFTER_COMBINE_RNE"), epilogue
 //           ("NONE" | "W8A8_POW2"), mfma_profile_hash ("0x" and 16 hex
 //           digits), schedule {bm, bn, bk, waves_m, waves_n, load_path,
-//           group_m, stages}
+//           group_m, stages, last_bm, last_bn, last_waves_m, last_waves_n,
+//           last_stages}
 //   reduce: version, in_type, acc_type, out_type, op ("sum" | "sumsq" |
 //           "sum_and_sumsq"), axis ("row" | "col"), leaf_len, leaf_order
 //           ("SEQUENTIAL_NO_SEED"), sq_fma ("fused" | "unfused"), tree
@@ -325,6 +326,11 @@ static bool gemm_from(Ctx& c, const Value& o, bg_gemm_desc& d)
                 else if (sk == "load_path") ok = c.i32(s.second, sk, g.load_path);
                 else if (sk == "group_m") ok = c.i32(s.second, sk, g.group_m);
                 else if (sk == "stages") ok = c.i32(s.second, sk, g.stages);
+                else if (sk == "last_bm") ok = c.i32(s.second, sk, g.last_bm);
+                else if (sk == "last_bn") ok = c.i32(s.second, sk, g.last_bn);
+                else if (sk == "last_waves_m") ok = c.i32(s.second, sk, g.last_waves_m);
+                else if (sk == "last_waves_n") ok = c.i32(s.second, sk, g.last_waves_n);
+                else if (sk == "last_stages") ok = c.i32(s.second, sk, g.last_stages);
                 else return c.fail("unknown gemm schedule key \"" + sk + "\"");
                 if (!ok) return false;
             }
@@ -482,6 +488,11 @@ bg_status bg_desc_to_json(const bg_gemm_desc* g, const bg_reduce_desc* r, char* 
         o.num("load_path", sc.load_path);
         o.num("group_m", sc.group_m);
         o.num("stages", sc.stages);
+        o.num("last_bm", sc.last_bm);
+        o.num("last_bn", sc.last_bn);
+        o.num("last_waves_m", sc.last_waves_m);
+        o.num("last_waves_n", sc.last_waves_n);
+        o.num("last_stages", sc.last_stages);
         o.trim();
         o.s += "}}";
         if (r) o.s += ", ";

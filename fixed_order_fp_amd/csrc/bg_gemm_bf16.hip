@@ -411,12 +411,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 // split partial added into C with atomics (the free-order twin only)
 // RED: 0 none, 1 and 2 fused reductions of the fp32 C tile (column and row
 // leaves; S = 1, OUT 0 or 1).
-template <int BM, int BN, int WM, int WN, int NS, int OUT, int RED = 0>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
-    PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU)))
-void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
-                           int64_t ldb, void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M,
-                           int64_t N, Cuts cuts, int tiles_m, int tiles_n, int group_m, RedArgs red)
+//
+// pipe_tile computes one output tile (walk index b) of one split into the
+// workgroup's LDS `lds`; the kernels below map workgroups to (b, split).
+template <int BM, int BN, int WM, int WN, int NS, int OUT, int RED>
+__device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int split,
+                                          const uint16_t* __restrict__ A, int64_t lda,
+                                          const uint16_t* __restrict__ B, int64_t ldb, void* __restrict__ C,
+                                          int64_t ldc, float* __restrict__ ws, int64_t M, int64_t N,
+                                          const Cuts& cuts, int tiles_m, int tiles_n, int group_m,
+                                          const RedArgs& red)
 {
     constexpr int BK = 32, CPR = BK / kChunk, KS = BK / 16;
     constexpr int NW = WM * WN, NT = 64 * NW;
@@ -435,20 +439,15 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
     static_assert(NS >= 3 && LOADS_HI * (NS - 2) < 64, "stages: three at least, waits within vmcnt");
     static_assert(KS == 2, "two k-steps per turn: the fragment buffers alternate within a turn");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
-    __shared__ u32x4 lds[LDS_BYTES / 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of(b, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    // the last split (which takes the remainder, so it is the deepest) is
-    // dispatched first: longest work first balances the CUs (a schedule
-    // choice; each split's chain and the combine are unchanged)
-    const int split = (int)gridDim.y - 1 - (int)blockIdx.y;
     const int64_t k_begin = cuts.c[split];
     const int64_t k_end = cuts.c[split + 1];
     const int n_full = (int)((k_end - k_begin) / BK);
@@ -703,10 +702,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
                     Cb[gm * ldc + gn + u] = (uint16_t)(v[u / 2] >> (16 * (u % 2)));
             }
         }
-    } else {
-        float* out = OUT == 2 ? ws + (int64_t)split * M * N : (float*)C;
-        const int64_t ld = OUT == 2 ? N : ldc;
-        const bool vec_ok = (ld % 4) == 0;
+    } else if constexpr (OUT == 3) {
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
@@ -716,16 +712,114 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
                     const int64_t gm = m0 + wm * WTM + i * 32 + r_in;
                     const int64_t gn = n0 + wn * WTN + j * 32 + 8 * q + 4 * h;
                     if (gm >= M || gn >= N) continue;
+                    float* p = (float*)C + gm * ldc + gn;
+                    for (int u = 0; u < 4 && gn + u < N; u++) unsafeAtomicAdd(p + u, acc[j][i][4 * q + u]);
+                }
+    } else {
+        // fp32 C or a split's partial plane: each wave stages one 32x32 block
+        // at a time in its own LDS slice (rows of 36 floats keep every row
+        // 16-byte aligned) and writes it back as 8 rows of 128 contiguous
+        // bytes per store instruction, instead of 32 rows of 32 bytes from the
+        // MFMA layout.  Only this wave reads its slice: the LDS keeps one
+        // wave's accesses in order, so no barrier is needed between blocks.
+        constexpr int PITCH = 36;
+        static_assert(NW * 32 * PITCH * 4 <= LDS_BYTES, "the store slices fit in LDS");
+        float* out = OUT == 2 ? ws + (int64_t)split * M * N : (float*)C;
+        const int64_t ld = OUT == 2 ? N : ldc;
+        const bool vec_ok = (ld % 4) == 0;
+        __syncthreads();  // every wave is done with the operand stages
+        float* st = (float*)lds + wave * (32 * PITCH);
+        const int rr = lane >> 3, cc = (lane & 7) * 4;  // this lane's row (of 8) and column in a store
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    f32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+                    *(f32x4*)(st + r_in * PITCH + 8 * q + 4 * h) = v;
+                }
+                const int64_t gn = n0 + wn * WTN + j * 32 + cc;
+#pragma unroll
+                for (int pass = 0; pass < 4; pass++) {
+                    const int row = 8 * pass + rr;
+                    const f32x4 v = *(const f32x4*)(st + row * PITCH + cc);
+                    const int64_t gm = m0 + wm * WTM + i * 32 + row;
+                    if (gm >= M || gn >= N) continue;
                     float* p = out + gm * ld + gn;
-                    if constexpr (OUT == 3) {
-                        for (int u = 0; u < 4 && gn + u < N; u++) unsafeAtomicAdd(p + u, acc[j][i][4 * q + u]);
-                    } else if (vec_ok && gn + 4 <= N) {
-                        f32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+                    if (vec_ok && gn + 4 <= N) {
                         *(f32x4*)p = v;
                     } else {
-                        for (int u = 0; u < 4 && gn + u < N; u++) p[u] = acc[j][i][4 * q + u];
+                        for (int u = 0; u < 4 && gn + u < N; u++) p[u] = v[u];
                     }
                 }
+            }
+    }
+}
+
+// One tile shape for every split: workgroup x walks the tiles, y the splits.
+// The last split (which takes the remainder, so it is the deepest) is
+// dispatched first: longest work first balances the CUs (a schedule choice;
+// each split's chain and the combine are unchanged).
+template <int BM, int BN, int WM, int WN, int NS, int OUT, int RED = 0>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
+    PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, OUT>::WAVES_PER_EU)))
+void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+                           int64_t ldb, void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M,
+                           int64_t N, Cuts cuts, int tiles_m, int tiles_n, int group_m, RedArgs red)
+{
+    __shared__ u32x4 lds[PipeLds<BM, BN, NS, OUT>::BYTES / 16];
+    pipe_tile<BM, BN, WM, WN, NS, OUT, RED>(lds, (int)blockIdx.x, (int)gridDim.y - 1 - (int)blockIdx.y, A, lda, B,
+                                            ldb, C, ldc, ws, M, N, cuts, tiles_m, tiles_n, group_m, red);
+}
+
+// Two tile shapes in one launch: the last split (the cut rule's remainder,
+// the deepest) takes tile BM2 x BN2, the other splits BM x BN.  A deep split
+// on the large tile would be the critical path (few workgroups, many k
+// tiles), on the small tile of every split the copies would grow with
+// 1/BM + 1/BN; both shapes share the launch so that the CUs stay busy
+// through both.  The workgroups of the last split come first when
+// `last_first` is set, else last.  Only the schedule differs: every split's
+// chain is the one its k range gives, and its partial plane is the same.
+template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2>
+struct DualLds {
+    static constexpr int A = PipeLds<BM, BN, NS, 2>::BYTES, B = PipeLds<BM2, BN2, NS2, 2>::BYTES;
+    static constexpr int BYTES = A > B ? A : B;
+    static constexpr int W0 = (160 * 1024) / BYTES * WM * WN / 4;
+    static constexpr int WAVES_PER_EU = W0 < 1 ? 1 : W0;
+};
+
+// OUT: 2 partial planes in the workspace, 3 partials added into C with
+// atomics (the free-order twin only).
+template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2, int OUT>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
+    DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::WAVES_PER_EU,
+    DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::WAVES_PER_EU)))
+void gemm_bf16_pipe_dual_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
+                                int64_t ldb, void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M,
+                                int64_t N, Cuts cuts, int S, int tiles_m, int tiles_n, int group_m, int tiles_m2,
+                                int tiles_n2, int group_m2, int last_first)
+{
+    static_assert(OUT == 2 || OUT == 3, "split partials only");
+    static_assert(WM * WN == WM2 * WN2, "both shapes run with the workgroup's waves");
+    __shared__ u32x4 lds[DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::BYTES / 16];
+    const int n_last = tiles_m2 * tiles_n2, n_body = tiles_m * tiles_n * (S - 1);
+    int b = (int)blockIdx.x;
+    bool is_last;
+    if (last_first) {
+        is_last = b < n_last;
+        if (!is_last) b -= n_last;
+    } else {
+        is_last = b >= n_body;
+        if (is_last) b -= n_body;
+    }
+    if (is_last) {
+        pipe_tile<BM2, BN2, WM2, WN2, NS2, OUT, 0>(lds, b, S - 1, A, lda, B, ldb, C, ldc, ws, M, N, cuts, tiles_m2,
+                                                   tiles_n2, group_m2, RedArgs{});
+    } else {
+        const int T = tiles_m * tiles_n;
+        pipe_tile<BM, BN, WM, WN, NS, OUT, 0>(lds, b % T, b / T, A, lda, B, ldb, C, ldc, ws, M, N, cuts, tiles_m,
+                                              tiles_n, group_m, RedArgs{});
     }
 }
 
@@ -980,6 +1074,52 @@ bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves
     return false;
 }
 
+// The (other splits, last split) tile pairs compiled in: BM, BN, waves_m,
+// waves_n, stages of each (pipelined path, 32x32x16).  The first entry of a
+// pair of shapes is its default stage count.
+#define BG_GEMM_DUAL_TILES(X)                    \
+    X(256, 256, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(256, 256, 2, 2, 4, 128, 64, 2, 2, 4)       \
+    X(256, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(192, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(128, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(256, 256, 2, 4, 4, 128, 64, 4, 2, 8)       \
+    X(256, 256, 2, 4, 4, 64, 128, 2, 4, 8)
+
+bool gemm_bf16_has_dual_tile(int bm, int bn, int waves_m, int waves_n, int stages, int bm2, int bn2, int waves_m2,
+                             int waves_n2, int stages2)
+{
+#define BG_DHAS(BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_)                                            \
+    if (bm == BM_ && bn == BN_ && waves_m == WM_ && waves_n == WN_ && (stages == 0 || stages == NS_) &&           \
+        bm2 == BM2_ && bn2 == BN2_ && waves_m2 == WM2_ && waves_n2 == WN2_ && (stages2 == 0 || stages2 == NS2_))   \
+        return true;
+    BG_GEMM_DUAL_TILES(BG_DHAS)
+#undef BG_DHAS
+    return false;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2>
+static hipError_t launch_dual(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
+{
+    constexpr int PER_CU = (160 * 1024) / DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::BYTES;
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int tiles_m2 = (int)((M + BM2 - 1) / BM2), tiles_n2 = (int)((N + BN2 - 1) / BN2);
+    const int group_m = p.group_m > 0 ? p.group_m : walk_group_m(tiles_m, tiles_n, BM, BN, PER_CU);
+    const int group_m2 = p.group_m > 0 ? p.group_m : walk_group_m(tiles_m2, tiles_n2, BM2, BN2, PER_CU);
+    const int64_t wgs = (int64_t)tiles_m * tiles_n * (p.S - 1) + (int64_t)tiles_m2 * tiles_n2;
+    if (p.S < 2 || wgs > 0x7fffffff) return hipErrorInvalidValue;
+    if (p.atomic)  // free-order twin only
+        hipLaunchKernelGGL((gemm_bf16_pipe_dual_kernel<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, 3>),
+                           dim3((unsigned)wgs), dim3(64 * WM * WN), 0, stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts,
+                           p.S, tiles_m, tiles_n, group_m, tiles_m2, tiles_n2, group_m2, p.last_first ? 1 : 0);
+    else
+        hipLaunchKernelGGL((gemm_bf16_pipe_dual_kernel<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, 2>),
+                           dim3((unsigned)wgs), dim3(64 * WM * WN), 0, stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts,
+                           p.S, tiles_m, tiles_n, group_m, tiles_m2, tiles_n2, group_m2, p.last_first ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, const uint16_t* A,
                             int64_t lda, const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws,
                             hipStream_t stream)
@@ -993,7 +1133,20 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, 
         found = true;                                                                                    \
         err = TileLauncher<D_>::template run<I, BM_, BN_, BK_, WM_, WN_, NS_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream); \
     }
-    BG_GEMM_TILES(BG_LAUNCH)
+    if (p.bm2) {
+#define BG_DLAUNCH(BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_)                                        \
+        if (!found && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_ &&                      \
+            (p.stages == 0 || p.stages == NS_) && p.bm2 == BM2_ && p.bn2 == BN2_ && p.waves_m2 == WM2_ &&          \
+            p.waves_n2 == WN2_ && (p.stages2 == 0 || p.stages2 == NS2_)) {                                       \
+            found = true;                                                                                          \
+            err = launch_dual<BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_>(p, M, N, A, lda, B, ldb, C, ldc, \
+                                                                                   ws, stream);                    \
+        }
+        BG_GEMM_DUAL_TILES(BG_DLAUNCH)
+#undef BG_DLAUNCH
+    } else {
+        BG_GEMM_TILES(BG_LAUNCH)
+    }
 #undef BG_LAUNCH
     if (!found || err != hipSuccess) return found ? err : hipErrorInvalidValue;
     if (p.S > 1 && !p.atomic) {

@@ -68,6 +68,9 @@ struct GemmPlan {
     int direct;      // 1: operand tiles copied global -> LDS directly; 2: pipelined
     int stages;      // k tiles in LDS (pipelined path)
     int group_m;     // tile rows per group of the workgroup walk
+    int bm2, bn2;    // the last split's tile (pipelined path, S > 1); 0 = none
+    int waves_m2, waves_n2, stages2;
+    bool last_first; // dispatch the last split's workgroups before the others
     bool atomic;     // free-order twin: splits added into a zeroed fp32 C with atomics
     int red;         // fused reduction of C: 0 none, 1 column leaves, 2 row leaves
     RedArgs red_args;
@@ -137,6 +140,10 @@ hipError_t launch_requantize_pow2(int64_t N, int64_t K, const int8_t* W, int64_t
 // which tile shapes the GEMM kernel is instantiated for
 hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream);
 bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct, int stages);
+// a compiled (other splits, last split) pair of pipelined tiles; stages == 0
+// takes the first compiled pair of the two shapes
+bool gemm_bf16_has_dual_tile(int bm, int bn, int waves_m, int waves_n, int stages, int bm2, int bn2, int waves_m2,
+                             int waves_n2, int stages2);
 // tiles built with the fused reductions (pipelined path, S = 1)
 bool gemm_bf16_red_has_tile(int bm, int bn, int waves_m, int waves_n, int stages);
 hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,

@@ -59,7 +59,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t; /* the HIP runtime's stream handle */
 
-#define BG_ABI_VERSION 1
+#define BG_ABI_VERSION 2
 #define BG_MAX_SPLIT 64
 
 typedef enum {
@@ -110,6 +110,15 @@ typedef struct {
                                  fewest A and B rows)                      */
     int32_t stages;           /* k tiles held in LDS by path 2 (0 = the
                                  tile's default)                           */
+    int32_t last_bm, last_bn; /* path 2 with split_k > 1: the last split
+                                 (the cut rule's remainder, the deepest)
+                                 takes this tile in the same launch; all
+                                 five last_* 0 = the same tile as the other
+                                 splits.  Needs bm..waves_n set; the pair
+                                 must be compiled in and have the same
+                                 number of waves                           */
+    int32_t last_waves_m, last_waves_n;
+    int32_t last_stages;
 } bg_gemm_schedule;
 
 /* GEMM descriptor ([T] 3.2.2 and 4).  Every field before `sched` is an order
@@ -231,6 +240,14 @@ bg_status bg_gemm_workspace_bytes(const bg_gemm_desc* d, int64_t M, int64_t N, i
                                   size_t* bytes);
 
 /* ---- the hot path -------------------------------------------------------- */
+
+/* The tiles bg_gemm_bf16 would launch for this descriptor and shape (host
+ * only: no device, no memory read): the descriptor's schedule, or the
+ * library's choice (a speed knob, [T] 3.2.2; for split_k > 1 the last split
+ * may take its own tile, last_*).  lda = ldb = K and ldc = N are assumed.
+ * M or N of 0 is BG_E_INVALID (nothing would launch); any descriptor or size
+ * bg_gemm_bf16 refuses is refused with the same status. */
+bg_status bg_gemm_bf16_plan(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, bg_gemm_schedule* out);
 
 /* C = A * B^T in bf16 with fp32 accumulation, order fixed by d ([T] 3.2):
  *   for each output (m, n) and split s: acc = +0; for the blocks of

@@ -156,8 +156,12 @@ def loops(lines):
 
 
 def check_kernel(lines, instr, ksteps, blocks):
-    """Problems found in one kernel (an empty list certifies it)."""
+    """Problems found in one kernel (an empty list certifies it).  `blocks`
+    is the number of output blocks a wave owns, or a set of them for a kernel
+    that runs two tile shapes (each must have its own k walk)."""
     problems = []
+    allowed = set(blocks) if isinstance(blocks, (set, frozenset)) else {blocks}
+    seen = set()
     ins = instructions(lines)
     mf = [(i, op, ops) for i, op, ops in ins if op.startswith("v_mfma")]
     for i, op, ops in mf:
@@ -184,8 +188,9 @@ def check_kernel(lines, instr, ksteps, blocks):
         elif next(iter(counts)) % ksteps:
             problems.append(f"loop at {a}: {next(iter(counts))} instructions per accumulator, not a multiple "
                             f"of {ksteps} k-steps")
-        if len(accs) != blocks:
-            problems.append(f"loop at {a}: {len(accs)} accumulators, the wave owns {blocks} blocks")
+        seen.add(len(accs))
+        if len(accs) not in allowed:
+            problems.append(f"loop at {a}: {len(accs)} accumulators, the wave owns {sorted(allowed)} blocks")
         for i, op, ops in body:
             if op.startswith("v_mfma") or op.startswith(STORES) or not ops:
                 continue
@@ -194,6 +199,8 @@ def check_kernel(lines, instr, ksteps, blocks):
                 problems.append(f"line {i}: {op} writes accumulator register {ops[0]} inside the k walk")
     if mf and n_walk == 0:
         problems.append("no loop holds the matrix instructions")
+    if mf and n_walk and not allowed <= seen:
+        problems.append(f"no k walk for the tiles whose waves own {sorted(allowed - seen)} blocks")
     return problems
 
 
@@ -205,6 +212,10 @@ def gemm_variants(asm):
         if "gemm_bf16_pipe_kernel" in name:          # <BM, BN, WM, WN, NS, OUT, RED>
             bm, bn, wm, wn = t[0], t[1], t[2], t[3]
             out.append((name, lines, 0, 32 // INSTR_K[0], (bm // wm // 32) * (bn // wn // 32)))
+        elif "gemm_bf16_pipe_dual_kernel" in name:   # <BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, OUT>
+            b1 = (t[0] // t[2] // 32) * (t[1] // t[3] // 32)
+            b2 = (t[5] // t[7] // 32) * (t[6] // t[8] // 32)
+            out.append((name, lines, 0, 32 // INSTR_K[0], {b1, b2}))
         elif "gemm_bf16_direct_kernel" in name:      # <INSTR, BM, BN, WM, WN, OUT_BF16, PARTIAL>, BK 64
             i, bm, bn, wm, wn = t[0], t[1], t[2], t[3], t[4]
             e = BLOCK[i]

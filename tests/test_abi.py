@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported(bg):
 
 
 def test_abi_version_and_profile(bg):
-    assert bg.lib().bg_abi_version() == 1
+    assert bg.lib().bg_abi_version() == 2
     prof = bg.load_profile()
     from fixed_order_fp_amd.build import profile_hash
     assert bg.profile_hash() == profile_hash()
@@ -201,6 +201,9 @@ JSON_DOCS = [
     '{"gemm": {"split_k": 2, "cut_rule": "EXPLICIT", "cuts": [0, 256, 512], "out_type": "fp32"}}',
     '{"gemm": {"split_k": 16, "out_type": "fp32", "schedule": {"bm": 128, "bn": 64, "bk": 32, '
     '"waves_m": 2, "waves_n": 2, "load_path": 2, "stages": 8}}}',
+    '{"gemm": {"split_k": 16, "out_type": "fp32", "schedule": {"bm": 256, "bn": 256, "bk": 32, "waves_m": 2, '
+    '"waves_n": 4, "load_path": 2, "stages": 4, "last_bm": 128, "last_bn": 64, "last_waves_m": 4, '
+    '"last_waves_n": 2, "last_stages": 8}}}',
     '{"gemm": {"mfma": "F32_16X16X32_BF16", "combine": "SEQUENTIAL", "cut_unit": 128, "split_k": 3}}',
     '{"gemm": {"mfma": "I32_32X32X32_I8", "a_type": "int8", "b_type": "int8", "acc_type": "int32", '
     '"out_type": "bf16", "epilogue": "W8A8_POW2"}}',
@@ -284,3 +287,53 @@ def test_json_writer_buffer_and_names(bg):
     assert L.bg_desc_to_json(C.byref(g), None, big, 4096, C.byref(n)) == 1
     assert L.bg_desc_to_json(None, None, big, 4096, C.byref(n)) == 1
     assert L.bg_desc_from_json(None, C.byref(g), None) == 1
+
+
+# ---------------------------------------------------------------------------
+# the plan query: which tiles a call would launch (host only)
+# ---------------------------------------------------------------------------
+def test_plan_reports_the_schedule_and_the_choice(bg):
+    """An explicit schedule comes back as given (stage counts filled in); the
+    library's choice is a compiled tile; a split sweep whose remainder split
+    is four times deeper than the others (256 x 2560 x 9728, S = 16: fifteen
+    spans of 512 and one of 2048) gives that split its own smaller tile."""
+    sched = dict(bm=128, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2, stages=8)
+    got = bg.gemm_bf16_plan(bg.gemm_desc({"split_k": 2, "schedule": sched}), 300, 500, 1024)
+    assert {k: got[k] for k in sched} == sched and got["last_bm"] == 0
+    pair = dict(sched, stages=0, last_bm=64, last_bn=64, last_waves_m=2, last_waves_n=2)
+    got = bg.gemm_bf16_plan(bg.gemm_desc({"split_k": 3, "schedule": pair}), 300, 500, 1024)
+    assert (got["stages"], got["last_bm"], got["last_bn"], got["last_stages"]) == (4, 64, 64, 8)
+    one = bg.gemm_bf16_plan(bg.gemm_desc({"out_type": "bf16"}), 4000, 9728, 2560)
+    assert (one["bm"], one["bn"], one["last_bm"]) == (320, 256, 0)
+    deep = bg.gemm_bf16_plan(bg.gemm_desc({"split_k": 16, "out_type": "fp32"}), 256, 2560, 9728)
+    assert deep["last_bm"] and deep["last_bm"] * deep["last_bn"] < deep["bm"] * deep["bn"]
+    assert deep["last_waves_m"] * deep["last_waves_n"] == deep["waves_m"] * deep["waves_n"]
+    for S in (1, 2, 4, 8, 16):  # every choice is launchable: the plan fed back is accepted as given
+        d = bg.gemm_desc({"split_k": S, "out_type": "fp32"})
+        p = bg.gemm_bf16_plan(d, 256, 2560, 9728)
+        assert bg.gemm_bf16_plan(bg.gemm_desc({"split_k": S, "out_type": "fp32", "schedule": p}),
+                                 256, 2560, 9728) == p
+
+
+@pytest.mark.parametrize("S,sched,why", [
+    (1, dict(bm=256, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2, last_bm=128, last_bn=64, last_waves_m=4,
+             last_waves_n=2), "split_k > 1"),
+    (4, dict(last_bm=64, last_bn=64, last_waves_m=2, last_waves_n=2), "other splits' tile"),
+    (4, dict(bm=256, bn=256, bk=32, waves_m=2, waves_n=2, load_path=2, last_bm=32, last_bn=32, last_waves_m=1,
+             last_waves_n=1), "not compiled"),
+    (4, dict(bm=256, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2, last_bm=64, last_bn=64, last_waves_m=2,
+             last_waves_n=2), "not compiled"),
+    (4, dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2, load_path=1, last_bm=64, last_bn=64, last_waves_m=2,
+             last_waves_n=2), "not compiled"),
+])
+def test_last_split_tile_refusals(bg, S, sched, why):
+    """A last-split tile needs a split, the other splits' tile, and a
+    compiled pair with the same number of waves; the plan query and the call
+    refuse alike, before any launch."""
+    d = bg.gemm_desc({"split_k": S, "schedule": sched})
+    with pytest.raises(bg.BgError) as e:
+        bg.gemm_bf16_plan(d, 300, 504, 1024)
+    assert e.value.status == "BG_E_UNSUPPORTED" and why in str(e.value)
+    p = 0x10000  # never dereferenced
+    st = bg.lib().bg_gemm_bf16(C.byref(d), 300, 504, 1024, p, 1024, p, 1024, p, 504, p, 1 << 30, None)
+    assert st == 2 and why in bg.lib().bg_last_error().decode()

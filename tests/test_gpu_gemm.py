@@ -47,6 +47,16 @@ SCHEDULES = {
                           dict(bm=16, bn=32, bk=64, waves_m=1, waves_n=2)],
 }
 
+# (other splits, last split) pairs: the last split, the cut rule's remainder,
+# takes its own tile in the same launch (split_k > 1 only)
+DUAL_SCHEDULES = [dict(bm=bm, bn=bn, bk=32, waves_m=wm, waves_n=wn, load_path=2, stages=ns, last_bm=bm2,
+                       last_bn=bn2, last_waves_m=wm2, last_waves_n=wn2, last_stages=ns2)
+                  for bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2 in
+                  [(256, 256, 2, 2, 4, 64, 64, 2, 2, 8), (256, 256, 2, 2, 4, 128, 64, 2, 2, 4),
+                   (256, 128, 2, 2, 4, 64, 64, 2, 2, 8), (192, 128, 2, 2, 4, 64, 64, 2, 2, 8),
+                   (128, 128, 2, 2, 4, 64, 64, 2, 2, 8), (256, 256, 2, 4, 4, 128, 64, 4, 2, 8),
+                   (256, 256, 2, 4, 4, 64, 128, 2, 4, 8)]]
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -103,10 +113,11 @@ def test_schedules_do_not_move_bits(instr):
     print_case("schedules", instr)
     A = synth.bf16_spread(31, (97, 600), -20, 20)
     B = synth.bf16_spread(32, (136, 600), -20, 20)
-    for S in (1, 2):
-        outs = [run_gemm({"mfma": instr, "split_k": S, "schedule": s}, A, B) for s in SCHEDULES[instr]]
-        for o in outs[1:]:
-            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    for S in (1, 2, 3):
+        scheds = SCHEDULES[instr] + (DUAL_SCHEDULES if S > 1 and instr == "F32_32X32X16_BF16" else [])
+        outs = [run_gemm({"mfma": instr, "split_k": S, "cut_unit": 64, "schedule": s}, A, B) for s in scheds]
+        for s, o in zip(scheds[1:], outs[1:]):
+            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), (S, s)
 
 
 @pytest.mark.parametrize("instr", INSTRS)
@@ -162,7 +173,8 @@ def test_spread_parity_ragged(instr):
     for S in (1, 3):
         spec = {"mfma": instr, "split_k": S, "cut_unit": 64}
         ref = oracle.gemm_bf16(oracle_desc(spec, instr), A, B)
-        for sched in [None] + SCHEDULES[instr]:
+        duals = DUAL_SCHEDULES if S > 1 and instr == "F32_32X32X16_BF16" else []
+        for sched in [None] + SCHEDULES[instr] + duals:
             print_case("spread_parity", instr, S, sched)
             got = run_gemm(dict(spec, schedule=sched) if sched else spec, A, B)
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), sched
