@@ -13,4 +13,4 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
-    config.addinivalue_line("markers", "slow: long CPU test")
+    config.addinivalue_line("markers", "slow: long test (CPU, or oracle work beside a GPU test)")

@@ -180,6 +180,23 @@ def test_spread_parity_ragged(instr):
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), sched
 
 
+@pytest.mark.parametrize("S", [5, 6, 7, 9, 15])
+def test_every_combine_width(S):
+    """The combine kernels built for S = 5, 6 and 7 (an odd partial carried
+    up at some level of the tree) and the runtime-S kernel (9, 15): exponent-
+    spread operands, fp32 and bf16 output, 0 ULP against the oracle."""
+    import oracle
+    A = synth.bf16_spread(70 + S, (77, 1000), -20, 20)
+    B = synth.bf16_spread(80 + S, (104, 1000), -20, 20)
+    for out in ("fp32", "bf16"):
+        print_case("combine width", S, out)
+        spec = {"split_k": S, "cut_unit": 64}
+        ref = oracle.gemm_bf16(oracle_desc(dict(spec, out_type=out), "F32_32X32X16_BF16"), A, B)
+        got = run_gemm(spec, A, B, out=out)
+        assert np.array_equal(got.view(np.uint16 if out == "bf16" else np.uint32),
+                              ref.view(np.uint16 if out == "bf16" else np.uint32))
+
+
 @pytest.mark.parametrize("instr", INSTRS)
 def test_widest_split(instr):
     """S = 64, the most splits built: 63 spans of 256 and a last one of 272
@@ -260,6 +277,38 @@ def test_splitk_sweep_full_size(S):
     ni = rng.integers(0, B.shape[0], 96)
     ref = oracle.gemm_bf16_points(oracle_desc({"split_k": S, "out_type": "fp32"}, "F32_32X32X16_BF16"), A, B, mi, ni)
     assert np.array_equal(C[mi, ni].view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("S", [1, 2, 4, 8, 16])
+def test_splitk_sweep_every_output(S):
+    """M = 256, N = 2560, K = 9728 with the plan the bench times: all
+    655,360 fp32 outputs of each S bit-identical to the oracle (about 12.7
+    GFLOP of oracle work per S)."""
+    import oracle
+    A, B = synth.gemm_splitk_sweep()
+    print_case("split-K sweep, every output", S)
+    C = run_gemm({"split_k": S}, A, B, out="fp32")
+    ref = oracle.gemm_bf16(oracle_desc({"split_k": S, "out_type": "fp32"}, "F32_32X32X16_BF16"), A, B)
+    bad = np.flatnonzero(C.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, f"{bad.size} outputs differ, first at {np.unravel_index(bad[0], C.shape)}"
+
+
+@pytest.mark.slow
+def test_batch_sweep_row_bands_every_output():
+    """M = 4000, N = 9728, K = 2560, bf16 out: eight bands of 32 rows spread
+    over M (the first and the ragged last tile row included), every output
+    of each band bit-identical to the oracle; the other M are shown
+    row-identical to M = 4000 by test_batch_sweep_full_size."""
+    import oracle
+    X, W = synth.gemm_batch_sweep(M=4000)
+    print_case("batch sweep M=4000, row bands")
+    C = run_gemm({}, X, W, out="bf16")
+    starts = [0, 320, 1000, 1630, 2240, 2880, 3500, 3968]
+    rows = np.concatenate([np.arange(r, r + 32) for r in starts])
+    ref = oracle.gemm_bf16(oracle_desc({"out_type": "bf16"}, "F32_32X32X16_BF16"), np.ascontiguousarray(X[rows]), W)
+    bad = np.flatnonzero(C[rows] != ref)
+    assert bad.size == 0, f"{bad.size} outputs differ, first at band row {np.unravel_index(bad[0], ref.shape)}"
 
 
 def test_two_rounds_of_large_tiles_match_one_round_tiles():
