@@ -835,6 +835,27 @@ def reduce_extras(args, torch, bg, synth):
             key = f"reduce_{axis}_{in_type}_{rows}x{cols}"
             out[key]["cpu_oracle"] = oracle_rate(lambda: oracle.reduce(sub2, axis, in_type=in_type),
                                                  sub2.size * elt / 1e9, "GB/s", smp)
+        if axis == "row":
+            # the one-read pass against the sum and the sum of squares done as
+            # two separate passes (each reads the matrix once)
+            sep = {}
+            for o in ("sum", "sumsq"):
+                do = bg.reduce_desc(dict(in_type=in_type, op=o, axis=axis))
+                nwo = bg.reduce_workspace_bytes(do, rows, cols)
+                wso = torch.empty(nwo, dtype=torch.uint8, device="cuda") if nwo else None
+                sep[o] = (lambda do=do, wso=wso: bg.reduce_tree(do, rot.next()[0], s, q, wso))
+            settle(fn, torch, 100.0)
+            il = graph_interleaved_ms({"one_pass": fn, "sum_only": sep["sum"], "sumsq_only": sep["sumsq"]},
+                                      args.steps, torch)
+            two = il["sum_only"] + il["sumsq_only"]
+            out[f"reduce_{axis}_{in_type}_{rows}x{cols}"]["separate_passes"] = {
+                "one_pass_graph_us": round(il["one_pass"] * 1e3, 2),
+                "sum_only_graph_us": round(il["sum_only"] * 1e3, 2),
+                "sumsq_only_graph_us": round(il["sumsq_only"] * 1e3, 2),
+                "one_pass_over_two_passes_time": round(il["one_pass"] / two, 4),
+                "timing": "graph replays of the three interleaved over 5 rounds (medians)"}
+            log(f"bench: reduce row one pass {il['one_pass'] * 1e3:.2f} us against sum {il['sum_only'] * 1e3:.2f} "
+                f"+ sumsq {il['sumsq_only'] * 1e3:.2f} us")
         log(f"bench: reduce {axis}: {t * 1e3:.2f} us, graph {tg * 1e3:.2f} us, {gbs:.0f} GB/s "
             f"(free {tf * 1e3:.2f} / {tfg * 1e3:.2f} us)")
     return out
