@@ -974,8 +974,7 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
 
 static size_t align16z(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// slicing: a workgroup per row of A and of B; combine: a lane per output
-// (which also bounds the workspace, 64 M N bytes of int32 products)
+// slicing: a workgroup per row of A and of B; the stacked product 4M x 4N
 bool ozaki_fits(int64_t M, int64_t N)
 {
     return grid_fits(M, 256) && grid_fits(N, 256) && grid_fits((M * N + 255) / 256, 256);
@@ -988,7 +987,7 @@ bg_status bg_gemm_ozaki_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t*
     if (!ozaki_fits(M, N)) return fail(BG_E_UNSUPPORTED, "M, N below 2^24 and M x N below 2^32 for one launch");
     const size_t Kp = (size_t)((K + 15) / 16 * 16);
     *bytes = align16z(4 * (size_t)M * Kp) + align16z(4 * (size_t)N * Kp) + align16z(4 * (size_t)M) +
-             align16z(4 * (size_t)N) + 16 * (size_t)M * (size_t)N * 4;
+             align16z(4 * (size_t)N);
     return BG_OK;
 }
 
@@ -1022,13 +1021,11 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
     w.ea = (int*)base;
     base += align16z(4 * (size_t)M);
     w.eb = (int*)base;
-    base += align16z(4 * (size_t)N);
-    w.acc = (int32_t*)base;
     // speed only: the pipelined int8 tiles (every shape gives the same integers)
     bg::W8A8Plan p{};
     p.mfma = BG_MFMA_I32_32X32X32_I8;
     choose_w8a8_pipe(p, 4 * M, 4 * N);
-    if (!tiles_fit(4 * M, 4 * N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
+    if (!bg::w8a8_ozaki_has_tile(p) || !tiles_fit(4 * M, 4 * N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
         return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     bg_status st = check_device();
     if (st != BG_OK) return st;

@@ -43,6 +43,23 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float x0, float x1)
     return (p & ~m) | (0x7fc07fc0u & m);
 }
 
+// fp64 -> bf16 bits, one rounding to nearest even (no pass through fp32)
+__device__ __forceinline__ uint16_t bf16_from_f64(double v)
+{
+    if (v != v) return 0x7fc0;
+    const uint16_t sign = __builtin_signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);              // a in [2^(e-1), 2^e)
+    int ue = e - 8;                  // bf16 keeps 8 significant bits
+    if (ue < -133) ue = -133;        // subnormal spacing 2^-133
+    const double y = ldexp(rint(ldexp(a, -ue)), ue);
+    if (y >= 0x1p128) return sign | 0x7f80;
+    const float f = (float)y;        // exact: at most 8 significant bits
+    return (uint16_t)(sign | ((__float_as_uint(f) >> 16) & 0x7fff));
+}
+
 // ---- plans handed from the C ABI layer to the launchers -------------------
 struct Cuts {
     int64_t c[BG_MAX_SPLIT + 1];
@@ -104,8 +121,14 @@ struct OzakiWs {
     int8_t* qb;
     int* ea;
     int* eb;
-    int32_t* acc;
 };
+// the Ozaki GEMM's products and recombination (stacked sizes M4 = 4 M, N4 =
+// 4 N; slices interleaved as rows 4r + s); pipelined tiles listed in
+// bg_w8a8.hip only
+bool w8a8_ozaki_has_tile(const W8A8Plan& p);
+hipError_t launch_w8a8_ozaki(const W8A8Plan& p, int64_t M4, int64_t N4, int64_t Kp, const int8_t* qa,
+                             const int8_t* qb, const int* ea, const int* eb, bool out_bf16, void* C, int64_t ldc,
+                             hipStream_t stream);
 // Y == nullptr: the int32 accumulators only (pipelined tiles)
 hipError_t launch_ozaki(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, bool in_bf16, const void* A, int64_t lda,
                         const void* B, int64_t ldb, bool out_bf16, void* C, int64_t ldc, const OzakiWs& w,

@@ -11,14 +11,16 @@
 //   slicing (one workgroup per row): e = frexp exponent of max |x| (0 for a
 //     zero row); r = x * 2^-e in fp64 (exact, |r| < 1); for s = 0..3:
 //     r = 128 r, q_s = trunc(r) in [-127, 127], r = r - q_s (all exact).
-//     Slices go to [4][rows][Kp] int8 (Kp = K rounded up to 16, zero padded).
-//   products: one int8 GEMM of the stacked slices, [4M][Kp] x [4N][Kp]^T,
-//     into int32 [4M][4N] (the pipelined W8A8 kernel, accumulators only):
-//     acc[sM + m][tN + n] = sum_k qA_s[m][k] qB_t[n][k].
-//   recombination (one thread per output): v = sum over pairs of
-//     acc_st 2^(-7 (s + t + 2)) in fp64, in the order s + t = 6, 5, ..., 0
-//     (least significant first), s ascending within a level; v = v 2^(eA + eB);
-//     one rounding to fp32 or bf16 (nearest even).
+//     Slices go to [rows][4][Kp] int8, row 4r + s holding slice s of row r
+//     (Kp = K rounded up to 16, zero padded).
+//   products and recombination in one launch: the int8 GEMM of the stacked
+//     slices, [4M][Kp] x [4N][Kp]^T on the pipelined W8A8 kernel, whose
+//     stacked output (4m + s, 4n + t) is acc_st = sum_k qA_s[m][k] qB_t[n][k];
+//     its epilogue finds all sixteen acc_st of an output in one 32x32 block
+//     and sums acc_st 2^(-7 (s + t + 2)) in fp64 in the order s + t = 6, 5,
+//     ..., 0 (least significant first), s ascending within a level; then
+//     v = v 2^(eA + eB) and one rounding to fp32 or bf16 (nearest even).
+//     The products are never written out.
 #include "bg_internal.h"
 
 namespace bg {
@@ -66,49 +68,8 @@ __global__ __launch_bounds__(256) void ozaki_slice_kernel(const void* __restrict
             }
         }
 #pragma unroll
-        for (int s = 0; s < 4; s++) *(uint32_t*)(Q + ((int64_t)s * rows + r) * Kp + k0) = packed[s];
+        for (int s = 0; s < 4; s++) *(uint32_t*)(Q + (4 * r + s) * Kp + k0) = packed[s];
     }
-}
-
-// fp64 -> bf16 bits, one rounding to nearest even (no pass through fp32)
-__device__ __forceinline__ uint16_t bf16_from_f64(double v)
-{
-    if (v != v) return 0x7fc0;
-    const uint16_t sign = __builtin_signbit(v) ? 0x8000 : 0;
-    const double a = fabs(v);
-    if (a == 0.0) return sign;
-    int e;
-    (void)frexp(a, &e);              // a in [2^(e-1), 2^e)
-    int ue = e - 8;                  // bf16 keeps 8 significant bits
-    if (ue < -133) ue = -133;        // subnormal spacing 2^-133
-    const double y = ldexp(rint(ldexp(a, -ue)), ue);
-    if (y >= 0x1p128) return sign | 0x7f80;
-    const float f = (float)y;        // exact: at most 8 significant bits
-    return (uint16_t)(sign | ((__float_as_uint(f) >> 16) & 0x7fff));
-}
-
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void ozaki_combine_kernel(const int32_t* __restrict__ acc, int64_t M, int64_t N,
-                                                            const int* __restrict__ EA, const int* __restrict__ EB,
-                                                            void* __restrict__ C, int64_t ldc)
-{
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= M * N) return;
-    const int64_t m = idx / N, n = idx % N;
-    const int64_t ld = 4 * N;
-    double v = 0.0;
-#pragma unroll
-    for (int lev = 6; lev >= 0; lev--)
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const int t = lev - s;
-            if (t < 0 || t > 3) continue;
-            // each product is read once, by whole lines: a streaming load
-            v = v + ldexp((double)__builtin_nontemporal_load(&acc[(s * M + m) * ld + t * N + n]), -7 * (lev + 2));
-        }
-    v = ldexp(v, EA[m] + EB[n]);
-    if constexpr (OUT_BF16) ((uint16_t*)C)[m * ldc + n] = bf16_from_f64(v);
-    else ((float*)C)[m * ldc + n] = (float)v;  // one rounding, nearest even
 }
 
 }  // namespace ozaki_impl
@@ -132,14 +93,7 @@ hipError_t launch_ozaki(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, bool
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_w8a8(p, 4 * M, 4 * N, w.Kp, w.qa, w.Kp, w.qb, w.Kp, nullptr, nullptr, nullptr, 0, w.acc, 4 * N, stream);
-    if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((M * N + 255) / 256));
-    if (out_bf16)
-        hipLaunchKernelGGL(ozaki_combine_kernel<true>, grid, dim3(256), 0, stream, w.acc, M, N, w.ea, w.eb, C, ldc);
-    else
-        hipLaunchKernelGGL(ozaki_combine_kernel<false>, grid, dim3(256), 0, stream, w.acc, M, N, w.ea, w.eb, C, ldc);
-    return hipGetLastError();
+    return launch_w8a8_ozaki(p, 4 * M, 4 * N, w.Kp, w.qa, w.qb, w.ea, w.eb, out_bf16, C, ldc, stream);
 }
 
 }  // namespace bg

@@ -207,14 +207,17 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
 // through registers with zeros past K.
 // MODE 0: Y; 1: Y and the int32 accumulators; 2: the accumulators only (no
 // scales, no Y: the integer products other paths build on); 3: Y with the
-// epilogue's order left free (the bench's free-order twin)
+// epilogue's order left free (the bench's free-order twin); 4 and 5: the
+// Ozaki-scheme recombination of slice products into fp32 (4) or bf16 (5)
+// outputs written through Y (see the epilogue)
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
     PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU)))
 void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* __restrict__ W, int64_t ldw,
                       const float* __restrict__ a_scale, const float* __restrict__ w_scale,
                       uint16_t* __restrict__ Y, int64_t ldy, int32_t* __restrict__ acc_out, int64_t ld_acc,
-                      int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, int group_m)
+                      int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, int group_m,
+                      const int* __restrict__ ea, const int* __restrict__ eb)
 {
     constexpr int PK = 64, PCPR = PK / kChunk, KS = PK / 32;  // k tile, chunks per row, k-steps
     constexpr int NW = WM * WN, NT = 64 * NW;
@@ -381,6 +384,55 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
 
     // epilogue: block (j, i), element 4q+u of lane l is row m = wm*WTM + 32i +
     // l%32, column n = wn*WTN + 32j + 8q + 4(l/32) + u
+    if constexpr (MODE >= 4) {
+        // Ozaki-scheme recombination ("GPU Mechanism", the exact-GEMM
+        // paragraph).  The operands are stacked slices, interleaved: stacked
+        // row 4m + s is slice s of row m of A, stacked column 4n + t slice t of
+        // row n of B, so one 32x32 block of stacked outputs holds all sixteen
+        // slice products of 8 x 8 outputs.  Each wave stages its block in LDS
+        // as [m'][s][n'][t]; lane (m' = l/8, n' = l%8) reads its sixteen
+        // products and sums them in fp64 in the fixed order -- s + t = 6, 5,
+        // ..., 0, s ascending within a level, product st weighted 2^-7(s+t+2)
+        // -- scales by 2^(ea[m] + eb[n]) and rounds once.
+        static_assert(NW * 1024 * 4 <= LDS_BYTES, "a staged block per wave fits in LDS");
+        __syncthreads();  // every wave is done with the operand stages
+        int32_t* sb = (int32_t*)lds + wave * 1024;
+        const int mo = lane >> 3, no = lane & 7;
+        const int64_t M4 = M / 4, N4 = N / 4;  // outputs: the stacked sizes are 4 M and 4 N
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                // lane (r_in = 4 m' + s, h) holds n' = 2q + h, t = 0..3 for q = 0..3
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const i32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]};
+                    *(i32x4*)(sb + (((r_in >> 2) * 4 + (r_in & 3)) * 8 + 2 * q + h) * 4) = v;
+                }
+                i32x4 g[4];
+#pragma unroll
+                for (int s4 = 0; s4 < 4; s4++) g[s4] = *(const i32x4*)(sb + ((mo * 4 + s4) * 8 + no) * 4);
+                const int64_t m = (m0 + wm * WTM + 32 * i) / 4 + mo;
+                const int64_t n = (n0 + wn * WTN + 32 * j) / 4 + no;
+                if (m < M4 && n < N4) {
+                    double v = 0.0;
+#pragma unroll
+                    for (int lev = 6; lev >= 0; lev--)
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; s4++) {
+                            const int t4 = lev - s4;
+                            if (t4 < 0 || t4 > 3) continue;
+                            v = v + ldexp((double)g[s4][t4], -7 * (lev + 2));
+                        }
+                    v = ldexp(v, ea[m] + eb[n]);
+                    if constexpr (MODE == 5) Y[m * ldy + n] = bf16_from_f64(v);
+                    else ((float*)Y)[m * ldy + n] = (float)v;  // one rounding, nearest even
+                }
+                // the next block's stores follow these loads in this wave's
+                // LDS order: no barrier
+            }
+        return;
+    }
     // MODE 3 (free-order twin, bench only): Y with the epilogue's order left
     // free -- one combined scale a_scale * w_scale multiplied in once
     constexpr bool WANT_Y = MODE != 2, WANT_ACC = MODE == 1 || MODE == 2;
@@ -457,16 +509,20 @@ hipError_t launch_pipe(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const
     dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
     if (p.free_epilogue)  // free-order twin (bench only)
         hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 3>), grid, block, 0, stream, A, lda, W, ldw,
-                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m, nullptr,
+                           nullptr);
     else if (!Y)
         hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 2>), grid, block, 0, stream, A, lda, W, ldw,
-                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m, nullptr,
+                           nullptr);
     else if (acc_out)
         hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 1>), grid, block, 0, stream, A, lda, W, ldw,
-                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m, nullptr,
+                           nullptr);
     else
         hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 0>), grid, block, 0, stream, A, lda, W, ldw,
-                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m);
+                           a_scale, w_scale, Y, ldy, acc_out, ld_acc, M, N, K, tiles_m, tiles_n, group_m, nullptr,
+                           nullptr);
     return hipGetLastError();
 }
 
@@ -548,6 +604,55 @@ struct W8A8Launcher<2> {
                                                ld_acc, stream);
     }
 };
+
+// The pipelined tiles built with the Ozaki recombination epilogue (the ones
+// the library picks for the stacked product): BM, BN, waves_m, waves_n, stages.
+#define BG_OZAKI_TILES(X) \
+    X(256, 256, 2, 4, 4)  \
+    X(128, 192, 4, 2, 5)  \
+    X(128, 128, 2, 2, 5)  \
+    X(64, 64, 2, 2, 8)
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_pipe_ozaki(const W8A8Plan& p, int64_t M4, int64_t N4, int64_t Kp, const int8_t* qa,
+                             const int8_t* qb, const int* ea, const int* eb, bool out_bf16, void* C, int64_t ldc,
+                             hipStream_t stream)
+{
+    const int tiles_m = (int)((M4 + BM - 1) / BM), tiles_n = (int)((N4 + BN - 1) / BN);
+    const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
+    dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
+    if (out_bf16)
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 5>), grid, block, 0, stream, qa, Kp, qb, Kp, nullptr,
+                           nullptr, (uint16_t*)C, ldc, nullptr, 0, M4, N4, Kp, tiles_m, tiles_n, group_m, ea, eb);
+    else
+        hipLaunchKernelGGL((w8a8_pipe_kernel<BM, BN, WM, WN, NS, 4>), grid, block, 0, stream, qa, Kp, qb, Kp, nullptr,
+                           nullptr, (uint16_t*)C, ldc, nullptr, 0, M4, N4, Kp, tiles_m, tiles_n, group_m, ea, eb);
+    return hipGetLastError();
+}
+
+bool w8a8_ozaki_has_tile(const W8A8Plan& p)
+{
+#define BG_OHAS(BM_, BN_, WM_, WN_, NS_)                                                                     \
+    if (p.path == 2 && p.mfma == BG_MFMA_I32_32X32X32_I8 && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ &&  \
+        p.waves_n == WN_ && (p.stages == 0 || p.stages == NS_))                                                \
+        return true;
+    BG_OZAKI_TILES(BG_OHAS)
+#undef BG_OHAS
+    return false;
+}
+
+hipError_t launch_w8a8_ozaki(const W8A8Plan& p, int64_t M4, int64_t N4, int64_t Kp, const int8_t* qa,
+                             const int8_t* qb, const int* ea, const int* eb, bool out_bf16, void* C, int64_t ldc,
+                             hipStream_t stream)
+{
+#define BG_OLAUNCH(BM_, BN_, WM_, WN_, NS_)                                                                  \
+    if (p.path == 2 && p.mfma == BG_MFMA_I32_32X32X32_I8 && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ &&  \
+        p.waves_n == WN_ && (p.stages == 0 || p.stages == NS_))                                                \
+        return launch_pipe_ozaki<BM_, BN_, WM_, WN_, NS_>(p, M4, N4, Kp, qa, qb, ea, eb, out_bf16, C, ldc, stream);
+    BG_OZAKI_TILES(BG_OLAUNCH)
+#undef BG_OLAUNCH
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_w8a8(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
                        const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,

@@ -337,7 +337,8 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
  * element.  Inputs must be finite.
  * A: [M][lda], B: [N][ldb] of in_type (BG_FP32 or BG_BF16), K contiguous;
  * C: [M][ldc] of out_type.  ws: at least bg_gemm_ozaki_workspace_bytes(),
- * 16-byte aligned (slices, exponents and the 16 M N int32 products).
+ * 16-byte aligned (the slices and exponents; the products are recombined
+ * where the int8 GEMM produces them and never written out).
  * M, N < 2^24 and M * N < 2^32; K rounded up to 16 at most 133,144. */
 bg_status bg_gemm_ozaki_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const void* A, int64_t lda,

@@ -61,6 +61,15 @@ def test_against_oracle(in_type, out_type, M, N, K):
     check(A, B, in_type, out_type)
 
 
+@pytest.mark.parametrize("M,N,K,out_type", [(500, 1000, 300, "fp32"), (260, 3000, 200, "bf16")])
+def test_mid_size_tiles(M, N, K, out_type):
+    """Stacked products large enough for the 128-row int8 tiles (the
+    recombination runs in every tile's epilogue), ragged M and N."""
+    print_case("ozaki mid", M, N, K, out_type)
+    A, B = synth.f32_spread(60 + M, (M, K), -12, 12), synth.f32_spread(61 + N, (N, K), -12, 12)
+    check(A, B, "fp32", out_type)
+
+
 def test_wide_spread_and_zero_rows():
     """Exponents over +-30 (the slices keep 28 bits below each row's largest),
     zero rows in both operands."""
@@ -93,13 +102,14 @@ def test_k_order_does_not_move_a_bit():
 
 def test_headline_shape_sampled():
     """M=4000, N=9728, K=2560 bf16 (the batch-sweep operands) to bf16, checked
-    on 8 rows x 64 columns through the oracle on those rows and columns."""
+    on 32 rows x 128 columns (the first and last of each included) through
+    the oracle on those rows and columns."""
     print_case("ozaki headline")
     X, W = synth.gemm_batch_sweep(M=4000)
     C = run(X, W, "bf16", "bf16")
     rng = np.random.default_rng(4)
-    mi = np.sort(rng.choice(4000, 8, replace=False))
-    ni = np.sort(rng.choice(9728, 64, replace=False))
+    mi = np.sort(np.concatenate([rng.choice(4000, 30, replace=False), [0, 3999]]))
+    ni = np.sort(np.concatenate([rng.choice(9728, 126, replace=False), [0, 9727]]))
     Co = oracle.ozaki_gemm(X[mi], W[ni], in_type="bf16", out_type="bf16")
     assert np.array_equal(C[np.ix_(mi, ni)], Co)
 
