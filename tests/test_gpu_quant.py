@@ -60,7 +60,7 @@ def test_workload_1024x2048():
 
 @pytest.mark.parametrize("M,K,pad,offset", [(7, 1, 0, 0), (5, 3, 1, 0), (33, 2049, 0, 0), (9, 4097, 3, 1),
                                             (17, 256, 0, 1), (3, 1000, 24, 0), (2, 0, 0, 0), (1, 8192 + 4, 0, 0),
-                                            (2, 8192, 0, 0)])
+                                            (2, 8192, 0, 0), (7, 4096, 0, 0), (6, 4092, 4, 0), (5, 4, 0, 0)])
 def test_ragged_and_unaligned(M, K, pad, offset):
     print_case("quantize ragged", M, K, pad, offset)
     x = synth.f32_spread(300 + K, (M, K), -20, 20) if K else np.zeros((M, 0), np.float32)
@@ -121,7 +121,7 @@ def test_requantize_6144x2048(mode):
 
 @pytest.mark.parametrize("mode", ["nearest", "ceil"])
 @pytest.mark.parametrize("N,K,pad,offset", [(5, 1, 0, 0), (9, 17, 3, 1), (33, 100, 0, 0), (4, 4096 + 16, 16, 0),
-                                            (3, 0, 0, 0)])
+                                            (3, 0, 0, 0), (7, 48, 16, 0), (1001, 16, 0, 0)])
 def test_requantize_ragged(mode, N, K, pad, offset):
     print_case("requantize ragged", mode, N, K, pad, offset)
     W = synth.int8_uniform(400 + K, (N, K))
