@@ -149,6 +149,26 @@ bg_status check_common_order(const bg_gemm_desc* d)
 // latency rather than by the MFMA rate.  Needs p.S and p.cuts set.
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of the current device, for the tile choices (speed only; 256
+// on MI355X, and 256 when no device can be asked, as in a host-only plan
+// query).  Read once per device.
+std::mutex g_cu_mu;
+std::vector<int> g_cus;
+int64_t device_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    std::lock_guard<std::mutex> lk(g_cu_mu);
+    if ((int)g_cus.size() <= dev) g_cus.resize(dev + 1, 0);
+    if (!g_cus[dev]) {
+        int n = 0;
+        g_cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                         ? n
+                         : 256;
+    }
+    return g_cus[dev];
+}
+
 // Speed only (int32 sums are exact in any order): the pipelined int8 tile.
 // Outputs of at least 1.5 rounds of 256x256 tiles take that tile (the fewest
 // operand bytes per product; 1.27x the 128x128 tile's rate on the stacked
@@ -160,7 +180,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // deep-pipelined small tiles.
 void choose_w8a8_pipe(bg::W8A8Plan& p, int64_t M, int64_t N)
 {
-    const int64_t n_cu = 256;
+    const int64_t n_cu = device_cus();
     const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), t192 = ceil_div(M, 128) * ceil_div(N, 192);
     p.path = 2;
     if (ceil_div(M, 256) * ceil_div(N, 256) >= n_cu * 3 / 2) {
@@ -267,7 +287,7 @@ const DualPair kDualPairs[] = {{256, 256, 2, 2, 4, 64, 64, 2, 2, 8},  {256, 256,
 // splits' depths; the cheapest wins, a single tile on a tie.
 void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
 {
-    const int64_t n_cu = 256;
+    const int64_t n_cu = device_cus();
     int64_t body = 0;
     for (int s = 0; s + 1 < p.S; s++) body = std::max<int64_t>(body, p.cuts.c[s + 1] - p.cuts.c[s]);
     const int64_t last = p.cuts.c[p.S] - p.cuts.c[p.S - 1];
@@ -324,14 +344,14 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
         else set(32, 32, 64, 1, 1, 0, 0);
         return;
     }
-    const int64_t n_cu = 256;
+    const int64_t n_cu = device_cus();
     // fraction of the last round of workgroups that is busy, weighted in
     auto quant = [&](int64_t bm, int64_t bn, int per_cu) {
         const int64_t wgs = ceil_div(M, bm) * ceil_div(N, bn) * p.S;
         const int64_t slots = n_cu * per_cu;
         return (double)(M * N) / (double)(ceil_div(wgs, slots) * slots * bm * bn) * p.S;
     };
-    if (ceil_div(M, 256) * ceil_div(N, 256) * p.S >= 384) {
+    if (ceil_div(M, 256) * ceil_div(N, 256) * p.S >= n_cu * 3 / 2) {
         if (quant(320, 256, 1) >= quant(256, 320, 1)) set(320, 256, 32, 2, 4, 2, 4);
         else set(256, 320, 32, 4, 2, 2, 4);
         return;
