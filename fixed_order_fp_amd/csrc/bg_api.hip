@@ -297,6 +297,8 @@ void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
     bool have = false;
     for (const PipeTileCost& c : kPipeCosts) {
         if (c.bm > 64 && M <= 64) continue;
+        // some costed shapes exist only as the last split's half of a pair
+        if (!bg::gemm_bf16_has_tile(BG_MFMA_F32_32X32X16_BF16, c.bm, c.bn, 32, c.wm, c.wn, 2, c.ns)) continue;
         const int64_t n = tiles(c.bm, c.bn);
         const double t = lpt2(n * (p.S - 1), wg_us(c, tb), n, wg_us(c, tl), n_cu, pipe_lds_bytes(c));
         if (!have || t < best) {
@@ -308,7 +310,8 @@ void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
     for (const DualPair& d : kDualPairs) {
         const PipeTileCost* a = pipe_cost(d.bm, d.bn, d.wm, d.wn, d.ns);
         const PipeTileCost* b = pipe_cost(d.bm2, d.bn2, d.wm2, d.wn2, d.ns2);
-        if (!a || !b) continue;
+        if (!a || !b || !bg::gemm_bf16_has_dual_tile(d.bm, d.bn, d.wm, d.wn, d.ns, d.bm2, d.bn2, d.wm2, d.wn2, d.ns2))
+            continue;
         const double ta = wg_us(*a, tb), tl2 = wg_us(*b, tl);
         const double t = lpt2(tiles(d.bm, d.bn) * (p.S - 1), ta, tiles(d.bm2, d.bn2), tl2, n_cu,
                               std::max(pipe_lds_bytes(*a), pipe_lds_bytes(*b)));

@@ -337,3 +337,21 @@ def test_last_split_tile_refusals(bg, S, sched, why):
     p = 0x10000  # never dereferenced
     st = bg.lib().bg_gemm_bf16(C.byref(d), 300, 504, 1024, p, 1024, p, 1024, p, 504, p, 1 << 30, None)
     assert st == 2 and why in bg.lib().bg_last_error().decode()
+
+
+def test_every_planned_schedule_is_compiled(bg):
+    """Across shapes and split counts (deep remainder splits among them) the
+    library's choice is always a compiled tile or pair: fed back as an
+    explicit schedule it is accepted and planned identically."""
+    n = 0
+    for M in (65, 100, 256, 300, 1000, 4000):
+        for N in (64, 500, 2560, 9728):
+            for K in (2048, 9728, 20000):
+                for S in (1, 2, 3, 4, 5, 8, 16, 32):
+                    if 256 * S > K:
+                        continue
+                    spec = {"split_k": S, "out_type": "fp32"}
+                    p = bg.gemm_bf16_plan(bg.gemm_desc(spec), M, N, K)
+                    assert bg.gemm_bf16_plan(bg.gemm_desc(dict(spec, schedule=p)), M, N, K) == p, (M, N, K, S, p)
+                    n += p["last_bm"] > 0
+    assert n > 0  # some of them take a pair of tiles
