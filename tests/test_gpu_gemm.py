@@ -334,6 +334,9 @@ def test_two_rounds_of_large_tiles_match_one_round_tiles():
     '{"gemm": {"split_k": 3, "cut_unit": 64, "out_type": "bf16"}}',
     '{"gemm": {"mfma": "F32_16X16X32_BF16", "split_k": 4, "cut_unit": 128, "out_type": "fp32", '
     '"schedule": {"bm": 64, "bn": 64, "bk": 64, "waves_m": 2, "waves_n": 2}}}',
+    '{"gemm": {"split_k": 5, "cut_unit": 64, "out_type": "bf16", "schedule": {"bm": 128, "bn": 128, "bk": 32, '
+    '"waves_m": 2, "waves_n": 2, "load_path": 2, "last_bm": 64, "last_bn": 64, "last_waves_m": 2, '
+    '"last_waves_n": 2}}}',
 ])
 def test_one_json_record_drives_both_sides(text):
     """[T] section 4: one frozen record.  The same descriptor text is read by
