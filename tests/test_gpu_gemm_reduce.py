@@ -157,3 +157,38 @@ def test_argument_errors():
         bg.gemm_bf16_reduce(bg.gemm_desc({}, out_type="fp32"), ok_rd, A, A, Cc, s, None, ws[:1])
     big = bg.reduce_desc({"in_type": "fp32", "axis": "row", "op": "sum"})
     assert bg.gemm_bf16_reduce_workspace_bytes(bg.gemm_desc({}), big, 4, 40000, 64) == 1250 * 4 * 4
+
+
+@pytest.mark.parametrize("axis", ["col", "row"])
+def test_sliced_operand_views(axis):
+    """A and B given as views of wider rows (K = 24 of rows of 40, a k range
+    that is not a whole 32-deep tile), with a short last leaf: the padding
+    columns past K hold large values that must not enter any product, and
+    the fused GEMM and the plain GEMM agree with the oracle on the sliced
+    operands.  (K not a multiple of 8 is refused: test_abi.)"""
+    import torch
+    import fixed_order_fp_amd as bg
+    print_case("gemm_reduce sliced", axis)
+    M, N, K, LD = 45, 70, 24, 40
+    Aw = synth.bf16_normal(901, (M, LD))
+    Bw = synth.bf16_normal(902, (N, LD), sigma=0.05)
+    big = synth.f32_to_bf16_bits(np.float32(1e30))
+    Aw[:, K:] = big
+    Bw[:, K:] = big
+    A, B = np.ascontiguousarray(Aw[:, :K]), np.ascontiguousarray(Bw[:, :K])
+    C32, (rs, rq) = oracle_ref(A, B, axis)
+    d = bg.gemm_desc({"mfma": "F32_32X32X16_BF16"}, out_type="fp32")
+    rd = bg.reduce_desc({"in_type": "fp32", "axis": axis, "op": "sum_and_sumsq"})
+    dA, dB = to_dev_u16(Aw)[:, :K], to_dev_u16(Bw)[:, :K]
+    dC = torch.empty((M, 72), dtype=torch.float32, device="cuda")[:, :N]
+    n_out = N if axis == "col" else M
+    s = torch.empty(n_out, dtype=torch.float32, device="cuda")
+    q = torch.empty(n_out, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(bg.gemm_bf16_reduce_workspace_bytes(d, rd, M, N, K), 4) // 4, dtype=torch.float32,
+                     device="cuda")
+    bg.gemm_bf16_reduce(d, rd, dA, dB, dC, s, q, ws)
+    dC2 = torch.empty((M, 72), dtype=torch.float32, device="cuda")[:, :N]
+    bg.gemm_bf16(d, dA, dB, dC2, None)
+    torch.cuda.synchronize()
+    assert same(dC.cpu().numpy(), C32) and same(dC2.cpu().numpy(), C32)
+    assert same(s.cpu().numpy(), rs) and same(q.cpu().numpy(), rq)
