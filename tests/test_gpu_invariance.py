@@ -74,6 +74,21 @@ def _workloads():
             return [Cc]
         out[f"gemm_bf16 S={S} {otype}"] = gemm
 
+    # a deep remainder split: the plan runs the two-tile-shape split kernel
+    Xd = to_dev_u16(synth.bf16_normal(1004, (300, 9728)))
+    Wd = to_dev_u16(synth.bf16_normal(2004, (1000, 9728), 0.0, 0.02))
+    d16 = bg.gemm_desc({"split_k": 16, "out_type": "fp32"})
+    assert bg.gemm_bf16_plan(d16, 300, 1000, 9728)["last_bm"] > 0
+    n16 = bg.gemm_workspace_bytes(d16, 300, 1000, 9728)
+
+    def gemm_deep(stream):
+        Cc = torch.empty((300, 1000), dtype=torch.float32, device="cuda")
+        ws = torch.empty(n16, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        bg.gemm_bf16(d16, Xd, Wd, Cc, ws, stream=stream)
+        return [Cc]
+    out["gemm_bf16 S=16 two tile shapes"] = gemm_deep
+
     a_q, w_q, a_s, w_s = synth.w8a8_input(M=256, N=768, K=2048)
     dA, dW = torch.from_numpy(a_q).cuda(), torch.from_numpy(w_q).cuda()
     dsa, dsw = torch.from_numpy(a_s).cuda(), torch.from_numpy(w_s).cuda()
