@@ -168,6 +168,17 @@ def host_cost(head, torch, bg, n=100, reps=5):
                     f"{reps} batches; the plan is derived on every call, no cache"}
 
 
+def plan_note(bg, g):
+    """The tiles the library picked for a workload (its own plan query), as
+    text: BMxBN/waves/stages, and the last split's own tile where it has one."""
+    p = bg.gemm_bf16_plan(g.desc, g.M, g.N, g.K)
+    s = f"{p['bm']}x{p['bn']} tile, {p['waves_m']}x{p['waves_n']} waves, {p['stages']} stages"
+    if p["last_bm"]:
+        s += (f"; last split {p['last_bm']}x{p['last_bn']} tile, {p['last_waves_m']}x{p['last_waves_n']} waves, "
+              f"{p['last_stages']} stages")
+    return s
+
+
 def time_steps(fn, steps, warmup, torch, settle_ms=100.0):
     """Warm up (`warmup` calls, then the same call for `settle_ms` of wall
     time: after host-side work the clock takes tens of milliseconds to come
@@ -524,7 +535,8 @@ def gemm_extras(X, W, args, torch, bg, synth):
                                "free_same_split_graph_us": round(same_g * 1e3, 2),
                                "fixed_over_free_same_split_time": round(tg / same_g, 3),
                                "outputs_differing_from_S1": {"fp32": diff32, "after_bf16_rounding": diff16,
-                                                             "of": int(g.M * g.N)}}
+                                                             "of": int(g.M * g.N)},
+                               "plan": plan_note(bg, g)}
         if S == 16 and not args.no_cpu_baseline:
             import numpy as np
             import oracle
@@ -1039,7 +1051,7 @@ def main():
                    "M": 4000, "N": 9728, "K": 2560, "split_k": 1, "mfma": "F32_32X32X16_BF16",
                    "out": "bf16", "inputs": head.rot.note(), "hot_ms_per_step": round(ms_hot, 5),
                    "per_launch_ms": per_launch,
-                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 5)},
+                   "wall_ms_per_step": round(wall * 1e3 / args.steps, 5), "plan": plan_note(bg, head)},
         "parity": par,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
