@@ -180,6 +180,22 @@ def test_spread_parity_ragged(instr):
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), sched
 
 
+def test_two_tile_shapes_on_tiny_outputs():
+    """Every compiled (other splits, last split) pair on outputs much smaller
+    than either tile (one row, eight columns; 33 x 40), the remainder split
+    the deepest: 0 ULP against the oracle."""
+    import oracle
+    for M, N in ((1, 8), (33, 40)):
+        A = synth.bf16_spread(90 + M, (M, 600), -20, 20)
+        B = synth.bf16_spread(91 + N, (N, 600), -20, 20)
+        spec = {"split_k": 3, "cut_unit": 64}
+        ref = oracle.gemm_bf16(oracle_desc(dict(spec, out_type="fp32"), "F32_32X32X16_BF16"), A, B)
+        for sched in DUAL_SCHEDULES:
+            print_case("two tile shapes, tiny", M, N, sched)
+            got = run_gemm(dict(spec, schedule=sched), A, B)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (M, N, sched)
+
+
 @pytest.mark.parametrize("S", [5, 6, 7, 9, 15])
 def test_every_combine_width(S):
     """The combine kernels built for S = 5, 6 and 7 (an odd partial carried
