@@ -223,3 +223,35 @@ def two_stage_instr(acc, a_bits, b_bits, group, F, G):
             s = cut(s, Fraction(2) ** (lead - G), True)
         acc = round_f32(s, "rne") if s != 0 else np.float32(0.0)
     return acc
+
+
+def catalan(n):
+    from math import comb
+    return comb(2 * n, n) // (n + 1)
+
+
+def all_tree_values(vals):
+    """fp32 values of every ordered binary tree over vals (Catalan(S-1) of
+    them), by intervals: the trees over [i, j) are those over [i, k) joined
+    to those over [k, j), k ascending, each pair added in fp32; the array
+    order is that enumeration."""
+    S = len(vals)
+    V = {(i, i + 1): np.array([vals[i]], dtype=np.float32) for i in range(S)}
+    for length in range(2, S + 1):
+        for i in range(S - length + 1):
+            j = i + length
+            V[(i, j)] = np.concatenate([(V[(i, k)][:, None] + V[(k, j)][None, :]).ravel() for k in range(i + 1, j)])
+    return V[(0, S)]
+
+
+def tree_index(tree, i, j):
+    """Position of one tree over [i, j) in all_tree_values' order."""
+    if isinstance(tree, int):
+        return 0
+
+    def span(t):
+        return (t, t + 1) if isinstance(t, int) else (span(t[0])[0], span(t[1])[1])
+
+    k = span(tree[0])[1]
+    off = sum(catalan(kk - i - 1) * catalan(j - kk - 1) for kk in range(i + 1, k))
+    return off + tree_index(tree[0], i, k) * catalan(j - k - 1) + tree_index(tree[1], k, j)

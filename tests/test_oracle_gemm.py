@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from exact import all_trees, eval_tree, pairwise_recursive
+from exact import all_tree_values, all_trees, catalan, eval_tree, pairwise_recursive, tree_index
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 ONE = 0x3F80  # bf16 1.0
@@ -196,38 +196,6 @@ def test_combine_is_the_balanced_member_of_all_trees(S):
     assert caught[others].all()
 
 
-def _catalan(n):
-    from math import comb
-    return comb(2 * n, n) // (n + 1)
-
-
-def _all_tree_values(vals):
-    """fp32 values of every ordered binary tree over vals (Catalan(S-1) of
-    them), by intervals: the trees over [i, j) are those over [i, k) joined
-    to those over [k, j), k ascending, each pair added in fp32; the array
-    order is that enumeration."""
-    S = len(vals)
-    V = {(i, i + 1): np.array([vals[i]], dtype=np.float32) for i in range(S)}
-    for length in range(2, S + 1):
-        for i in range(S - length + 1):
-            j = i + length
-            V[(i, j)] = np.concatenate([(V[(i, k)][:, None] + V[(k, j)][None, :]).ravel() for k in range(i + 1, j)])
-    return V[(0, S)]
-
-
-def _tree_index(tree, i, j):
-    """Position of one tree over [i, j) in _all_tree_values' order."""
-    if isinstance(tree, int):
-        return 0
-
-    def span(t):
-        return (t, t + 1) if isinstance(t, int) else (span(t[0])[0], span(t[1])[1])
-
-    k = span(tree[0])[1]
-    off = sum(_catalan(kk - i - 1) * _catalan(j - kk - 1) for kk in range(i + 1, k))
-    return off + _tree_index(tree[0], i, k) * _catalan(j - k - 1) + _tree_index(tree[1], k, j)
-
-
 @pytest.mark.parametrize("S", [11, 12, 16])
 def test_combine_is_the_balanced_member_of_all_trees_up_to_16(S):
     """The same check for split counts up to 16, where the trees are too many
@@ -235,11 +203,11 @@ def test_combine_is_the_balanced_member_of_all_trees_up_to_16(S):
     computed by intervals, the oracle's combine equals the balanced
     neighbours-first member's value, and over 80 exponent-spread draws every
     other tree gives other bits at least once."""
-    mine = _tree_index(_level_pairs_tree(0, S), 0, S)
-    caught = np.zeros(_catalan(S - 1), dtype=bool)
+    mine = tree_index(_level_pairs_tree(0, S), 0, S)
+    caught = np.zeros(catalan(S - 1), dtype=bool)
     for draw in range(80):
         vals = synth.f32_spread(1000 + 97 * S + draw, (S,), -12, 12)
-        allv = _all_tree_values(vals)
+        allv = all_tree_values(vals)
         got = np.float32(oracle.tree_balanced(vals))
         assert allv[mine] == got, draw
         caught |= allv != got

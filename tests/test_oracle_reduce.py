@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from exact import all_trees, eval_tree, pairwise_recursive
+from exact import all_tree_values, all_trees, catalan, eval_tree, pairwise_recursive, tree_index
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -90,6 +90,23 @@ def test_reduction_is_one_member_of_all_trees(n, leaf):
         assert s[0] == eval_tree(mine, x[0])
         caught |= np.array([eval_tree(t, x[0]) for t in trees], dtype=np.float32) != s[0]
     assert caught[[i for i, t in enumerate(trees) if t != mine]].all()
+
+
+@pytest.mark.parametrize("n,leaf", [(16, 1), (16, 2), (16, 4), (16, 8), (16, 16), (13, 4), (14, 3)])
+def test_reduction_is_one_member_of_all_trees_up_to_16(n, leaf):
+    """The same at n up to 16 (9,694,845 ordered trees at n = 16), every
+    tree's fp32 value computed by intervals: the oracle's sum equals its
+    stated tree's value, and over 80 exponent-spread draws every other tree
+    gives other bits at least once."""
+    mine = tree_index(_expected_tree(n, leaf), 0, n)
+    caught = np.zeros(catalan(n - 1), dtype=bool)
+    for draw in range(80):
+        x = synth.f32_spread(700 + 13 * n + leaf + draw, (1, n), -12, 12)
+        s, _ = oracle.reduce(x, "row", leaf_len=leaf)
+        allv = all_tree_values(x[0])
+        assert allv[mine] == s[0], draw
+        caught |= allv != s[0]
+    assert not caught[mine] and int(caught.sum()) == len(caught) - 1
 
 
 def test_one_leaf_is_a_sequential_fold():
