@@ -29,7 +29,7 @@ The same JSON line also carries:
                 (rates are quoted on it).
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--no-cpu-baseline] [--no-extra]
-       [--only-headline] [--copy-calibration]
+       [--only-headline | --only-reductions | --only-w8a8] [--copy-calibration]
        python bench.py --summarize-trace <rocprofv3 kernel_trace.csv> [timed steps, 50]
 """
 import argparse
@@ -918,6 +918,38 @@ def reductions_only(args, torch, bg, synth):
     print(json.dumps({"note": "reductions only (counter run)", "reductions": res}), flush=True)
 
 
+def w8a8_only(args, torch, bg, synth):
+    """Eager, rotated calls of the W8A8 GEMM (1024 x 6144 x 2048, power-of-two
+    epilogue), for counter runs: no graphs and no twins, so that every GEMM
+    dispatch is this kernel; sampled outputs checked against the oracle."""
+    import numpy as np
+    import oracle
+    a_q, w_q, a_s, w_s = synth.w8a8_input()
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    d = bg.gemm_desc(dict(mfma="I32_32X32X32_I8", a_type="int8", b_type="int8", acc_type="int32",
+                          out_type="bf16", epilogue="W8A8_POW2"))
+    dA, dW = torch.from_numpy(a_q).cuda(), torch.from_numpy(w_q).cuda()
+    sa, sw = torch.from_numpy(a_s).cuda(), torch.from_numpy(w_s).cuda()
+    dY = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    bg.gemm_w8a8_pow2(d, dA, dW, sa, sw, dY)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(M, 16, replace=False))
+    Yo, _ = oracle.w8a8_pow2(a_q[rows], w_q, a_s[rows], w_s)
+    bad = int(np.sum(dY.cpu().numpy().view(np.uint16)[rows] != Yo))
+    rot = Rotation([dA, dW, sa, sw])
+
+    def fn():
+        a, w, x, y = rot.next()
+        bg.gemm_w8a8_pow2(d, a, w, x, y, dY)
+
+    t, _ = time_steps(fn, args.steps, args.warmup, torch)
+    ops = 2.0 * M * N * K
+    print(json.dumps({"note": "W8A8 only (counter run)", "us": round(t * 1e3, 2),
+                      "TOP/s": round(ops / t / 1e9, 2), "inputs": rot.note(),
+                      "parity": {"sampled_rows": int(len(rows)), "mismatches": bad}}), flush=True)
+
+
 def summarize_trace(path, tail):
     """Markdown table of a rocprofv3 kernel-trace CSV grouped by kernel and grid
     size (one workload per grid), so a kernel that serves several workloads
@@ -996,6 +1028,8 @@ def main():
                     help="time the headline GEMM only (for counter runs): no twins, extras or CPU baseline")
     ap.add_argument("--only-reductions", action="store_true",
                     help="eager calls of the row and column reductions only (for counter runs)")
+    ap.add_argument("--only-w8a8", action="store_true",
+                    help="eager calls of the W8A8 GEMM only, 1024 x 6144 x 2048 (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
@@ -1016,6 +1050,9 @@ def main():
         if args.copy_calibration:
             copy_calibration(torch)
         reductions_only(args, torch, bg, synth)
+        return
+    if args.only_w8a8:
+        w8a8_only(args, torch, bg, synth)
         return
     log("bench: generating the batch-sweep workload")
     X, W = synth.gemm_batch_sweep(M=4000)
