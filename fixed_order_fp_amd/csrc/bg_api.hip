@@ -336,7 +336,7 @@ bool dual_last_first(const bg::GemmPlan& p)
     return wg_us(*b, (last + 31) / 32) >= wg_us(*a, (body + 31) / 32);
 }
 
-void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
+void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N, int64_t lda, int64_t ldb)
 {
     auto set = [&](int bm, int bn, int bk, int wm, int wn, int direct, int stages) {
         p.bm = bm, p.bn = bn, p.bk = bk, p.waves_m = wm, p.waves_n = wn, p.direct = direct, p.stages = stages;
@@ -355,8 +355,12 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N)
         return (double)(M * N) / (double)(ceil_div(wgs, slots) * slots * bm * bn) * p.S;
     };
     if (ceil_div(M, 256) * ceil_div(N, 256) * p.S >= n_cu * 3 / 2) {
-        if (quant(320, 256, 1) >= quant(256, 320, 1)) set(320, 256, 32, 2, 4, 2, 4);
-        else set(256, 320, 32, 4, 2, 2, 4);
+        // 64-deep k tiles in two stages (whole 128-byte lines per copy) where
+        // the copy offsets fit, else the 32-deep four-stage ring
+        const bool tall = quant(320, 256, 1) >= quant(256, 320, 1);
+        const bool deep = bg::pipe_offsets_fit(tall ? 320 : 256, tall ? 256 : 320, lda, ldb);
+        if (tall) deep ? set(320, 256, 64, 2, 4, 2, 2) : set(320, 256, 32, 2, 4, 2, 4);
+        else deep ? set(256, 320, 64, 4, 2, 2, 2) : set(256, 320, 32, 4, 2, 2, 4);
         return;
     }
     if (M <= 32) {  // 304 workgroups of 32x64 stream W faster than 152 of 64x64
@@ -648,13 +652,17 @@ bg_status check_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K
 
 // the tiles of plan p (M, N > 0): the descriptor's schedule, or the
 // library's choice for the shape
-bg_status resolve_gemm_schedule(const bg_gemm_desc* d, int64_t M, int64_t N, bg::GemmPlan& p)
+bg_status resolve_gemm_schedule(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t lda, int64_t ldb,
+                                bg::GemmPlan& p)
 {
     const bg_gemm_schedule& s = d->sched;
     p.group_m = s.group_m;
     if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
         if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path, s.stages))
             return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path, stages) is not compiled in");
+        if (s.load_path == 2 && s.bk == 64 && !bg::pipe_offsets_fit(s.bm, s.bn, lda, ldb))
+            return fail(BG_E_UNSUPPORTED, "a 64-deep pipelined tile addresses its copies by 32-bit offsets: "
+                                          "(bm - 1) x lda and (bn - 1) x ldb must stay below 2^31 elements");
         p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
         p.direct = s.load_path;
         p.stages = s.stages;
@@ -678,7 +686,7 @@ bg_status resolve_gemm_schedule(const bg_gemm_desc* d, int64_t M, int64_t N, bg:
     } else {
         if (s.last_bm || s.last_bn || s.last_waves_m || s.last_waves_n || s.last_stages)
             return fail(BG_E_UNSUPPORTED, "a last-split tile needs the other splits' tile (bm .. waves_n) set");
-        choose_gemm_tile(p, M, N);
+        choose_gemm_tile(p, M, N, lda, ldb);
     }
     if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n) || (p.S > 1 && !grid_fits((M * N + 255) / 256, 256)))
         return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
@@ -695,7 +703,7 @@ bg_status bg_gemm_bf16_plan(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
     bg_status st = check_gemm_bf16(d, M, N, K, K, K, N, p);
     if (st != BG_OK) return st;
     if (M == 0 || N == 0) return fail(BG_E_INVALID, "an empty product launches nothing");
-    st = resolve_gemm_schedule(d, M, N, p);
+    st = resolve_gemm_schedule(d, M, N, K, K, p);
     if (st != BG_OK) return st;
     bg_gemm_schedule s{};
     s.bm = p.bm, s.bn = p.bn, s.bk = p.bk, s.waves_m = p.waves_m, s.waves_n = p.waves_n, s.load_path = p.direct;
@@ -722,7 +730,7 @@ bg_status bg_gemm_bf16(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t K, c
         if (!ws || ws_bytes < need) return fail(BG_E_WORKSPACE, "split-K needs S*M*N*4 bytes of workspace");
         if (!aligned16(ws)) return fail(BG_E_ALIGN, "workspace must be 16-byte aligned");
     }
-    st = resolve_gemm_schedule(d, M, N, p);
+    st = resolve_gemm_schedule(d, M, N, lda, ldb, p);
     if (st != BG_OK) return st;
     st = check_device();
     if (st != BG_OK) return st;
@@ -962,19 +970,28 @@ bg_status bg_gemm_bf16_reduce(const bg_gemm_desc* d, const bg_reduce_desc* rd, i
     const bg_gemm_schedule& s = d->sched;
     p.group_m = s.group_m;
     if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
-        if ((s.bk && s.bk != 32) || (s.load_path && s.load_path != 2) ||
-            !bg::gemm_bf16_red_has_tile(s.bm, s.bn, s.waves_m, s.waves_n, s.stages))
+        const int bk = s.bk ? s.bk : 32;
+        if ((s.load_path && s.load_path != 2) ||
+            !bg::gemm_bf16_red_has_tile(s.bm, s.bn, bk, s.waves_m, s.waves_n, s.stages))
             return fail(BG_E_UNSUPPORTED, "schedule is not built with the fused reductions");
-        p.bm = s.bm, p.bn = s.bn, p.bk = 32, p.waves_m = s.waves_m, p.waves_n = s.waves_n, p.direct = 2;
+        if (bk == 64 && !bg::pipe_offsets_fit(s.bm, s.bn, lda, ldb))
+            return fail(BG_E_UNSUPPORTED, "a 64-deep pipelined tile addresses its copies by 32-bit offsets: "
+                                          "(bm - 1) x lda and (bn - 1) x ldb must stay below 2^31 elements");
+        p.bm = s.bm, p.bn = s.bn, p.bk = bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n, p.direct = 2;
         p.stages = s.stages;
     } else {  // speed only: the tiles built with the reductions
-        auto set = [&](int bm, int bn, int wm, int wn, int ns) {
-            p.bm = bm, p.bn = bn, p.bk = 32, p.waves_m = wm, p.waves_n = wn, p.direct = 2, p.stages = ns;
+        auto set = [&](int bm, int bn, int bk, int wm, int wn, int ns) {
+            p.bm = bm, p.bn = bn, p.bk = bk, p.waves_m = wm, p.waves_n = wn, p.direct = 2, p.stages = ns;
         };
         const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-        if (big >= 384) set(320, 256, 2, 4, 4);
-        else if (M > 64 && ((M + 255) / 256) * ((N + 127) / 128) >= 150) set(256, 128, 2, 2, 4);
-        else set(64, 64, 2, 2, 8);
+        if (big >= 384) {
+            if (bg::pipe_offsets_fit(320, 256, lda, ldb)) set(320, 256, 64, 2, 4, 2);
+            else set(320, 256, 32, 2, 4, 4);
+        } else if (M > 64 && ((M + 255) / 256) * ((N + 127) / 128) >= 150) {
+            set(256, 128, 32, 2, 2, 4);
+        } else {
+            set(64, 64, 32, 2, 2, 8);
+        }
     }
     if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n) || !grid_fits((n_out + 63) / 64, 1024))
         return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
@@ -1115,7 +1132,7 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     p.S = 1;
     p.cuts.c[0] = 0;
     p.cuts.c[1] = K;
-    choose_gemm_tile(p, M, N);
+    choose_gemm_tile(p, M, N, lda, ldb);
     int S = split_k;
     if (S <= 0) {  // at least one workgroup per CU, each split at least 256 deep
         int dev = 0, n_cu = 256;
@@ -1131,7 +1148,7 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     for (int s = 0; s < S; s++) p.cuts.c[s] = s * span;
     p.cuts.c[S] = K;
     p.atomic = S > 1;
-    if (S > 1) choose_gemm_tile(p, M, N);  // the tile (or pair of tiles) for the split grid
+    if (S > 1) choose_gemm_tile(p, M, N, lda, ldb);  // the tile (or pair of tiles) for the split grid
     if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
         return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     p.atomic = S > 1;

@@ -168,7 +168,16 @@ bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves
 bool gemm_bf16_has_dual_tile(int bm, int bn, int waves_m, int waves_n, int stages, int bm2, int bn2, int waves_m2,
                              int waves_n2, int stages2);
 // tiles built with the fused reductions (pipelined path, S = 1)
-bool gemm_bf16_red_has_tile(int bm, int bn, int waves_m, int waves_n, int stages);
+bool gemm_bf16_red_has_tile(int bm, int bn, int bk, int waves_m, int waves_n, int stages);
+
+// The 64-deep pipelined tiles address each copy by a 32-bit byte offset from
+// the tile's first row: (rows - 1) x leading dimension x 2 bytes, plus a
+// 128-byte row piece, must stay below 2^32.
+inline bool pipe_offsets_fit(int64_t bm, int64_t bn, int64_t lda, int64_t ldb)
+{
+    const int64_t lim = (int64_t)1 << 32;
+    return (bm - 1) * lda * 2 + 128 < lim && (bn - 1) * ldb * 2 + 128 < lim;
+}
 hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                                    const uint16_t* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream);
 

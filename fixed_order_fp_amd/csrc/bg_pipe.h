@@ -63,6 +63,32 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr)
         : "memory");
 }
 
+// The same copy addressed as a 64-bit scalar base plus a 32-bit byte offset
+// per lane (the global instruction's scalar-base form), so that a lane keeps
+// one register per copy instead of a pointer pair: the base walks k in
+// scalar registers, the offsets stay fixed for the whole walk.
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds_addr)
+{
+    lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds_addr)
+        : "memory");
+}
+
+// s_waitcnt lgkmcnt(0), other counters untouched: this wave's LDS reads and
+// writes are complete
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
 // s_waitcnt vmcnt(N), other counters untouched
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -101,19 +127,19 @@ __device__ __forceinline__ int c_swizzle(int ch, int m)
     else return ch ^ (m & (CHR - 1));
 }
 
-// LDS a pipelined kernel uses (NS stages of a 64-byte k tile per row of A and
-// B; a bf16 output tile staged when OUT == 1), and the waves per SIMD that
-// leaves room for
-template <int BM, int BN, int NS, int OUT>
+// LDS a pipelined kernel uses (NS stages of a k tile of ROW_BYTES per row of
+// A and B; a bf16 output tile staged when OUT == 1), and the waves per SIMD
+// that leaves room for
+template <int BM, int BN, int NS, int OUT, int ROW_BYTES = 64>
 struct PipeLds {
-    static constexpr int STAGE_BYTES = (BM + BN) * 64;
+    static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
     static constexpr int PIPE = NS * STAGE_BYTES, EPI = OUT == 1 ? BM * BN * 2 : 0;
     static constexpr int BYTES = PIPE > EPI ? PIPE : EPI;
     static constexpr int WG_PER_CU = (160 * 1024) / BYTES;
 };
-template <int BM, int BN, int WM, int WN, int NS, int OUT>
+template <int BM, int BN, int WM, int WN, int NS, int OUT, int ROW_BYTES = 64>
 struct PipeOcc {
-    static constexpr int W = PipeLds<BM, BN, NS, OUT>::WG_PER_CU * WM * WN / 4;
+    static constexpr int W = PipeLds<BM, BN, NS, OUT, ROW_BYTES>::WG_PER_CU * WM * WN / 4;
     static constexpr int WAVES_PER_EU = W < 1 ? 1 : W;
 };
 

@@ -40,7 +40,7 @@ def test_every_w8a8_variant(w8a8_asm):
 
 def _headline(asm):
     for name, lines, i, ks, bl in T.gemm_variants(asm):
-        if "pipe_kernelILi320ELi256ELi2ELi4ELi4ELi1ELi0E" in name:
+        if "pipe_kernelILi320ELi256ELi2ELi4ELi2ELi1ELi0ELi64E" in name:
             return list(lines), i, ks, bl
     raise AssertionError("headline variant not compiled")
 
