@@ -414,7 +414,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 // t, before its first MFMA; every wave waits for its copies and for its LDS
 // reads of tile t before the turn's barrier, after which tile t+1's first
 // operands are read and tile t's last k-step is multiplied.  Measured 10 %
-// faster than the 32-deep ring on the large-output tile, bit-identical.
+// faster than the 32-deep ring on the large-output tiles (8 waves, two
+// rounds of workgroups or more), bit-identical; on the mid-size tiles (4
+// waves, one round) the single tile in flight made it 10-90 % slower, so
+// those keep the 32-deep ring.
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32
 // split partial added into C with atomics (the free-order twin only)
@@ -1160,9 +1163,6 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
 #define BG_GEMM_TILES(X)                                            \
     X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 64, 2, 4, 2, 2)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 64, 4, 2, 2, 2)          \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 64, 2, 4, 2, 2)          \
-    X(BG_MFMA_F32_32X32X16_BF16, 256, 128, 64, 2, 2, 2, 2)          \
-    X(BG_MFMA_F32_32X32X16_BF16, 192, 128, 64, 2, 2, 2, 2)          \
     X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 32, 2, 4, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 32, 4, 2, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 2, 2, 4)          \
