@@ -177,20 +177,24 @@ int64_t device_cus()
 // per CU: rounds x workgroups per CU x (BM + BN), one workgroup per CU
 // (128x192, 8 waves) costing ~1.4x per byte against two (128x128, 5 stages),
 // as measured at 1024 x 6144 x 2048 with inputs not in the MALL.  Otherwise
-// deep-pipelined small tiles.
-void choose_w8a8_pipe(bg::W8A8Plan& p, int64_t M, int64_t N)
+// deep-pipelined small tiles.  The large and mid-size tiles take 128-byte k
+// tiles in two stages (whole 128-byte lines per copy: 3-13 % faster than
+// the 64-byte rings on these shapes, measured on MI355X) where the copy
+// offsets fit, else the 64-byte ring.
+void choose_w8a8_pipe(bg::W8A8Plan& p, int64_t M, int64_t N, int64_t lda, int64_t ldw)
 {
     const int64_t n_cu = device_cus();
     const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), t192 = ceil_div(M, 128) * ceil_div(N, 192);
     p.path = 2;
     if (ceil_div(M, 256) * ceil_div(N, 256) >= n_cu * 3 / 2) {
-        p.bm = 256, p.bn = 256, p.waves_m = 2, p.waves_n = 4, p.stages = 4;
+        p.bm = 256, p.bn = 256, p.waves_m = 2, p.waves_n = 4;
+        p.stages = bg::i8_offsets_fit(256, 256, lda, ldw) ? 2 : 4;
     } else if (t128 >= 192) {
         const double c128 = (double)ceil_div(t128, 2 * n_cu) * 2 * 256;
         const double c192 = (double)ceil_div(t192, n_cu) * 320 * 1.4;
         if (c192 < c128) p.bm = 128, p.bn = 192, p.waves_m = 4, p.waves_n = 2;
         else p.bm = 128, p.bn = 128, p.waves_m = 2, p.waves_n = 2;
-        p.stages = 5;
+        p.stages = bg::i8_offsets_fit(p.bm, p.bn, lda, ldw) ? 2 : 5;
     } else {
         p.bm = 64, p.bn = 64, p.waves_m = 2, p.waves_n = 2, p.stages = 8;
     }
@@ -788,10 +792,18 @@ bg_status bg_gemm_w8a8_pow2(const bg_gemm_desc* d, int64_t M, int64_t N, int64_t
         const int path = s.load_path ? s.load_path : 1;
         if (!bg::w8a8_has_tile(p.mfma, s.bm, s.bn, s.waves_m, s.waves_n, path, s.stages))
             return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, waves, load_path, stages) is not compiled in for W8A8");
+        // two stages on the pipelined path: 128-byte k tiles, copies addressed
+        // by 32-bit offsets (the first compiled entry of a shape, so also
+        // stages 0 where the shape has it)
+        const bool two = path == 2 && (s.stages == 2 ||
+                                       (s.stages == 0 && bg::w8a8_has_tile(p.mfma, s.bm, s.bn, s.waves_m, s.waves_n, 2, 2)));
+        if (two && !bg::i8_offsets_fit(s.bm, s.bn, lda, ldw))
+            return fail(BG_E_UNSUPPORTED, "a two-stage W8A8 tile addresses its copies by 32-bit offsets: "
+                                          "(bm - 1) x lda and (bn - 1) x ldw must stay below 2^32 bytes");
         p.bm = s.bm, p.bn = s.bn, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
-        p.path = path, p.stages = s.stages;
+        p.path = path, p.stages = two ? 2 : s.stages;
     } else if (p.mfma == BG_MFMA_I32_32X32X32_I8) {
-        choose_w8a8_pipe(p, M, N);
+        choose_w8a8_pipe(p, M, N, lda, ldw);
     } else {
         const bool big = M >= 128 && N >= 128 && ((M + 127) / 128) * ((N + 127) / 128) >= 128;
         p.bm = big ? 128 : 64, p.bn = big ? 128 : 64, p.waves_m = 2, p.waves_n = 2;
@@ -1064,7 +1076,7 @@ bg_status bg_gemm_ozaki(int64_t M, int64_t N, int64_t K, uint32_t in_type, const
     // speed only: the pipelined int8 tiles (every shape gives the same integers)
     bg::W8A8Plan p{};
     p.mfma = BG_MFMA_I32_32X32X32_I8;
-    choose_w8a8_pipe(p, 4 * M, 4 * N);
+    choose_w8a8_pipe(p, 4 * M, 4 * N, Kp, Kp);
     if (!bg::w8a8_ozaki_has_tile(p) || !tiles_fit(4 * M, 4 * N, p.bm, p.bn, 64 * p.waves_m * p.waves_n))
         return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     bg_status st = check_device();
@@ -1174,7 +1186,7 @@ bg_status bg_bench_gemm_w8a8_free(int64_t M, int64_t N, int64_t K, const int8_t*
         return fail(BG_E_ALIGN, "pointers must be aligned and leading dimensions multiples of 16 (int8) / 8");
     bg::W8A8Plan p{};
     p.mfma = BG_MFMA_I32_32X32X32_I8;
-    choose_w8a8_pipe(p, M, N);  // the same tile and main loop as bg_gemm_w8a8_pow2
+    choose_w8a8_pipe(p, M, N, lda, ldw);  // the same tile and main loop as bg_gemm_w8a8_pow2
     p.free_epilogue = true;
     if (!tiles_fit(M, N, p.bm, p.bn, 64 * p.waves_m * p.waves_n)) return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
     bg_status st = check_device();

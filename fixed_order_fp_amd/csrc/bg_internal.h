@@ -178,6 +178,12 @@ inline bool pipe_offsets_fit(int64_t bm, int64_t bn, int64_t lda, int64_t ldb)
     const int64_t lim = (int64_t)1 << 32;
     return (bm - 1) * lda * 2 + 128 < lim && (bn - 1) * ldb * 2 + 128 < lim;
 }
+// the same for the two-stage W8A8 tiles (int8 operands: one byte per element)
+inline bool i8_offsets_fit(int64_t bm, int64_t bn, int64_t lda, int64_t ldw)
+{
+    const int64_t lim = (int64_t)1 << 32;
+    return (bm - 1) * lda + 128 < lim && (bn - 1) * ldw + 128 < lim;
+}
 hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                                    const uint16_t* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream);
 

@@ -212,14 +212,18 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
 // outputs written through Y (see the epilogue)
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
-    PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU, PipeOcc<BM, BN, WM, WN, NS, 1>::WAVES_PER_EU)))
+    PipeOcc<BM, BN, WM, WN, NS, 1, NS == 2 ? 128 : 64>::WAVES_PER_EU,
+    PipeOcc<BM, BN, WM, WN, NS, 1, NS == 2 ? 128 : 64>::WAVES_PER_EU)))
 void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* __restrict__ W, int64_t ldw,
                       const float* __restrict__ a_scale, const float* __restrict__ w_scale,
                       uint16_t* __restrict__ Y, int64_t ldy, int32_t* __restrict__ acc_out, int64_t ld_acc,
                       int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, int group_m,
                       const int* __restrict__ ea, const int* __restrict__ eb)
 {
-    constexpr int PK = 64, PCPR = PK / kChunk, KS = PK / 32;  // k tile, chunks per row, k-steps
+    // k tile (bytes), chunks per row, k-steps: 64-byte tiles in a ring of
+    // three or more stages, or 128-byte tiles (whole 128-byte lines per copy)
+    // in two stages
+    constexpr int PK = NS == 2 ? 128 : 64, PCPR = PK / kChunk, KS = PK / 32;
     constexpr int NW = WM * WN, NT = 64 * NW;
     constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int A_CH = BM * PCPR, B_CH = BN * PCPR;
@@ -227,11 +231,12 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
     constexpr int SLOTS = STAGE / 64, ROUNDS = (SLOTS + NW - 1) / NW, EXTRA = SLOTS % NW;
     constexpr int LOADS_HI = ROUNDS, LOADS_LO = EXTRA ? ROUNDS - 1 : ROUNDS;
     constexpr int CHR = BN / 8;
-    constexpr int LDS_BYTES = PipeLds<BM, BN, NS, 1>::BYTES;
+    constexpr int LDS_BYTES = PipeLds<BM, BN, NS, 1, PK>::BYTES;
     static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "tile rows must fill whole copy slots");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole MFMA blocks");
-    static_assert(NS >= 3 && LOADS_HI * (NS - 2) < 64, "stages: three at least, waits within vmcnt");
-    static_assert(KS == 2, "two k-steps per turn");
+    static_assert(NS == 2 || (NS >= 3 && LOADS_HI * (NS - 2) < 64), "stages: three at least, waits within vmcnt");
+    static_assert(NS == 2 || KS == 2, "two k-steps per turn");
+    static_assert(NS != 2 || (EXTRA == 0 && ROUNDS < 64), "128-byte tiles: equal copy rounds");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
     __shared__ u32x4 lds[LDS_BYTES / 16];
 
@@ -247,60 +252,17 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
     const int n_turns = (int)((K + PK - 1) / PK);
     const bool hi = EXTRA == 0 || wave < EXTRA;
 
-    const int8_t* rows[ROUNDS];
-    int kcs[ROUNDS];
-#pragma unroll
-    for (int r = 0; r < ROUNDS; r++) {
-        const int s = r * NW + wave;
-        const int c = (s < SLOTS ? s : 0) * 64 + lane;
-        const bool is_a = c < A_CH;
-        const int row = is_a ? c / PCPR : (c - A_CH) / PCPR;
-        kcs[r] = (c % PCPR) ^ ((row >> 2) & 3);
-        int64_t g = (is_a ? m0 : n0) + row;
-        const int64_t lim = is_a ? M : N;
-        g = g < lim ? g : lim - 1;  // rows past M or N read a clamped row: never stored
-        rows[r] = is_a ? A + g * lda : W + g * ldw;
-    }
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)lds);
-
-    // round r of this wave's copies of a whole k tile `turn` (the last
-    // round's slots past the stage's end belong to no wave)
-    auto copy_round = [&](int turn, int r) {
-        const int s = r * NW + wave;
-        if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS)
-            dma16(rows[r] + (int64_t)turn * PK + kcs[r] * kChunk,
-                  lds_base + (uint32_t)((turn % NS) * STAGE + s * 64) * 16u);
-    };
-    auto issue = [&](int turn) {
-        const int st = turn % NS;
-        const int64_t kb = (int64_t)turn * PK;
-#pragma unroll
-        for (int r = 0; r < ROUNDS; r++) {
-            const int s = r * NW + wave;
-            if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS) {
-                if (turn < n_full)
-                    copy_round(turn, r);
-                else
-                    lds[st * STAGE + s * 64 + lane] = load_chunk_i8(rows[r], kb + kcs[r] * kChunk, K);
-            }
-        }
-    };
-    auto dma_newer = [&](int after, int last) {
-        const int l = last < n_full - 1 ? last : n_full - 1;
-        return l > after ? l - after : 0;
-    };
-    auto wait_newer = [&](int newer, auto max_tag) {
-        constexpr int MAXN = decltype(max_tag)::value;
-        if (hi) wait_turns<LOADS_HI, MAXN>(newer);
-        else wait_turns<LOADS_LO, MAXN>(newer);
-    };
-
+    // position of logical 16-byte chunk kc in the LDS row `row`: rows of 64
+    // bytes swizzled by (row >> 2) & 3, rows of 128 bytes by (row >> 1) & 7
+    // (the operand reads of 16 consecutive rows hit 16 distinct bank groups)
+    auto kswz = [](int kc, int row) { return PCPR == 4 ? kc ^ ((row >> 2) & 3) : kc ^ ((row >> 1) & 7); };
     const int r_in = lane & 31, h = lane >> 5;
     int a_off[KS], b_off[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
-        a_off[ks] = (wm * WTM + r_in) * PCPR + ((2 * ks + h) ^ ((r_in >> 2) & 3));
-        b_off[ks] = A_CH + (wn * WTN + r_in) * PCPR + ((2 * ks + h) ^ ((r_in >> 2) & 3));
+        a_off[ks] = (wm * WTM + r_in) * PCPR + kswz(2 * ks + h, r_in);
+        b_off[ks] = A_CH + (wn * WTN + r_in) * PCPR + kswz(2 * ks + h, r_in);
     }
     auto rd = [&](int turn, int ks, i32x4* a, i32x4* b) {
         const u32x4* base = lds + (turn % NS) * STAGE;
@@ -323,64 +285,191 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
             for (int i = 0; i < TM; i++)
                 acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j][i], 0, 0, 0);
     };
-    // the same products with this wave's copies of a whole k tile `turn`
-    // spread evenly among them (after instruction q of TM TN, the first
-    // ROUNDS q / (TM TN) rounds are out) instead of issued in one burst
-    auto mm_issue = [&](const i32x4* a, const i32x4* b, int turn) {
-        int q = 0, r = 0;
+    if constexpr (NS >= 3) {
+        const int8_t* rows[ROUNDS];
+        int kcs[ROUNDS];
 #pragma unroll
-        for (int j = 0; j < TN; j++)
+        for (int r = 0; r < ROUNDS; r++) {
+            const int s = r * NW + wave;
+            const int c = (s < SLOTS ? s : 0) * 64 + lane;
+            const bool is_a = c < A_CH;
+            const int row = is_a ? c / PCPR : (c - A_CH) / PCPR;
+            kcs[r] = kswz(c % PCPR, row);
+            int64_t g = (is_a ? m0 : n0) + row;
+            const int64_t lim = is_a ? M : N;
+            g = g < lim ? g : lim - 1;  // rows past M or N read a clamped row: never stored
+            rows[r] = is_a ? A + g * lda : W + g * ldw;
+        }
+
+        // round r of this wave's copies of a whole k tile `turn` (the last
+        // round's slots past the stage's end belong to no wave)
+        auto copy_round = [&](int turn, int r) {
+            const int s = r * NW + wave;
+            if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS)
+                dma16(rows[r] + (int64_t)turn * PK + kcs[r] * kChunk,
+                      lds_base + (uint32_t)((turn % NS) * STAGE + s * 64) * 16u);
+        };
+        auto issue = [&](int turn) {
+            const int st = turn % NS;
+            const int64_t kb = (int64_t)turn * PK;
 #pragma unroll
-            for (int i = 0; i < TM; i++) {
-                acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j][i], 0, 0, 0);
-                ++q;
+            for (int r = 0; r < ROUNDS; r++) {
+                const int s = r * NW + wave;
+                if (r + 1 < ROUNDS || EXTRA == 0 || s < SLOTS) {
+                    if (turn < n_full)
+                        copy_round(turn, r);
+                    else
+                        lds[st * STAGE + s * 64 + lane] = load_chunk_i8(rows[r], kb + kcs[r] * kChunk, K);
+                }
+            }
+        };
+        auto dma_newer = [&](int after, int last) {
+            const int l = last < n_full - 1 ? last : n_full - 1;
+            return l > after ? l - after : 0;
+        };
+        auto wait_newer = [&](int newer, auto max_tag) {
+            constexpr int MAXN = decltype(max_tag)::value;
+            if (hi) wait_turns<LOADS_HI, MAXN>(newer);
+            else wait_turns<LOADS_LO, MAXN>(newer);
+        };
+
+        // the same products with this wave's copies of a whole k tile `turn`
+        // spread evenly among them (after instruction q of TM TN, the first
+        // ROUNDS q / (TM TN) rounds are out) instead of issued in one burst
+        auto mm_issue = [&](const i32x4* a, const i32x4* b, int turn) {
+            int q = 0, r = 0;
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+#pragma unroll
+                for (int i = 0; i < TM; i++) {
+                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j][i], 0, 0, 0);
+                    ++q;
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < ROUNDS; u++)
+                        if (r < ROUNDS && r * (TM * TN) < ROUNDS * q - (TM * TN - 1)) copy_round(turn, r++);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        };
+
+#pragma unroll
+        for (int s = 0; s < NS - 1; s++)
+            if (s < n_turns) issue(s);
+        wait_newer(dma_newer(0, NS - 2), std::integral_constant<int, NS - 2>{});
+        __syncthreads();
+
+        i32x4 xa[2][TM], xb[2][TN];
+        rd(0, 0, xa[0], xb[0]);
+        auto turn = [&](int t, auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            rd(t, 1, xa[1], xb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(xa[0], xb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (FULL) {
+                if (hi) wait_vmcnt<LOADS_HI * (NS - 3)>();
+                else wait_vmcnt<LOADS_LO * (NS - 3)>();
+            } else {
+                const int last = t + NS - 2 < n_turns - 1 ? t + NS - 2 : n_turns - 1;
+                wait_newer(dma_newer(t + 1, last), std::integral_constant<int, NS - 3>{});
+            }
+            __builtin_amdgcn_s_barrier();
+            if constexpr (FULL) {
+                rd(t + 1, 0, xa[0], xb[0]);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < ROUNDS; u++)
-                    if (r < ROUNDS && r * (TM * TN) < ROUNDS * q - (TM * TN - 1)) copy_round(turn, r++);
+                mm_issue(xa[1], xb[1], t + NS - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                if (t + NS - 1 < n_turns) issue(t + NS - 1);
+                rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
+                __builtin_amdgcn_sched_barrier(0);
+                mm(xa[1], xb[1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-    };
+        };
+        const int n_steady = n_full - (NS - 1);
+        int t = 0;
+        for (; t < n_steady; t++) turn(t, std::true_type{});
+        for (; t < n_turns; t++) turn(t, std::false_type{});
 
+    } else {
+        // 128-byte k tiles in two stages (as the large bf16 tiles): each
+        // lane's copies are addressed from the tile's first row of A or W (a
+        // scalar base that walks k) by a fixed 32-bit offset (row within the
+        // tile, clamped, times the leading dimension, plus the swizzled
+        // chunk); the copies of tile t+1 go out in one burst at the top of
+        // turn t, and every wave waits for its copies and its LDS reads of
+        // tile t before the turn's barrier.
+        const int8_t* const a_base = A + m0 * lda;
+        const int8_t* const w_base = W + n0 * ldw;
+        uint32_t off[ROUNDS];
 #pragma unroll
-    for (int s = 0; s < NS - 1; s++)
-        if (s < n_turns) issue(s);
-    wait_newer(dma_newer(0, NS - 2), std::integral_constant<int, NS - 2>{});
-    __syncthreads();
-
-    i32x4 xa[2][TM], xb[2][TN];
-    rd(0, 0, xa[0], xb[0]);
-    auto turn = [&](int t, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        rd(t, 1, xa[1], xb[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        mm(xa[0], xb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FULL) {
-            if (hi) wait_vmcnt<LOADS_HI * (NS - 3)>();
-            else wait_vmcnt<LOADS_LO * (NS - 3)>();
-        } else {
-            const int last = t + NS - 2 < n_turns - 1 ? t + NS - 2 : n_turns - 1;
-            wait_newer(dma_newer(t + 1, last), std::integral_constant<int, NS - 3>{});
+        for (int r = 0; r < ROUNDS; r++) {
+            const int c = (r * NW + wave) * 64 + lane;
+            const bool is_a = c < A_CH;
+            const int row = is_a ? c / PCPR : (c - A_CH) / PCPR;
+            const int64_t first = is_a ? m0 : n0, lim = is_a ? M : N;
+            const int64_t g = first + row < lim ? first + row : lim - 1;
+            off[r] = (uint32_t)((g - first) * (is_a ? lda : ldw) + kswz(c % PCPR, row) * kChunk);
         }
-        __builtin_amdgcn_s_barrier();
-        if constexpr (FULL) {
-            rd(t + 1, 0, xa[0], xb[0]);
+        auto slot_base = [&](int s) { return s * 64 < A_CH ? a_base : w_base; };
+        auto issue_full = [&](int turn) {
+#pragma unroll
+            for (int r = 0; r < ROUNDS; r++) {
+                const int s = r * NW + wave;
+                dma16_off(slot_base(s) + (int64_t)turn * PK, off[r],
+                          lds_base + (uint32_t)((turn % NS) * STAGE + s * 64) * 16u);
+            }
+        };
+        // the short last tile (K not a multiple of 128) through registers,
+        // zeros past K
+        auto issue_short = [&](int turn) {
+#pragma unroll
+            for (int r = 0; r < ROUNDS; r++) {
+                const int s = r * NW + wave;
+                const int c = s * 64 + lane;
+                const int row = c < A_CH ? c / PCPR : (c - A_CH) / PCPR;
+                const int kc = kswz(c % PCPR, row);
+                lds[(turn % NS) * STAGE + s * 64 + lane] =
+                    load_chunk_i8(slot_base(s) + off[r] - kc * kChunk, (int64_t)turn * PK + kc * kChunk, K);
+            }
+        };
+        if (n_full > 0) issue_full(0);
+        else if (n_turns > 0) issue_short(0);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __syncthreads();
+        i32x4 xa[2][TM], xb[2][TN];
+        rd(0, 0, xa[0], xb[0]);
+        // NEXT: 0 tile t is the last, 1 tile t+1 is whole, 2 it is the short
+        // last one
+        auto turn = [&](int t, auto next_tag) {
+            constexpr int NEXT = decltype(next_tag)::value;
+            if constexpr (NEXT == 1) issue_full(t + 1);
+            if constexpr (NEXT == 2) issue_short(t + 1);
             __builtin_amdgcn_sched_barrier(0);
-            mm_issue(xa[1], xb[1], t + NS - 1);
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ks++) {
+                rd(t, ks + 1, xa[(ks + 1) & 1], xb[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mm(xa[ks & 1], xb[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (NEXT != 0) {
+                wait_vmcnt<0>();
+                wait_lgkmcnt0();
+                __builtin_amdgcn_s_barrier();
+                rd(t + 1, 0, xa[0], xb[0]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mm(xa[(KS - 1) & 1], xb[(KS - 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-        } else {
-            if (t + NS - 1 < n_turns) issue(t + NS - 1);
-            rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
-            __builtin_amdgcn_sched_barrier(0);
-            mm(xa[1], xb[1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    const int n_steady = n_full - (NS - 1);
-    int t = 0;
-    for (; t < n_steady; t++) turn(t, std::true_type{});
-    for (; t < n_turns; t++) turn(t, std::false_type{});
+        };
+        int t = 0;
+        for (; t + 1 < n_full; t++) turn(t, std::integral_constant<int, 1>{});
+        if (t + 1 < n_turns) turn(t++, std::integral_constant<int, 2>{});
+        if (t < n_turns) turn(t, std::integral_constant<int, 0>{});
+    }
 
     // epilogue: block (j, i), element 4q+u of lane l is row m = wm*WTM + 32i +
     // l%32, column n = wn*WTN + 32j + 8q + 4(l/32) + u
@@ -504,6 +593,7 @@ hipError_t launch_pipe(const W8A8Plan& p, int64_t M, int64_t N, int64_t K, const
                        const int8_t* W, int64_t ldw, const float* a_scale, const float* w_scale, uint16_t* Y,
                        int64_t ldy, int32_t* acc_out, int64_t ld_acc, hipStream_t stream)
 {
+    if (NS == 2 && !i8_offsets_fit(BM, BN, lda, ldw)) return hipErrorInvalidValue;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
     dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);
@@ -550,6 +640,9 @@ using namespace w8a8_impl;
 // (instruction, BM, BN, waves_m, waves_n, load path: 1 direct-to-LDS double
 // buffer, 2 pipelined, LDS stages of the pipelined path)
 #define BG_W8A8_TILES(X)                             \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 192, 4, 2, 2, 2) \
+    X(BG_MFMA_I32_32X32X32_I8, 256, 256, 2, 4, 2, 2) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 2) \
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 4) \
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 5) \
     X(BG_MFMA_I32_32X32X32_I8, 256, 256, 2, 4, 2, 4) \
@@ -608,9 +701,9 @@ struct W8A8Launcher<2> {
 // The pipelined tiles built with the Ozaki recombination epilogue (the ones
 // the library picks for the stacked product): BM, BN, waves_m, waves_n, stages.
 #define BG_OZAKI_TILES(X) \
-    X(256, 256, 2, 4, 4)  \
-    X(128, 192, 4, 2, 5)  \
-    X(128, 128, 2, 2, 5)  \
+    X(256, 256, 2, 4, 2)  \
+    X(128, 192, 4, 2, 2)  \
+    X(128, 128, 2, 2, 2)  \
     X(64, 64, 2, 2, 8)
 
 template <int BM, int BN, int WM, int WN, int NS>
@@ -618,6 +711,7 @@ hipError_t launch_pipe_ozaki(const W8A8Plan& p, int64_t M4, int64_t N4, int64_t 
                              const int8_t* qb, const int* ea, const int* eb, bool out_bf16, void* C, int64_t ldc,
                              hipStream_t stream)
 {
+    if (NS == 2 && !i8_offsets_fit(BM, BN, Kp, Kp)) return hipErrorInvalidValue;
     const int tiles_m = (int)((M4 + BM - 1) / BM), tiles_n = (int)((N4 + BN - 1) / BN);
     const int group_m = p.group_m > 0 ? p.group_m : tiles_m;
     dim3 grid((unsigned)(tiles_m * tiles_n)), block(64 * WM * WN);

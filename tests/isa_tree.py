@@ -231,9 +231,10 @@ def w8a8_variants(asm):
     out = []
     for name, lines in kernels(asm).items():
         t = template_ints(name)
-        if "w8a8_pipe_kernel" in name:               # <BM, BN, WM, WN, NS, MODE>, k tiles of 64 bytes
-            bm, bn, wm, wn = t[0], t[1], t[2], t[3]
-            out.append((name, lines, 2, 64 // INSTR_K[2], (bm // wm // 32) * (bn // wn // 32)))
+        if "w8a8_pipe_kernel" in name:               # <BM, BN, WM, WN, NS, MODE>: k tiles of 64 bytes, 128 at NS 2
+            bm, bn, wm, wn, ns = t[0], t[1], t[2], t[3], t[4]
+            pk = 128 if ns == 2 else 64
+            out.append((name, lines, 2, pk // INSTR_K[2], (bm // wm // 32) * (bn // wn // 32)))
         elif "w8a8_kernel" in name:                  # <INSTR, BM, BN, WM, WN, ACC_OUT>, k tiles of 128 bytes
             i, bm, bn, wm, wn = t[0], t[1], t[2], t[3], t[4]
             e = BLOCK[i]
