@@ -367,12 +367,14 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N, int64_t lda, int64_
         else deep ? set(256, 320, 64, 4, 2, 2, 2) : set(256, 320, 32, 4, 2, 2, 4);
         return;
     }
+    // small M: each CU streams its strip of W from HBM; 64-deep k tiles
+    // (whole 128-byte lines per copy) in a ring of six stages
     if (M <= 32) {  // 304 workgroups of 32x64 stream W faster than 152 of 64x64
-        set(32, 64, 32, 1, 2, 2, 8);
+        set(32, 64, 64, 1, 2, 2, 6);
         return;
     }
     if (M <= 64) {
-        set(64, 64, 32, 2, 2, 2, 8);
+        set(64, 64, 64, 2, 2, 2, 6);
         return;
     }
     if (p.S > 1) {
@@ -387,28 +389,31 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N, int64_t lda, int64_
         }
     }
     // deep splits: the tile whose busiest CU finishes first.  Each CU moves
-    // operands at ~38 GB/s and multiplies at ~8.1 TFLOP/s (both measured on
-    // these kernels, at the clock they settle at), so a tile costs rounds of
-    // workgroups x max(copy time, MFMA time) of one workgroup over the
-    // deepest split.  Shallow splits: small tiles (their prologue and
-    // epilogue weigh less).
+    // operands at ~38 GB/s with 32-deep k tiles (64-byte row pieces) and
+    // ~50 GB/s with 64-deep ones (whole 128-byte lines), and multiplies at
+    // ~8.1 TFLOP/s (all measured on these kernels, at the clock they settle
+    // at), so a tile costs rounds of workgroups x max(copy time, MFMA time)
+    // of one workgroup over the deepest split.  Shallow splits: small tiles
+    // (their prologue and epilogue weigh less).
     auto wgs = [&](int64_t bm, int64_t bn) { return ceil_div(M, bm) * ceil_div(N, bn) * p.S; };
     const int64_t turns = p.cuts.c[1] / 32;
     if (turns >= 64) {
-        struct Cand { int bm, bn, wm, wn, ns; };
-        static const Cand cands[] = {{320, 256, 2, 4, 4}, {256, 256, 2, 4, 4}, {192, 256, 2, 4, 4}, {256, 128, 2, 2, 4},
-                                     {192, 128, 2, 2, 4}, {128, 128, 2, 2, 5}, {128, 64, 2, 2, 8}, {64, 64, 2, 2, 8}};
+        struct Cand { int bm, bn, bk, wm, wn, ns; };
+        static const Cand cands[] = {{320, 256, 32, 2, 4, 4}, {256, 256, 32, 2, 4, 4}, {192, 256, 32, 2, 4, 4},
+                                     {256, 128, 32, 2, 2, 4}, {192, 128, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 5},
+                                     {128, 64, 32, 2, 2, 8},  {64, 64, 32, 2, 2, 8},   {128, 128, 64, 2, 2, 4},
+                                     {128, 64, 64, 2, 2, 4},  {64, 64, 64, 2, 2, 6}};
         int64_t kmax = 0;
         for (int s = 0; s < p.S; s++) kmax = std::max<int64_t>(kmax, p.cuts.c[s + 1] - p.cuts.c[s]);
         const Cand* pick = nullptr;
         double best = 0.0;
         for (const Cand& c : cands) {
-            const double copy = (double)(c.bm + c.bn) * (double)kmax * 2.0 / 38e9;
+            const double copy = (double)(c.bm + c.bn) * (double)kmax * 2.0 / (c.bk == 64 ? 50e9 : 38e9);
             const double mfma = (double)c.bm * c.bn * (double)kmax * 2.0 / 8.1e12;
             const double t = (double)ceil_div(wgs(c.bm, c.bn), n_cu) * std::max(copy, mfma);
             if (!pick || t < best) pick = &c, best = t;
         }
-        set(pick->bm, pick->bn, 32, pick->wm, pick->wn, 2, pick->ns);
+        set(pick->bm, pick->bn, pick->bk, pick->wm, pick->wn, 2, pick->ns);
         return;
     }
     if (wgs(64, 64) <= 2048) set(64, 64, 32, 2, 2, 2, 8);

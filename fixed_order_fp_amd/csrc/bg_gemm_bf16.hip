@@ -416,8 +416,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 // operands are read and tile t's last k-step is multiplied.  Measured 10 %
 // faster than the 32-deep ring on the large-output tiles (8 waves, two
 // rounds of workgroups or more), bit-identical; on the mid-size tiles (4
-// waves, one round) the single tile in flight made it 10-90 % slower, so
-// those keep the 32-deep ring.
+// waves, one round) the single tile in flight made it 10-90 % slower.
+// Those, and the small tiles, take 64-deep k tiles in a ring of four or
+// more stages instead (the same ring as the 32-deep one, four k-steps per
+// turn): 8-29 % faster on the small-M and split-K products, where each CU
+// streams its operands from HBM; a ring of three measured slower.
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32
 // split partial added into C with atomics (the free-order twin only)
@@ -449,9 +452,8 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
     static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "tile rows must fill whole copy slots");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole MFMA blocks");
     static_assert(BK == 32 || BK == 64, "k tiles of 32 or 64");
-    static_assert(BK != 32 || (NS >= 3 && LOADS_HI * (NS - 2) < 64), "stages: three at least, waits within vmcnt");
-    static_assert(BK != 32 || KS == 2, "two k-steps per turn: the fragment buffers alternate within a turn");
-    static_assert(BK != 64 || (NS == 2 && EXTRA == 0 && ROUNDS < 64), "64-deep tiles: two stages, equal copy rounds");
+    static_assert(NS == 2 || (NS >= 3 && LOADS_HI * (NS - 2) < 64), "a ring of three stages at least, waits within vmcnt");
+    static_assert(NS != 2 || (BK == 64 && EXTRA == 0 && ROUNDS < 64), "two stages: 64-deep tiles, equal copy rounds");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
 
     const int tid = threadIdx.x;
@@ -505,7 +507,7 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
             for (int i = 0; i < TM; i++)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
     };
-    if constexpr (BK == 32) {
+    if constexpr (NS >= 3) {
         // the chunk this lane copies in round r: stage chunk c = 64 s + lane (A
         // rows first, then B rows), global (row, logical chunk kc) under the swizzle
         const uint16_t* src[ROUNDS];
@@ -597,11 +599,15 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
         // count LDS reads across the back edge)
         auto turn = [&](int t, auto full_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
-            // k-step 0: read the operands of k-step 1, multiply k-step 0
-            rd(t, 1, xa[1], xb[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mm(xa[0], xb[0]);
-            __builtin_amdgcn_sched_barrier(0);
+            // k-steps 0 .. KS-2: read the operands of the next k-step,
+            // multiply this one (the fragment buffers alternate)
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ks++) {
+                rd(t, ks + 1, xa[(ks + 1) & 1], xb[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mm(xa[ks & 1], xb[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             // tile t+1 must have landed in every wave's share before its first read
             if constexpr (FULL) {
                 if (hi) wait_vmcnt<LOADS_HI * (NS - 3)>();
@@ -1163,6 +1169,10 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
 #define BG_GEMM_TILES(X)                                            \
     X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 64, 2, 4, 2, 2)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 64, 4, 2, 2, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 2, 4)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 128, 64, 64, 2, 2, 2, 4)           \
+    X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2, 2, 6)            \
+    X(BG_MFMA_F32_32X32X16_BF16, 32, 64, 64, 1, 2, 2, 6)            \
     X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 32, 2, 4, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 32, 4, 2, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 256, 32, 2, 2, 2, 4)          \
