@@ -401,8 +401,8 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N, int64_t lda, int64_
         struct Cand { int bm, bn, bk, wm, wn, ns; };
         static const Cand cands[] = {{320, 256, 32, 2, 4, 4}, {256, 256, 32, 2, 4, 4}, {192, 256, 32, 2, 4, 4},
                                      {256, 128, 32, 2, 2, 4}, {192, 128, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 5},
-                                     {128, 64, 32, 2, 2, 8},  {64, 64, 32, 2, 2, 8},   {128, 128, 64, 2, 2, 4},
-                                     {128, 64, 64, 2, 2, 4},  {64, 64, 64, 2, 2, 6}};
+                                     {128, 64, 32, 2, 2, 8},  {64, 64, 32, 2, 2, 8},   {192, 128, 64, 2, 2, 4},
+                                     {128, 128, 64, 2, 2, 4}, {128, 64, 64, 2, 2, 4},  {64, 64, 64, 2, 2, 6}};
         int64_t kmax = 0;
         for (int s = 0; s < p.S; s++) kmax = std::max<int64_t>(kmax, p.cuts.c[s + 1] - p.cuts.c[s]);
         const Cand* pick = nullptr;

@@ -1169,6 +1169,7 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
 #define BG_GEMM_TILES(X)                                            \
     X(BG_MFMA_F32_32X32X16_BF16, 320, 256, 64, 2, 4, 2, 2)          \
     X(BG_MFMA_F32_32X32X16_BF16, 256, 320, 64, 4, 2, 2, 2)          \
+    X(BG_MFMA_F32_32X32X16_BF16, 192, 128, 64, 2, 2, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 128, 128, 64, 2, 2, 2, 4)          \
     X(BG_MFMA_F32_32X32X16_BF16, 128, 64, 64, 2, 2, 2, 4)           \
     X(BG_MFMA_F32_32X32X16_BF16, 64, 64, 64, 2, 2, 2, 6)            \

@@ -15,6 +15,7 @@ INSTRS = ["F32_32X32X16_BF16", "F32_16X16X32_BF16"]
 SCHEDULES = {
     "F32_32X32X16_BF16": [dict(bm=320, bn=256, bk=64, waves_m=2, waves_n=4, load_path=2),
                           dict(bm=256, bn=320, bk=64, waves_m=4, waves_n=2, load_path=2, group_m=3),
+                          dict(bm=192, bn=128, bk=64, waves_m=2, waves_n=2, load_path=2, stages=4),
                           dict(bm=128, bn=128, bk=64, waves_m=2, waves_n=2, load_path=2, stages=4),
                           dict(bm=128, bn=64, bk=64, waves_m=2, waves_n=2, load_path=2, stages=4),
                           dict(bm=64, bn=64, bk=64, waves_m=2, waves_n=2, load_path=2, stages=6),
