@@ -170,9 +170,11 @@ def host_cost(head, torch, bg, n=100, reps=5):
 
 def plan_note(bg, g):
     """The tiles the library picked for a workload (its own plan query), as
-    text: BMxBN/waves/stages, and the last split's own tile where it has one."""
+    text: BMxBN, waves, k tile depth, stages, and the last split's own tile
+    where it has one."""
     p = bg.gemm_bf16_plan(g.desc, g.M, g.N, g.K)
-    s = f"{p['bm']}x{p['bn']} tile, {p['waves_m']}x{p['waves_n']} waves, {p['stages']} stages"
+    s = (f"{p['bm']}x{p['bn']} tile, {p['waves_m']}x{p['waves_n']} waves, k tiles of {p['bk']}, "
+         f"{p['stages']} stages")
     if p["last_bm"]:
         s += (f"; last split {p['last_bm']}x{p['last_bn']} tile, {p['last_waves_m']}x{p['last_waves_n']} waves, "
               f"{p['last_stages']} stages")

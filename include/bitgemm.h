@@ -103,13 +103,19 @@ typedef struct {
     int32_t waves_m, waves_n; /* wave grid inside a workgroup              */
     int32_t load_path;        /* 0: global -> VGPR -> LDS; 1: global -> LDS;
                                  2: global -> LDS, multi-stage pipeline (k
-                                 tiles of 32; 32x32x16 instruction only)   */
+                                 tiles of 32 or 64; 32x32x16 instruction
+                                 only; 64-deep tiles in two stages address
+                                 their copies by 32-bit offsets and need
+                                 (bm - 1) x lda and (bn - 1) x ldb below
+                                 2^31 elements)                            */
     int32_t group_m;          /* tile rows per group of the workgroup walk
                                  (0 = 8; for path 2, the height that makes
                                  each XCD's concurrent tiles fetch the
                                  fewest A and B rows)                      */
     int32_t stages;           /* k tiles held in LDS by path 2 (0 = the
-                                 tile's default)                           */
+                                 tile's default); for W8A8 on path 2, two
+                                 stages take 128-byte k tiles, three or
+                                 more 64-byte ones                         */
     int32_t last_bm, last_bn; /* path 2 with split_k > 1: the last split
                                  (the cut rule's remainder, the deepest)
                                  takes this tile in the same launch; all
