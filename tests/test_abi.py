@@ -344,7 +344,7 @@ def test_every_planned_schedule_is_compiled(bg):
     library's choice is always a compiled tile or pair: fed back as an
     explicit schedule it is accepted and planned identically."""
     n = 0
-    for M in (65, 100, 256, 300, 1000, 4000):
+    for M in (1, 8, 32, 64, 65, 100, 256, 300, 1000, 4000):
         for N in (64, 500, 2560, 9728):
             for K in (2048, 9728, 20000):
                 for S in (1, 2, 3, 4, 5, 8, 16, 32):
@@ -355,3 +355,30 @@ def test_every_planned_schedule_is_compiled(bg):
                     assert bg.gemm_bf16_plan(bg.gemm_desc(dict(spec, schedule=p)), M, N, K) == p, (M, N, K, S, p)
                     n += p["last_bm"] > 0
     assert n > 0  # some of them take a pair of tiles
+
+
+def test_copy_offset_limit(bg):
+    """The 64-deep two-stage tiles address their copies by 32-bit byte
+    offsets from the tile's first row: an explicit schedule whose
+    (bm - 1) x lda x 2 bytes reaches 2^32 is refused before any launch
+    (bf16, and the W8A8 two-stage tiles with one byte per element), and the
+    library's own choice falls back to the 32-deep ring there."""
+    p = 0x10000  # never dereferenced
+    big = 7_000_000  # 319 x 7e6 x 2 bytes > 2^32; a multiple of 16
+    d = bg.gemm_desc({"schedule": {"bm": 320, "bn": 256, "bk": 64, "waves_m": 2, "waves_n": 4, "load_path": 2,
+                                   "stages": 2}})
+    st = bg.lib().bg_gemm_bf16(C.byref(d), 4000, 9728, 2560, p, big, p, 2560, p, 9728, None, 0, None)
+    assert st == 2 and "32-bit offsets" in bg.lib().bg_last_error().decode()
+    st = bg.lib().bg_gemm_bf16(C.byref(d), 4000, 9728, 2560, p, 2560, p, 9_000_000, p, 9728, None, 0, None)
+    assert st == 2 and "32-bit offsets" in bg.lib().bg_last_error().decode()  # 255 x 9e6 x 2 > 2^32
+    # the chooser: contiguous operands of a huge K take the 32-deep tile, of
+    # the headline's K the 64-deep one
+    free = bg.gemm_desc({"out_type": "bf16"})
+    assert bg.gemm_bf16_plan(free, 4000, 9728, big)["bk"] == 32
+    assert bg.gemm_bf16_plan(free, 4000, 9728, 2560)["bk"] == 64
+    w = bg.gemm_desc(dict(mfma="I32_32X32X32_I8", a_type="int8", b_type="int8", acc_type="int32", out_type="bf16",
+                          epilogue="W8A8_POW2", schedule={"bm": 256, "bn": 256, "waves_m": 2, "waves_n": 4,
+                                                          "load_path": 2, "stages": 2}))
+    huge = 20_000_000  # 255 x 2e7 bytes > 2^32
+    st = bg.lib().bg_gemm_w8a8_pow2(C.byref(w), 1024, 1024, 2048, p, huge, p, 2048, p, p, p, 1024, None, 0, None)
+    assert st == 2 and "32-bit offsets" in bg.lib().bg_last_error().decode()
