@@ -345,6 +345,9 @@ def test_two_rounds_of_large_tiles_match_one_round_tiles():
     walk = run_gemm({"schedule": dict(bm=320, bn=256, bk=32, waves_m=2, waves_n=4, load_path=2)}, A, B, out="bf16")
     one = run_gemm({"schedule": dict(bm=256, bn=128, bk=32, waves_m=2, waves_n=2, load_path=2)}, A, B, out="bf16")
     assert np.array_equal(walk, one)
+    # the same two rounds on 64-deep k tiles in two stages (1000 = 15 x 64 + 40: a short last tile)
+    deep = run_gemm({"schedule": dict(bm=320, bn=256, bk=64, waves_m=2, waves_n=4, load_path=2)}, A, B, out="bf16")
+    assert np.array_equal(deep, one)
     rng = np.random.default_rng(61)
     mi = rng.integers(0, 3000, 96)
     ni = rng.integers(0, 8000, 96)
@@ -383,3 +386,36 @@ def test_one_json_record_drives_both_sides(text):
     got = dC.cpu().numpy().view(np.uint32 if out == "fp32" else np.uint16)
     ref = oracle.gemm_bf16(spec, A, B)
     assert np.array_equal(got, ref.view(np.uint32 if out == "fp32" else np.uint16))
+
+
+def test_64_deep_tiles_on_sliced_views():
+    """The 64-deep tiles address their copies from each tile's first row by
+    byte offsets that carry the leading dimension: operands that are column
+    slices of wider buffers (lda, ldb > K), ragged M, N and K, every output
+    against the oracle, for the two-stage tile and the four- and six-stage
+    rings."""
+    import torch
+    import fixed_order_fp_amd as bg
+    import oracle
+    M, N, K = 700, 600, 1000
+    A = synth.bf16_spread(71, (M, K), -20, 20)
+    B = synth.bf16_spread(72, (N, K), -20, 20)
+    ref = oracle.gemm_bf16(oracle_desc({"out_type": "bf16"}, "F32_32X32X16_BF16"), A, B)
+    bufA = torch.zeros((M, K + 96), dtype=torch.int16, device="cuda")
+    bufB = torch.zeros((N, K + 160), dtype=torch.int16, device="cuda")
+    bufA[:, :K] = torch.from_numpy(A.view(np.int16)).cuda()
+    bufB[:, :K] = torch.from_numpy(B.view(np.int16)).cuda()
+    bufA[:, K:] = 0x7F80  # +inf past K: would show if a copy read beyond the row
+    bufB[:, K:] = 0x7F80
+    for sched in (dict(bm=320, bn=256, bk=64, waves_m=2, waves_n=4, load_path=2, stages=2),
+                  dict(bm=256, bn=320, bk=64, waves_m=4, waves_n=2, load_path=2, stages=2),
+                  dict(bm=192, bn=128, bk=64, waves_m=2, waves_n=2, load_path=2, stages=4),
+                  dict(bm=64, bn=64, bk=64, waves_m=2, waves_n=2, load_path=2, stages=6),
+                  dict(bm=32, bn=64, bk=64, waves_m=1, waves_n=2, load_path=2, stages=6)):
+        print_case("64-deep tiles on sliced views", sched)
+        d = bg.gemm_desc({"out_type": "bf16", "schedule": sched})
+        dC = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        bg.gemm_bf16(d, bufA[:, :K], bufB[:, :K], dC, None)
+        torch.cuda.synchronize()
+        got = dC.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref), sched
