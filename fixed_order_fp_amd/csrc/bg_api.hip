@@ -211,20 +211,26 @@ void choose_w8a8_pipe(bg::W8A8Plan& p, int64_t M, int64_t N, int64_t lda, int64_
 // each run that much slower.  The constants were fitted to the split sweep of
 // that product (S = 2 .. 16, the tiles and pairs below); the model ranks
 // tiles, it does not predict times.
+// The 64-deep tiles' per-turn costs (per 32 of k) come from the same sweep
+// where it was measured (64x64, 128x64, 128x128 at S = 1, 2, 4) and are
+// scaled from the 32-deep ones by the measured ratio elsewhere (0.87).
 struct PipeTileCost {
-    int bm, bn, wm, wn, ns;
+    int bm, bn, bk, wm, wn, ns;
     double turn_us;
 };
 const PipeTileCost kPipeCosts[] = {
-    {256, 256, 2, 4, 4, 0.858}, {256, 256, 2, 2, 4, 0.900}, {192, 256, 2, 4, 4, 0.613}, {256, 128, 2, 2, 4, 0.510},
-    {192, 128, 2, 2, 4, 0.407}, {128, 128, 2, 2, 4, 0.333}, {128, 128, 2, 2, 8, 0.327}, {128, 64, 2, 2, 4, 0.293},
-    {128, 64, 2, 2, 8, 0.259},  {64, 128, 2, 2, 4, 0.293},  {64, 128, 2, 2, 8, 0.267},  {64, 64, 2, 2, 8, 0.189},
-    {128, 64, 4, 2, 8, 0.259},  {64, 128, 2, 4, 8, 0.267}};
+    {256, 256, 32, 2, 4, 4, 0.858}, {256, 256, 32, 2, 2, 4, 0.900}, {192, 256, 32, 2, 4, 4, 0.613},
+    {256, 128, 32, 2, 2, 4, 0.510}, {192, 128, 32, 2, 2, 4, 0.407}, {128, 128, 32, 2, 2, 4, 0.333},
+    {128, 128, 32, 2, 2, 8, 0.327}, {128, 64, 32, 2, 2, 4, 0.293},  {128, 64, 32, 2, 2, 8, 0.259},
+    {64, 128, 32, 2, 2, 4, 0.293},  {64, 128, 32, 2, 2, 8, 0.267},  {64, 64, 32, 2, 2, 8, 0.189},
+    {128, 64, 32, 4, 2, 8, 0.259},  {64, 128, 32, 2, 4, 8, 0.267},  {256, 256, 64, 2, 4, 2, 0.750},
+    {192, 128, 64, 2, 2, 4, 0.354}, {128, 128, 64, 2, 2, 4, 0.319}, {128, 64, 64, 2, 2, 4, 0.220},
+    {128, 64, 64, 4, 2, 4, 0.220},  {64, 64, 64, 2, 2, 6, 0.148}};
 
-const PipeTileCost* pipe_cost(int bm, int bn, int wm, int wn, int ns)
+const PipeTileCost* pipe_cost(int bm, int bn, int bk, int wm, int wn, int ns)
 {
     for (const PipeTileCost& c : kPipeCosts)
-        if (c.bm == bm && c.bn == bn && c.wm == wm && c.wn == wn && c.ns == ns) return &c;
+        if (c.bm == bm && c.bn == bn && c.bk == bk && c.wm == wm && c.wn == wn && c.ns == ns) return &c;
     return nullptr;
 }
 
@@ -233,7 +239,7 @@ double wg_us(const PipeTileCost& c, int64_t turns)
     return 0.5 + (double)(turns + c.ns) * c.turn_us + (double)c.bm * c.bn * 4.0 / 30e3;
 }
 
-int pipe_lds_bytes(const PipeTileCost& c) { return c.ns * (c.bm + c.bn) * 64; }
+int pipe_lds_bytes(const PipeTileCost& c) { return c.ns * (c.bm + c.bn) * c.bk * 2; }
 
 // Longest-first list schedule of two kinds of workgroups on n_cu slots, one
 // at a time per slot: the longer kind is dealt out first (some slots take
@@ -278,18 +284,21 @@ double lpt2(int64_t na, double ta, int64_t nb, double tb, int64_t n_cu, int lds)
 }
 
 struct DualPair {
-    int bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2;
+    int bk, bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2;
 };
-// must list exactly the pairs bg_gemm_bf16.hip compiles in
-const DualPair kDualPairs[] = {{256, 256, 2, 2, 4, 64, 64, 2, 2, 8},  {256, 256, 2, 2, 4, 128, 64, 2, 2, 4},
-                               {256, 128, 2, 2, 4, 64, 64, 2, 2, 8},  {192, 128, 2, 2, 4, 64, 64, 2, 2, 8},
-                               {128, 128, 2, 2, 4, 64, 64, 2, 2, 8},  {256, 256, 2, 4, 4, 128, 64, 4, 2, 8},
-                               {256, 256, 2, 4, 4, 64, 128, 2, 4, 8}};
+// must list exactly the pairs bg_gemm_bf16.hip compiles in; on a tie of the
+// model below the earlier pair wins (128x128 + 128x64 on 64-deep tiles
+// measured 6 % ahead of 128x128 + 64x64 at S = 8, which the model ties)
+const DualPair kDualPairs[] = {{32, 256, 256, 2, 2, 4, 64, 64, 2, 2, 8}, {32, 256, 256, 2, 2, 4, 128, 64, 2, 2, 4},
+                               {32, 256, 128, 2, 2, 4, 64, 64, 2, 2, 8}, {32, 192, 128, 2, 2, 4, 64, 64, 2, 2, 8},
+                               {32, 128, 128, 2, 2, 4, 64, 64, 2, 2, 8}, {32, 256, 256, 2, 4, 4, 128, 64, 4, 2, 8},
+                               {32, 256, 256, 2, 4, 4, 64, 128, 2, 4, 8}, {64, 256, 256, 2, 4, 2, 128, 64, 4, 2, 4},
+                               {64, 128, 128, 2, 2, 4, 128, 64, 2, 2, 4}, {64, 128, 128, 2, 2, 4, 64, 64, 2, 2, 6}};
 
 // The split grid's tiles (S > 1): every single tile of the cost table and
 // every compiled (other splits, last split) pair is scored by lpt2 over the
 // splits' depths; the cheapest wins, a single tile on a tie.
-void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
+void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N, int64_t lda, int64_t ldb)
 {
     const int64_t n_cu = device_cus();
     int64_t body = 0;
@@ -302,26 +311,31 @@ void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
     for (const PipeTileCost& c : kPipeCosts) {
         if (c.bm > 64 && M <= 64) continue;
         // some costed shapes exist only as the last split's half of a pair
-        if (!bg::gemm_bf16_has_tile(BG_MFMA_F32_32X32X16_BF16, c.bm, c.bn, 32, c.wm, c.wn, 2, c.ns)) continue;
+        if (!bg::gemm_bf16_has_tile(BG_MFMA_F32_32X32X16_BF16, c.bm, c.bn, c.bk, c.wm, c.wn, 2, c.ns)) continue;
+        if (c.ns == 2 && !bg::pipe_offsets_fit(c.bm, c.bn, lda, ldb)) continue;
         const int64_t n = tiles(c.bm, c.bn);
         const double t = lpt2(n * (p.S - 1), wg_us(c, tb), n, wg_us(c, tl), n_cu, pipe_lds_bytes(c));
         if (!have || t < best) {
             have = true, best = t;
-            p.bm = c.bm, p.bn = c.bn, p.bk = 32, p.waves_m = c.wm, p.waves_n = c.wn, p.direct = 2, p.stages = c.ns;
+            p.bm = c.bm, p.bn = c.bn, p.bk = c.bk, p.waves_m = c.wm, p.waves_n = c.wn, p.direct = 2, p.stages = c.ns;
             p.bm2 = 0, p.bn2 = 0, p.waves_m2 = 0, p.waves_n2 = 0, p.stages2 = 0;
         }
     }
     for (const DualPair& d : kDualPairs) {
-        const PipeTileCost* a = pipe_cost(d.bm, d.bn, d.wm, d.wn, d.ns);
-        const PipeTileCost* b = pipe_cost(d.bm2, d.bn2, d.wm2, d.wn2, d.ns2);
-        if (!a || !b || !bg::gemm_bf16_has_dual_tile(d.bm, d.bn, d.wm, d.wn, d.ns, d.bm2, d.bn2, d.wm2, d.wn2, d.ns2))
+        const PipeTileCost* a = pipe_cost(d.bm, d.bn, d.bk, d.wm, d.wn, d.ns);
+        const PipeTileCost* b = pipe_cost(d.bm2, d.bn2, d.bk, d.wm2, d.wn2, d.ns2);
+        if (!a || !b ||
+            !bg::gemm_bf16_has_dual_tile(d.bm, d.bn, d.bk, d.wm, d.wn, d.ns, d.bm2, d.bn2, d.wm2, d.wn2, d.ns2))
+            continue;
+        if ((d.ns == 2 && !bg::pipe_offsets_fit(d.bm, d.bn, lda, ldb)) ||
+            (d.ns2 == 2 && !bg::pipe_offsets_fit(d.bm2, d.bn2, lda, ldb)))
             continue;
         const double ta = wg_us(*a, tb), tl2 = wg_us(*b, tl);
         const double t = lpt2(tiles(d.bm, d.bn) * (p.S - 1), ta, tiles(d.bm2, d.bn2), tl2, n_cu,
                               std::max(pipe_lds_bytes(*a), pipe_lds_bytes(*b)));
         if (t < best) {
             best = t;
-            p.bm = d.bm, p.bn = d.bn, p.bk = 32, p.waves_m = d.wm, p.waves_n = d.wn, p.direct = 2, p.stages = d.ns;
+            p.bm = d.bm, p.bn = d.bn, p.bk = d.bk, p.waves_m = d.wm, p.waves_n = d.wn, p.direct = 2, p.stages = d.ns;
             p.bm2 = d.bm2, p.bn2 = d.bn2, p.waves_m2 = d.wm2, p.waves_n2 = d.wn2, p.stages2 = d.ns2;
             p.last_first = tl2 >= ta;
         }
@@ -331,8 +345,8 @@ void choose_split_tiles(bg::GemmPlan& p, int64_t M, int64_t N)
 // whether the last split's workgroups go first (the longer kind first)
 bool dual_last_first(const bg::GemmPlan& p)
 {
-    const PipeTileCost* a = pipe_cost(p.bm, p.bn, p.waves_m, p.waves_n, p.stages);
-    const PipeTileCost* b = pipe_cost(p.bm2, p.bn2, p.waves_m2, p.waves_n2, p.stages2);
+    const PipeTileCost* a = pipe_cost(p.bm, p.bn, p.bk, p.waves_m, p.waves_n, p.stages);
+    const PipeTileCost* b = pipe_cost(p.bm2, p.bn2, p.bk, p.waves_m2, p.waves_n2, p.stages2);
     if (!a || !b) return true;
     int64_t body = 0;
     for (int s = 0; s + 1 < p.S; s++) body = std::max<int64_t>(body, p.cuts.c[s + 1] - p.cuts.c[s]);
@@ -384,7 +398,7 @@ void choose_gemm_tile(bg::GemmPlan& p, int64_t M, int64_t N, int64_t lda, int64_
         int64_t body = 0;
         for (int s = 0; s + 1 < p.S; s++) body = std::max<int64_t>(body, p.cuts.c[s + 1] - p.cuts.c[s]);
         if (p.cuts.c[p.S] - p.cuts.c[p.S - 1] >= 2 * body) {
-            choose_split_tiles(p, M, N);
+            choose_split_tiles(p, M, N, lda, ldb);
             return;
         }
     }
@@ -667,29 +681,43 @@ bg_status resolve_gemm_schedule(const bg_gemm_desc* d, int64_t M, int64_t N, int
     const bg_gemm_schedule& s = d->sched;
     p.group_m = s.group_m;
     if (s.bm || s.bn || s.bk || s.waves_m || s.waves_n) {
-        if (!bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path, s.stages))
+        // a pair's other-splits tile need not be compiled on its own (the
+        // pair is checked below)
+        const bool pair = s.last_bm || s.last_bn || s.last_waves_m || s.last_waves_n || s.last_stages;
+        if (!pair && !bg::gemm_bf16_has_tile(p.mfma, s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.load_path, s.stages))
             return fail(BG_E_UNSUPPORTED, "schedule (bm, bn, bk, waves, load_path, stages) is not compiled in");
-        if (s.load_path == 2 && s.bk == 64 && !bg::pipe_offsets_fit(s.bm, s.bn, lda, ldb))
-            return fail(BG_E_UNSUPPORTED, "a 64-deep pipelined tile addresses its copies by 32-bit offsets: "
+        // the two-stage 64-deep tiles (the first compiled entry of their
+        // shapes, so also stages 0) address their copies by 32-bit offsets
+        auto two_stage = [&](int bm, int bn, int wm, int wn, int ns) {
+            return s.load_path == 2 && s.bk == 64 &&
+                   (ns == 2 || (ns == 0 && bg::gemm_bf16_has_tile(p.mfma, bm, bn, 64, wm, wn, 2, 2)));
+        };
+        if (!pair && two_stage(s.bm, s.bn, s.waves_m, s.waves_n, s.stages) &&
+            !bg::pipe_offsets_fit(s.bm, s.bn, lda, ldb))
+            return fail(BG_E_UNSUPPORTED, "a 64-deep two-stage tile addresses its copies by 32-bit offsets: "
                                           "(bm - 1) x lda and (bn - 1) x ldb must stay below 2^31 elements");
         p.bm = s.bm, p.bn = s.bn, p.bk = s.bk, p.waves_m = s.waves_m, p.waves_n = s.waves_n;
         p.direct = s.load_path;
         p.stages = s.stages;
         if (s.last_bm || s.last_bn || s.last_waves_m || s.last_waves_n || s.last_stages) {
             if (p.S < 2) return fail(BG_E_UNSUPPORTED, "a last-split tile needs split_k > 1");
-            if (s.load_path != 2 || s.bk != 32 || p.mfma != BG_MFMA_F32_32X32X16_BF16 ||
-                !bg::gemm_bf16_has_dual_tile(s.bm, s.bn, s.waves_m, s.waves_n, s.stages, s.last_bm, s.last_bn,
+            if (s.load_path != 2 || p.mfma != BG_MFMA_F32_32X32X16_BF16 ||
+                !bg::gemm_bf16_has_dual_tile(s.bm, s.bn, s.bk, s.waves_m, s.waves_n, s.stages, s.last_bm, s.last_bn,
                                              s.last_waves_m, s.last_waves_n, s.last_stages))
                 return fail(BG_E_UNSUPPORTED, "the (tile, last-split tile) pair is not compiled in");
             p.bm2 = s.last_bm, p.bn2 = s.last_bn, p.waves_m2 = s.last_waves_m, p.waves_n2 = s.last_waves_n;
             p.stages2 = s.last_stages;
             for (const DualPair& dp : kDualPairs)  // the pair's compiled stage counts where left 0
-                if (dp.bm == p.bm && dp.bn == p.bn && dp.wm == p.waves_m && dp.wn == p.waves_n &&
+                if (dp.bk == p.bk && dp.bm == p.bm && dp.bn == p.bn && dp.wm == p.waves_m && dp.wn == p.waves_n &&
                     (!p.stages || dp.ns == p.stages) && dp.bm2 == p.bm2 && dp.bn2 == p.bn2 && dp.wm2 == p.waves_m2 &&
                     dp.wn2 == p.waves_n2 && (!p.stages2 || dp.ns2 == p.stages2)) {
                     p.stages = dp.ns, p.stages2 = dp.ns2;
                     break;
                 }
+            if (p.bk == 64 && ((p.stages == 2 && !bg::pipe_offsets_fit(p.bm, p.bn, lda, ldb)) ||
+                               (p.stages2 == 2 && !bg::pipe_offsets_fit(p.bm2, p.bn2, lda, ldb))))
+                return fail(BG_E_UNSUPPORTED, "a 64-deep two-stage tile addresses its copies by 32-bit offsets: "
+                                              "(bm - 1) x lda and (bn - 1) x ldb must stay below 2^31 elements");
             p.last_first = dual_last_first(p);
         }
     } else {

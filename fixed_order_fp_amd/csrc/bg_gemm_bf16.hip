@@ -925,11 +925,12 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, int64_t lda, const ui
 // tiles), on the small tile of every split the copies would grow with
 // 1/BM + 1/BN; both shapes share the launch so that the CUs stay busy
 // through both.  The workgroups of the last split come first when
-// `last_first` is set, else last.  Only the schedule differs: every split's
-// chain is the one its k range gives, and its partial plane is the same.
-template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2>
+// `last_first` is set, else last.  Both shapes take the same k tile depth
+// BK.  Only the schedule differs: every split's chain is the one its k range
+// gives, and its partial plane is the same.
+template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2, int BK = 32>
 struct DualLds {
-    static constexpr int A = PipeLds<BM, BN, NS, 2>::BYTES, B = PipeLds<BM2, BN2, NS2, 2>::BYTES;
+    static constexpr int A = PipeLds<BM, BN, NS, 2, BK * 2>::BYTES, B = PipeLds<BM2, BN2, NS2, 2, BK * 2>::BYTES;
     static constexpr int BYTES = A > B ? A : B;
     static constexpr int W0 = (160 * 1024) / BYTES * WM * WN / 4;
     static constexpr int WAVES_PER_EU = W0 < 1 ? 1 : W0;
@@ -937,10 +938,11 @@ struct DualLds {
 
 // OUT: 2 partial planes in the workspace, 3 partials added into C with
 // atomics (the free-order twin only).
-template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2, int OUT>
+template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2, int OUT,
+          int BK = 32>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
-    DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::WAVES_PER_EU,
-    DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::WAVES_PER_EU)))
+    DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, BK>::WAVES_PER_EU,
+    DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, BK>::WAVES_PER_EU)))
 void gemm_bf16_pipe_dual_kernel(const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B,
                                 int64_t ldb, void* __restrict__ C, int64_t ldc, float* __restrict__ ws, int64_t M,
                                 int64_t N, Cuts cuts, int S, int tiles_m, int tiles_n, int group_m, int tiles_m2,
@@ -948,7 +950,7 @@ void gemm_bf16_pipe_dual_kernel(const uint16_t* __restrict__ A, int64_t lda, con
 {
     static_assert(OUT == 2 || OUT == 3, "split partials only");
     static_assert(WM * WN == WM2 * WN2, "both shapes run with the workgroup's waves");
-    __shared__ u32x4 lds[DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::BYTES / 16];
+    __shared__ u32x4 lds[DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, BK>::BYTES / 16];
     const int n_last = tiles_m2 * tiles_n2, n_body = tiles_m * tiles_n * (S - 1);
     int b = (int)blockIdx.x;
     bool is_last;
@@ -960,11 +962,11 @@ void gemm_bf16_pipe_dual_kernel(const uint16_t* __restrict__ A, int64_t lda, con
         if (is_last) b -= n_body;
     }
     if (is_last) {
-        pipe_tile<BM2, BN2, WM2, WN2, NS2, OUT, 0>(lds, b, S - 1, A, lda, B, ldb, C, ldc, ws, M, N, cuts, tiles_m2,
+        pipe_tile<BM2, BN2, WM2, WN2, NS2, OUT, 0, BK>(lds, b, S - 1, A, lda, B, ldb, C, ldc, ws, M, N, cuts, tiles_m2,
                                                    tiles_n2, group_m2, RedArgs{});
     } else {
         const int T = tiles_m * tiles_n;
-        pipe_tile<BM, BN, WM, WN, NS, OUT, 0>(lds, b % T, b / T, A, lda, B, ldb, C, ldc, ws, M, N, cuts, tiles_m,
+        pipe_tile<BM, BN, WM, WN, NS, OUT, 0, BK>(lds, b % T, b / T, A, lda, B, ldb, C, ldc, ws, M, N, cuts, tiles_m,
                                               tiles_n, group_m, RedArgs{});
     }
 }
@@ -1229,35 +1231,42 @@ bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves
     return false;
 }
 
-// The (other splits, last split) tile pairs compiled in: BM, BN, waves_m,
-// waves_n, stages of each (pipelined path, 32x32x16).  The first entry of a
-// pair of shapes is its default stage count.
-#define BG_GEMM_DUAL_TILES(X)                    \
-    X(256, 256, 2, 2, 4, 64, 64, 2, 2, 8)        \
-    X(256, 256, 2, 2, 4, 128, 64, 2, 2, 4)       \
-    X(256, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
-    X(192, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
-    X(128, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
-    X(256, 256, 2, 4, 4, 128, 64, 4, 2, 8)       \
-    X(256, 256, 2, 4, 4, 64, 128, 2, 4, 8)
+// The (other splits, last split) tile pairs compiled in: the k tile depth
+// both shapes share, then BM, BN, waves_m, waves_n, stages of each
+// (pipelined path, 32x32x16).  The first entry of a pair of shapes is its
+// default stage count.
+#define BG_GEMM_DUAL_TILES(X)                        \
+    X(32, 256, 256, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(32, 256, 256, 2, 2, 4, 128, 64, 2, 2, 4)       \
+    X(32, 256, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(32, 192, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(32, 128, 128, 2, 2, 4, 64, 64, 2, 2, 8)        \
+    X(32, 256, 256, 2, 4, 4, 128, 64, 4, 2, 8)       \
+    X(32, 256, 256, 2, 4, 4, 64, 128, 2, 4, 8)       \
+    X(64, 256, 256, 2, 4, 2, 128, 64, 4, 2, 4)       \
+    X(64, 128, 128, 2, 2, 4, 64, 64, 2, 2, 6)        \
+    X(64, 128, 128, 2, 2, 4, 128, 64, 2, 2, 4)
 
-bool gemm_bf16_has_dual_tile(int bm, int bn, int waves_m, int waves_n, int stages, int bm2, int bn2, int waves_m2,
-                             int waves_n2, int stages2)
+bool gemm_bf16_has_dual_tile(int bm, int bn, int bk, int waves_m, int waves_n, int stages, int bm2, int bn2,
+                             int waves_m2, int waves_n2, int stages2)
 {
-#define BG_DHAS(BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_)                                            \
-    if (bm == BM_ && bn == BN_ && waves_m == WM_ && waves_n == WN_ && (stages == 0 || stages == NS_) &&           \
-        bm2 == BM2_ && bn2 == BN2_ && waves_m2 == WM2_ && waves_n2 == WN2_ && (stages2 == 0 || stages2 == NS2_))   \
+#define BG_DHAS(BK_, BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_)                                          \
+    if (bk == BK_ && bm == BM_ && bn == BN_ && waves_m == WM_ && waves_n == WN_ && (stages == 0 || stages == NS_) &&  \
+        bm2 == BM2_ && bn2 == BN2_ && waves_m2 == WM2_ && waves_n2 == WN2_ && (stages2 == 0 || stages2 == NS2_))       \
         return true;
     BG_GEMM_DUAL_TILES(BG_DHAS)
 #undef BG_DHAS
     return false;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2>
+template <int BK, int BM, int BN, int WM, int WN, int NS, int BM2, int BN2, int WM2, int WN2, int NS2>
 static hipError_t launch_dual(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                               const uint16_t* B, int64_t ldb, void* C, int64_t ldc, float* ws, hipStream_t stream)
 {
-    constexpr int PER_CU = (160 * 1024) / DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2>::BYTES;
+    using L = DualLds<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, BK>;
+    constexpr int PER_CU = (160 * 1024) / L::BYTES;
+    if (BK == 64 && ((NS == 2 && !pipe_offsets_fit(BM, BN, lda, ldb)) || (NS2 == 2 && !pipe_offsets_fit(BM2, BN2, lda, ldb))))
+        return hipErrorInvalidValue;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     const int tiles_m2 = (int)((M + BM2 - 1) / BM2), tiles_n2 = (int)((N + BN2 - 1) / BN2);
     const int group_m = p.group_m > 0 ? p.group_m : walk_group_m(tiles_m, tiles_n, BM, BN, PER_CU);
@@ -1265,11 +1274,11 @@ static hipError_t launch_dual(const GemmPlan& p, int64_t M, int64_t N, const uin
     const int64_t wgs = (int64_t)tiles_m * tiles_n * (p.S - 1) + (int64_t)tiles_m2 * tiles_n2;
     if (p.S < 2 || wgs > 0x7fffffff) return hipErrorInvalidValue;
     if (p.atomic)  // free-order twin only
-        hipLaunchKernelGGL((gemm_bf16_pipe_dual_kernel<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, 3>),
+        hipLaunchKernelGGL((gemm_bf16_pipe_dual_kernel<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, 3, BK>),
                            dim3((unsigned)wgs), dim3(64 * WM * WN), 0, stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts,
                            p.S, tiles_m, tiles_n, group_m, tiles_m2, tiles_n2, group_m2, p.last_first ? 1 : 0);
     else
-        hipLaunchKernelGGL((gemm_bf16_pipe_dual_kernel<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, 2>),
+        hipLaunchKernelGGL((gemm_bf16_pipe_dual_kernel<BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, 2, BK>),
                            dim3((unsigned)wgs), dim3(64 * WM * WN), 0, stream, A, lda, B, ldb, C, ldc, ws, M, N, p.cuts,
                            p.S, tiles_m, tiles_n, group_m, tiles_m2, tiles_n2, group_m2, p.last_first ? 1 : 0);
     return hipGetLastError();
@@ -1289,13 +1298,13 @@ hipError_t launch_gemm_bf16(const GemmPlan& p, int64_t M, int64_t N, int64_t K, 
         err = TileLauncher<D_>::template run<I, BM_, BN_, BK_, WM_, WN_, NS_>(p, M, N, A, lda, B, ldb, C, ldc, ws, stream); \
     }
     if (p.bm2) {
-#define BG_DLAUNCH(BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_)                                        \
-        if (!found && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_ &&                      \
+#define BG_DLAUNCH(BK_, BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_)                                   \
+        if (!found && p.bk == BK_ && p.bm == BM_ && p.bn == BN_ && p.waves_m == WM_ && p.waves_n == WN_ &&       \
             (p.stages == 0 || p.stages == NS_) && p.bm2 == BM2_ && p.bn2 == BN2_ && p.waves_m2 == WM2_ &&          \
             p.waves_n2 == WN2_ && (p.stages2 == 0 || p.stages2 == NS2_)) {                                       \
             found = true;                                                                                          \
-            err = launch_dual<BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_>(p, M, N, A, lda, B, ldb, C, ldc, \
-                                                                                   ws, stream);                    \
+            err = launch_dual<BK_, BM_, BN_, WM_, WN_, NS_, BM2_, BN2_, WM2_, WN2_, NS2_>(p, M, N, A, lda, B, ldb, C, \
+                                                                                        ldc, ws, stream);          \
         }
         BG_GEMM_DUAL_TILES(BG_DLAUNCH)
 #undef BG_DLAUNCH

@@ -165,8 +165,8 @@ hipError_t launch_zero_rows(float* C, int64_t M, int64_t N, int64_t ldc, hipStre
 bool gemm_bf16_has_tile(int mfma, int bm, int bn, int bk, int waves_m, int waves_n, int direct, int stages);
 // a compiled (other splits, last split) pair of pipelined tiles; stages == 0
 // takes the first compiled pair of the two shapes
-bool gemm_bf16_has_dual_tile(int bm, int bn, int waves_m, int waves_n, int stages, int bm2, int bn2, int waves_m2,
-                             int waves_n2, int stages2);
+bool gemm_bf16_has_dual_tile(int bm, int bn, int bk, int waves_m, int waves_n, int stages, int bm2, int bn2,
+                             int waves_m2, int waves_n2, int stages2);
 // tiles built with the fused reductions (pipelined path, S = 1)
 bool gemm_bf16_red_has_tile(int bm, int bn, int bk, int waves_m, int waves_n, int stages);
 

@@ -212,10 +212,10 @@ def gemm_variants(asm):
         if "gemm_bf16_pipe_kernel" in name:          # <BM, BN, WM, WN, NS, OUT, RED, BK>
             bm, bn, wm, wn, bk = t[0], t[1], t[2], t[3], t[7]
             out.append((name, lines, 0, bk // INSTR_K[0], (bm // wm // 32) * (bn // wn // 32)))
-        elif "gemm_bf16_pipe_dual_kernel" in name:   # <BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, OUT>
+        elif "gemm_bf16_pipe_dual_kernel" in name:   # <BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, OUT, BK>
             b1 = (t[0] // t[2] // 32) * (t[1] // t[3] // 32)
             b2 = (t[5] // t[7] // 32) * (t[6] // t[8] // 32)
-            out.append((name, lines, 0, 32 // INSTR_K[0], {b1, b2}))
+            out.append((name, lines, 0, t[11] // INSTR_K[0], {b1, b2}))
         elif "gemm_bf16_direct_kernel" in name:      # <INSTR, BM, BN, WM, WN, OUT_BF16, PARTIAL>, BK 64
             i, bm, bn, wm, wn = t[0], t[1], t[2], t[3], t[4]
             e = BLOCK[i]

@@ -8,9 +8,11 @@ the kernel's LDS.
 
 The walk restates the kernels' index arithmetic (copy slot s = r * waves +
 wave, stage chunk c = 64 s + lane, A rows first, 16-byte chunk kc of a row
-swizzled as kc ^ ((row >> 2) & 3), LDS byte (turn % stages * stage + 64 s +
-lane) * 16); the tile lists are read from the sources, so a tile added there
-is walked too."""
+swizzled as kc ^ ((row >> 2) & 3) in 64-byte rows and kc ^ ((row >> 1) & 7)
+in 128-byte rows, LDS byte (turn % stages * stage + 64 s + lane) * 16); the
+two-stage tiles address a copy by a 32-bit byte offset from the tile's first
+row, which must stay below 2^32.  The tile lists are read from the sources,
+so a tile added there is walked too."""
 import os
 import re
 
@@ -28,15 +30,19 @@ def _macro_rows(src, name):
 
 
 def bf16_pipe_tiles():
+    """(bm, bn, bk, wm, wn, ns) of the pipelined tiles, and the pairs as
+    (bk, bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2)."""
     src = open(os.path.join(CSRC, "bg_gemm_bf16.hip")).read()
-    single = [(bm, bn, wm, wn, ns) for i, bm, bn, bk, wm, wn, d, ns in _macro_rows(src, "BG_GEMM_TILES") if d == 2]
+    single = [(bm, bn, bk, wm, wn, ns) for i, bm, bn, bk, wm, wn, d, ns in _macro_rows(src, "BG_GEMM_TILES") if d == 2]
     dual = _macro_rows(src, "BG_GEMM_DUAL_TILES")
     return single, dual
 
 
 def w8a8_pipe_tiles():
+    """(bm, bn, wm, wn, ns, k tile bytes): two stages take 128-byte k tiles."""
     src = open(os.path.join(CSRC, "bg_w8a8.hip")).read()
-    return [(bm, bn, wm, wn, ns) for i, bm, bn, wm, wn, path, ns in _macro_rows(src, "BG_W8A8_TILES") if path == 2]
+    return [(bm, bn, wm, wn, ns, 128 if ns == 2 else 64)
+            for i, bm, bn, wm, wn, path, ns in _macro_rows(src, "BG_W8A8_TILES") if path == 2]
 
 
 def walk(bm, bn, wm, wn, ns, M, N, ld_a, ld_b, k_begin, k_end, row_bytes, elt, out_lds, clamp=True):
@@ -64,7 +70,7 @@ def walk(bm, bn, wm, wn, ns, M, N, ld_a, ld_b, k_begin, k_end, row_bytes, elt, o
     c = np.where(s < slots, s, 0) * 64 + lane
     is_a = c < a_ch
     row = np.where(is_a, c // cpr, (c - a_ch) // cpr)
-    kc = (c % cpr) ^ ((row >> 2) & 3)
+    kc = (c % cpr) ^ (((row >> 2) & 3) if cpr == 4 else ((row >> 1) & 7))
     worst_src = worst_k = 0
     lds_hi = 0
     if n_full:
@@ -79,6 +85,10 @@ def walk(bm, bn, wm, wn, ns, M, N, ld_a, ld_b, k_begin, k_end, row_bytes, elt, o
                 g = np.minimum(g, lim - 1)
             ld = np.where(is_a, ld_a, ld_b)
             size = np.where(is_a, M * ld_a, N * ld_b)
+            if ns == 2:  # the byte offset from the tile's first row is 32-bit
+                first_row = np.where(is_a, tm * bm, tn * bn)
+                off = ((g - first_row) * ld + kc * chunk) * elt
+                assert int(np.where(issued, off, 0).max()) + 16 <= 2 ** 32
             for t in ([0, n_full - 1] if n_full else []):
                 k0 = k_begin + t * bk + kc * chunk
                 first = g * ld + k0
@@ -98,21 +108,22 @@ SHAPES = [(97, 136, 600), (256, 2560, 1024), (300, 504, 1000), (33, 70, 520), (4
 def test_bf16_pipe_copies_stay_in_bounds(M, N, K):
     single, dual = bf16_pipe_tiles()
     assert len(single) >= 20 and len(dual) >= 5
-    shapes = set(single) | {d[:5] for d in dual} | {d[5:] for d in dual}
+    assert {t[2] for t in single} == {32, 64} and {d[0] for d in dual} == {32, 64}
+    shapes = set(single) | {(d[1], d[2], d[0]) + d[3:6] for d in dual} | {(d[6], d[7], d[0]) + d[8:] for d in dual}
     cuts = [0, (K // 3) // 8 * 8, K]  # two splits, the second deeper; and the whole range
-    for bm, bn, wm, wn, ns in sorted(shapes):
+    for bm, bn, bk, wm, wn, ns in sorted(shapes):
         for k0, k1 in ((0, K), (cuts[0], cuts[1]), (cuts[1], cuts[2])):
-            src, kk, lds_hi, lds = walk(bm, bn, wm, wn, ns, M, N, K + 8, K, k0, k1, 64, 2, True)
-            assert src <= 0 and kk <= 0, (bm, bn, wm, wn, ns, M, N, K, k0, k1, src, kk)
-            assert lds_hi <= lds <= 160 * 1024, (bm, bn, ns, lds_hi, lds)
+            src, kk, lds_hi, lds = walk(bm, bn, wm, wn, ns, M, N, K + 8, K, k0, k1, 2 * bk, 2, True)
+            assert src <= 0 and kk <= 0, (bm, bn, bk, wm, wn, ns, M, N, K, k0, k1, src, kk)
+            assert lds_hi <= lds <= 160 * 1024, (bm, bn, bk, ns, lds_hi, lds)
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 6144, 2048), (1024, 6144, 2048), (77, 200, 1040), (5, 64, 64)])
 def test_w8a8_pipe_copies_stay_in_bounds(M, N, K):
     tiles = w8a8_pipe_tiles()
-    assert len(tiles) >= 5
-    for bm, bn, wm, wn, ns in tiles:
-        src, kk, lds_hi, lds = walk(bm, bn, wm, wn, ns, M, N, K, K, 0, K, 64, 1, True)
+    assert len(tiles) >= 5 and {t[5] for t in tiles} == {64, 128}
+    for bm, bn, wm, wn, ns, row_bytes in tiles:
+        src, kk, lds_hi, lds = walk(bm, bn, wm, wn, ns, M, N, K, K, 0, K, row_bytes, 1, True)
         assert src <= 0 and kk <= 0, (bm, bn, wm, wn, ns, M, N, K, src, kk)
         assert lds_hi <= lds <= 160 * 1024
 

@@ -56,13 +56,14 @@ SCHEDULES = {
 
 # (other splits, last split) pairs: the last split, the cut rule's remainder,
 # takes its own tile in the same launch (split_k > 1 only)
-DUAL_SCHEDULES = [dict(bm=bm, bn=bn, bk=32, waves_m=wm, waves_n=wn, load_path=2, stages=ns, last_bm=bm2,
+DUAL_SCHEDULES = [dict(bm=bm, bn=bn, bk=bk, waves_m=wm, waves_n=wn, load_path=2, stages=ns, last_bm=bm2,
                        last_bn=bn2, last_waves_m=wm2, last_waves_n=wn2, last_stages=ns2)
-                  for bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2 in
-                  [(256, 256, 2, 2, 4, 64, 64, 2, 2, 8), (256, 256, 2, 2, 4, 128, 64, 2, 2, 4),
-                   (256, 128, 2, 2, 4, 64, 64, 2, 2, 8), (192, 128, 2, 2, 4, 64, 64, 2, 2, 8),
-                   (128, 128, 2, 2, 4, 64, 64, 2, 2, 8), (256, 256, 2, 4, 4, 128, 64, 4, 2, 8),
-                   (256, 256, 2, 4, 4, 64, 128, 2, 4, 8)]]
+                  for bk, bm, bn, wm, wn, ns, bm2, bn2, wm2, wn2, ns2 in
+                  [(32, 256, 256, 2, 2, 4, 64, 64, 2, 2, 8), (32, 256, 256, 2, 2, 4, 128, 64, 2, 2, 4),
+                   (32, 256, 128, 2, 2, 4, 64, 64, 2, 2, 8), (32, 192, 128, 2, 2, 4, 64, 64, 2, 2, 8),
+                   (32, 128, 128, 2, 2, 4, 64, 64, 2, 2, 8), (32, 256, 256, 2, 4, 4, 128, 64, 4, 2, 8),
+                   (32, 256, 256, 2, 4, 4, 64, 128, 2, 4, 8), (64, 256, 256, 2, 4, 2, 128, 64, 4, 2, 4),
+                   (64, 128, 128, 2, 2, 4, 64, 64, 2, 2, 6), (64, 128, 128, 2, 2, 4, 128, 64, 2, 2, 4)]]
 
 
 @pytest.fixture(scope="module", autouse=True)
