@@ -727,93 +727,6 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
     // Block (j, i), element e of lane l: row m = wm*WTM + 32i + l%32, columns
     // n = wn*WTN + 32j + 8(e/4) + 4(l/32) + (0..3) for e%4 = 0..3.
     //
-    // Fused reductions of the fp32 C values (before any rounding to the output
-    // type): each wave stages two 32x32 blocks at a time in its own LDS slice
-    // (rows of 36 floats, the second block 32 banks over, so that a column
-    // walk is free of bank conflicts and a row walk reads 16 bytes at a time);
-    // lane c of each half-wave folds column c of its block over the rows
-    // (RED 1: a leaf of 32 rows) or row c over the columns (RED 2: a leaf of
-    // 32 columns) in index order, with no seed (s = x0, s = s + xi; q = x0 x0,
-    // q = fma(xi, xi, q) or q + xi xi), and writes the leaf node.  The leaf's
-    // elements past M or N are left out (a short last leaf).
-    if constexpr (RED != 0) {
-        static_assert(OUT == 0 || OUT == 1, "fused reductions take the unsplit C");
-        constexpr int RP = 36;                     // floats per staged row (16-byte aligned)
-        constexpr int BLK = 32 * RP + 32;          // one staged block; the second one 32 banks over
-        constexpr int NB = TM * TN;
-        static_assert(NW * 2 * BLK * 4 <= LDS_BYTES, "the reduction slices fit in LDS");
-        __syncthreads();  // every wave is done with the operand stages
-        float* st = (float*)lds + wave * (2 * BLK);
-        const int half = lane >> 5, c = lane & 31;
-        // blocks b = 2p and 2p + 1 are staged together; lanes 0..31 fold
-        // the leaves of the first, lanes 32..63 those of the second
-        auto fold_all = [&](auto fused_tag) {
-            constexpr bool FUSED = decltype(fused_tag)::value;
-            auto step = [&](float v, float& sv, float& qv) {
-                sv = sv + v;
-                if constexpr (FUSED) {
-                    qv = __builtin_fmaf(v, v, qv);
-                } else {
-                    const float vv = v * v;
-                    qv = qv + vv;
-                }
-            };
-#pragma unroll
-            for (int p = 0; p < (NB + 1) / 2; p++) {
-#pragma unroll
-                for (int k = 0; k < 2; k++) {
-                    if (2 * p + k < NB) {
-                        const int j = (2 * p + k) / TM, i = (2 * p + k) % TM;
-                        float* sb = st + k * BLK;
-#pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            const f32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
-                                             acc[j][i][4 * q + 3]};
-                            *(f32x4*)(sb + r_in * RP + 8 * q + 4 * h) = v;
-                        }
-                    }
-                }
-                const int b = 2 * p + half;
-                const int j = b / TM, i = b % TM;
-                const int64_t rb = m0 + wm * WTM + 32 * i, cb = n0 + wn * WTN + 32 * j;
-                const int64_t n_el = RED == 1 ? M - rb : N - cb;  // elements of this lane's leaf
-                const int64_t o = (RED == 1 ? cb : rb) + c;        // this lane's output
-                const int64_t o_end = RED == 1 ? N : M;
-                if (b < NB && o < o_end && n_el > 0) {
-                    const int n = n_el < 32 ? (int)n_el : 32;
-                    const float* sb = st + half * BLK;
-                    float sv, qv;
-                    if (n == 32) {  // a whole leaf: its 32 elements are read at once, then folded
-                        float xv[32];
-                        if constexpr (RED == 1) {  // column c, down the rows
-#pragma unroll
-                            for (int e = 0; e < 32; e++) xv[e] = sb[c + RP * e];
-                        } else {  // row c, along the columns
-#pragma unroll
-                            for (int e = 0; e < 32; e += 4) {
-                                const f32x4 v = *(const f32x4*)(sb + c * RP + e);
-                                xv[e] = v[0], xv[e + 1] = v[1], xv[e + 2] = v[2], xv[e + 3] = v[3];
-                            }
-                        }
-                        sv = xv[0], qv = xv[0] * xv[0];
-#pragma unroll
-                        for (int e = 1; e < 32; e++) step(xv[e], sv, qv);
-                    } else {  // the short last leaf
-                        constexpr int STEP = RED == 1 ? RP : 1;
-                        const float* x = sb + (RED == 1 ? c : c * RP);
-                        sv = x[0], qv = x[0] * x[0];
-                        for (int e = 1; e < n; e++) step(x[e * STEP], sv, qv);
-                    }
-                    const int64_t leaf = (RED == 1 ? rb : cb) / 32;
-                    if (red.ws_sum) red.ws_sum[leaf * red.n_out + o] = sv;
-                    if (red.ws_sq) red.ws_sq[leaf * red.n_out + o] = qv;
-                }
-            }
-        };
-        if (red.fused) fold_all(std::true_type{});
-        else fold_all(std::false_type{});
-        __syncthreads();  // the slices are free again
-    }
 
     // epilogue
     if constexpr (OUT == 1) {
@@ -900,6 +813,98 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
                     }
                 }
             }
+    }
+
+    // Fused reductions of the fp32 C values (before any rounding to the output
+    // type), after the C epilogue -- the accumulators are still in
+    // registers, and the C tile's global stores drain during the fold: each
+    // wave stages two 32x32 blocks at a time in its own LDS slice
+    // (rows of 36 floats, the second block 32 banks over, so that a column
+    // walk is free of bank conflicts and a row walk reads 16 bytes at a time);
+    // lane c of each half-wave folds column c of its block over the rows
+    // (RED 1: a leaf of 32 rows) or row c over the columns (RED 2: a leaf of
+    // 32 columns) in index order, with no seed (s = x0, s = s + xi; q = x0 x0,
+    // q = fma(xi, xi, q) or q + xi xi), and writes the leaf node.  The leaf's
+    // elements past M or N are left out (a short last leaf).
+    if constexpr (RED != 0) {
+        static_assert(OUT == 0 || OUT == 1, "fused reductions take the unsplit C");
+        constexpr int RP = 36;                     // floats per staged row (16-byte aligned)
+        constexpr int BLK = 32 * RP + 32;          // one staged block; the second one 32 banks over
+        constexpr int NB = TM * TN;
+        static_assert(NW * 2 * BLK * 4 <= LDS_BYTES, "the reduction slices fit in LDS");
+        // every wave is done with the C tile's staging in LDS (its reads have
+        // returned): the fold reuses the LDS while the C stores drain
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        float* st = (float*)lds + wave * (2 * BLK);
+        const int half = lane >> 5, c = lane & 31;
+        // blocks b = 2p and 2p + 1 are staged together; lanes 0..31 fold
+        // the leaves of the first, lanes 32..63 those of the second
+        auto fold_all = [&](auto fused_tag) {
+            constexpr bool FUSED = decltype(fused_tag)::value;
+            auto step = [&](float v, float& sv, float& qv) {
+                sv = sv + v;
+                if constexpr (FUSED) {
+                    qv = __builtin_fmaf(v, v, qv);
+                } else {
+                    const float vv = v * v;
+                    qv = qv + vv;
+                }
+            };
+#pragma unroll
+            for (int p = 0; p < (NB + 1) / 2; p++) {
+#pragma unroll
+                for (int k = 0; k < 2; k++) {
+                    if (2 * p + k < NB) {
+                        const int j = (2 * p + k) / TM, i = (2 * p + k) % TM;
+                        float* sb = st + k * BLK;
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const f32x4 v = {acc[j][i][4 * q], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                                             acc[j][i][4 * q + 3]};
+                            *(f32x4*)(sb + r_in * RP + 8 * q + 4 * h) = v;
+                        }
+                    }
+                }
+                const int b = 2 * p + half;
+                const int j = b / TM, i = b % TM;
+                const int64_t rb = m0 + wm * WTM + 32 * i, cb = n0 + wn * WTN + 32 * j;
+                const int64_t n_el = RED == 1 ? M - rb : N - cb;  // elements of this lane's leaf
+                const int64_t o = (RED == 1 ? cb : rb) + c;        // this lane's output
+                const int64_t o_end = RED == 1 ? N : M;
+                if (b < NB && o < o_end && n_el > 0) {
+                    const int n = n_el < 32 ? (int)n_el : 32;
+                    const float* sb = st + half * BLK;
+                    float sv, qv;
+                    if (n == 32) {  // a whole leaf: its 32 elements are read at once, then folded
+                        float xv[32];
+                        if constexpr (RED == 1) {  // column c, down the rows
+#pragma unroll
+                            for (int e = 0; e < 32; e++) xv[e] = sb[c + RP * e];
+                        } else {  // row c, along the columns
+#pragma unroll
+                            for (int e = 0; e < 32; e += 4) {
+                                const f32x4 v = *(const f32x4*)(sb + c * RP + e);
+                                xv[e] = v[0], xv[e + 1] = v[1], xv[e + 2] = v[2], xv[e + 3] = v[3];
+                            }
+                        }
+                        sv = xv[0], qv = xv[0] * xv[0];
+#pragma unroll
+                        for (int e = 1; e < 32; e++) step(xv[e], sv, qv);
+                    } else {  // the short last leaf
+                        constexpr int STEP = RED == 1 ? RP : 1;
+                        const float* x = sb + (RED == 1 ? c : c * RP);
+                        sv = x[0], qv = x[0] * x[0];
+                        for (int e = 1; e < n; e++) step(x[e * STEP], sv, qv);
+                    }
+                    const int64_t leaf = (RED == 1 ? rb : cb) / 32;
+                    if (red.ws_sum) red.ws_sum[leaf * red.n_out + o] = sv;
+                    if (red.ws_sq) red.ws_sq[leaf * red.n_out + o] = qv;
+                }
+            }
+        };
+        if (red.fused) fold_all(std::true_type{});
+        else fold_all(std::false_type{});
     }
 }
 
