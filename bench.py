@@ -322,14 +322,19 @@ def headline_free_twins(head, args, torch, bg):
     """The headline product by kernels that leave part of the order free,
     timed in interleaved rounds with the order-fixed call: the same kernel
     with fp32 output (order unchanged; the output-width cost only), atomic
-    split-K at 2 and 4 splits (partials added into C in arrival order), the
-    other MFMA shape (16x16x32: another, equally fixed, order), and the vendor
-    library (hipBLASLt through torch.nn.functional.linear, bf16 out, its own
-    order).  Returns (twins dict, interleaved fixed ms)."""
+    split-K at 2 and 4 splits (partials added into C in arrival order), two
+    interleaved accumulator chains per output (on the 128x128 tile, beside
+    the order-fixed kernel on that same tile), the other MFMA shape
+    (16x16x32: another, equally fixed, order), and the vendor library
+    (hipBLASLt through torch.nn.functional.linear, bf16 out, its own order).
+    Returns (twins dict, interleaved fixed ms)."""
     import torch.nn.functional as F
     dF = torch.empty((head.M, head.N), dtype=torch.float32, device="cuda")
     dB16 = torch.empty((head.M, head.N), dtype=torch.int16, device="cuda")
     d16 = bg.gemm_desc({"mfma": "F32_16X16X32_BF16", "out_type": "bf16"})
+    d128 = bg.gemm_desc({"mfma": "F32_32X32X16_BF16", "out_type": "fp32",
+                         "schedule": {"bm": 128, "bn": 128, "bk": 64, "waves_m": 2, "waves_n": 2, "load_path": 2,
+                                      "stages": 4}})
 
     def free(split_k):
         def fn():
@@ -341,22 +346,38 @@ def headline_free_twins(head, args, torch, bg):
         A, B = head.rot.next()
         bg.gemm_bf16(d16, A, B, dB16, None)
 
+    def two_chains():
+        A, B = head.rot.next()
+        bg.bench_gemm_bf16_two_chains(A, B, dF)
+
+    def fixed_same_tile():
+        A, B = head.rot.next()
+        bg.gemm_bf16(d128, A, B, dF, None)
+
     def vendor():
         A, B = head.rot.next()
         F.linear(A.view(torch.bfloat16), B.view(torch.bfloat16))
 
     fns = {"fixed": head.run_rot, "same_kernel_fp32_out": free(1), "atomic_split_k2": free(2),
-           "atomic_split_k4": free(4), "mfma_16x16x32_fixed": other_shape, "vendor_hipblaslt": vendor}
+           "atomic_split_k4": free(4), "two_chains_128x128": two_chains, "fixed_128x128_fp32": fixed_same_tile,
+           "mfma_16x16x32_fixed": other_shape, "vendor_hipblaslt": vendor}
     settle(head.run_rot, torch, 200.0)
     ms = interleaved_ms(fns, max(10, args.steps), torch)
     order = {"same_kernel_fp32_out": "identical kernel and order, fp32 out (4 B per output)",
              "atomic_split_k2": "K cut in 2, fp32 partials atomically added into a zeroed C (arrival order)",
              "atomic_split_k4": "K cut in 4, atomic combine (arrival order)",
+             "two_chains_128x128": "two interleaved fp32 chains per output (even and odd 16-deep k-steps), added "
+                                   "once at the end; 128x128 tile, 64-deep k tiles, fp32 out",
              "mfma_16x16x32_fixed": "the other MFMA shape (another fixed order), bf16 out",
              "vendor_hipblaslt": "hipBLASLt via torch.nn.functional.linear, bf16 out, order left to the library"}
     twins = {k: {"ms": round(v, 5), "TFLOP/s": round(head.flops() / (v * 1e-3) / 1e12, 3),
                  "fixed_over_twin_time": round(ms["fixed"] / v, 4), "order": order[k]}
-             for k, v in ms.items() if k != "fixed"}
+             for k, v in ms.items() if k not in ("fixed", "fixed_128x128_fp32")}
+    # the cost of the single chain on one tile: the order-fixed kernel on the
+    # twin's own tile and output width against the twin
+    twins["two_chains_128x128"]["same_tile_fixed_ms"] = round(ms["fixed_128x128_fp32"], 5)
+    twins["two_chains_128x128"]["same_tile_fixed_over_twin_time"] = round(
+        ms["fixed_128x128_fp32"] / ms["two_chains_128x128"], 4)
     return twins, ms["fixed"]
 
 

@@ -112,6 +112,8 @@ _SYMBOLS = {
     "bg_bench_gemm_bf16_free": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                           C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int32,
                                           C.c_void_p]),
+    "bg_bench_gemm_bf16_two_chains": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
+                                                C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p]),
     "bg_bench_gemm_w8a8_free": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_void_p, C.c_int64, C.c_void_p,
                                           C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
     "bg_bench_reduce_free": (C.c_int, [C.c_uint32, C.c_uint32, C.c_int64, C.c_int64, C.c_void_p,
@@ -383,6 +385,15 @@ def bench_gemm_bf16_free(A, B, C_out, split_k=0, stream=None):
     N = B.shape[0]
     _check(lib().bg_bench_gemm_bf16_free(M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0),
                                          _ptr(C_out), C_out.stride(0), int(split_k), _stream(stream)))
+
+
+def bench_gemm_bf16_two_chains(A, B, C_out, stream=None):
+    """Free-order twin (bench only): C_out fp32 = A B^T with two interleaved
+    accumulator chains per output, on the 128x128 tile with 64-deep k tiles."""
+    M, K = A.shape
+    N = B.shape[0]
+    _check(lib().bg_bench_gemm_bf16_two_chains(M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                                               _ptr(C_out), C_out.stride(0), _stream(stream)))
 
 
 def bench_gemm_w8a8_free(A, W, a_scale, w_scale, Y, stream=None):

@@ -1206,6 +1206,27 @@ bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A
     return BG_OK;
 }
 
+bg_status bg_bench_gemm_bf16_two_chains(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                        const void* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream)
+{
+    if (M < 0 || N < 0 || K < 1) return fail(BG_E_INVALID, "bad sizes");
+    if (lda < K || ldb < K || ldc < N) return fail(BG_E_INVALID, "leading dimension smaller than the row");
+    if (K % 8) return fail(BG_E_UNSUPPORTED, "K must be a multiple of 8");
+    if (M == 0 || N == 0) return BG_OK;
+    if (!A || !B || !C) return fail(BG_E_INVALID, "NULL tensor");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || lda % 8 || ldb % 8 || ldc % 8)
+        return fail(BG_E_ALIGN, "pointers must be 16-byte aligned and leading dimensions multiples of 8");
+    if (!bg::pipe_offsets_fit(128, 128, lda, ldb))
+        return fail(BG_E_UNSUPPORTED, "leading dimensions too large for the tile's 32-bit copy offsets");
+    if (!tiles_fit(M, N, 128, 128, 256)) return fail(BG_E_UNSUPPORTED, "M x N too large for one launch");
+    bg_status st = check_device();
+    if (st != BG_OK) return st;
+    hipError_t e = bg::launch_gemm_bf16_two_chains(M, N, K, (const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc,
+                                                  stream);
+    if (e != hipSuccess) return fail(BG_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    return BG_OK;
+}
+
 bg_status bg_bench_gemm_w8a8_free(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda, const int8_t* W,
                                   int64_t ldw, const float* a_scale, const float* w_scale, void* Y, int64_t ldy,
                                   hipStream_t stream)

@@ -423,7 +423,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_direct_kernel(
 // streams its operands from HBM; a ring of three measured slower.
 
 // OUT: 0 fp32 C, 1 bf16 C, 2 fp32 split partial to the workspace, 3 fp32
-// split partial added into C with atomics (the free-order twin only)
+// split partial added into C with atomics, 4 fp32 C from two interleaved
+// accumulator chains per output (even k-steps into one, odd into the other,
+// the two added once after the walk); 3 and 4 are free-order twins only
 // RED: 0 none, 1 and 2 fused reductions of the fp32 C tile (column and row
 // leaves; S = 1, OUT 0 or 1).
 //
@@ -452,6 +454,7 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
     static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "tile rows must fill whole copy slots");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole MFMA blocks");
     static_assert(BK == 32 || BK == 64, "k tiles of 32 or 64");
+    static_assert(OUT != 4 || (RED == 0 && KS % 2 == 0), "two chains: fp32 C, whole pairs of k-steps per turn");
     static_assert(NS == 2 || (NS >= 3 && LOADS_HI * (NS - 2) < 64), "a ring of three stages at least, waits within vmcnt");
     static_assert(NS != 2 || (BK == 64 && EXTRA == 0 && ROUNDS < 64), "two stages: 64-deep tiles, equal copy rounds");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
@@ -494,18 +497,38 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
     };
 
     f32x16 acc[TN][TM];  // block (j, i): rows n of C^T = columns n of C
+    constexpr bool TWO = OUT == 4;
+    f32x16 acc2[TWO ? TN : 1][TWO ? TM : 1];  // the odd k-steps' chain (OUT 4)
 #pragma unroll
     for (int j = 0; j < TN; j++)
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[j][i][e] = 0.0f;
-    auto mm = [&](const bf16x8* a, const bf16x8* b) {
+    if constexpr (TWO) {
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 16; e++) acc2[j][i][e] = 0.0f;
+    }
+    // one instruction into block (j, i); `odd` (the k-step's parity, a
+    // constant once the loops are unrolled) picks the chain under OUT 4
+    auto mfma1 = [&](int j, int i, const bf16x8& a, const bf16x8& b, int odd) {
+        if constexpr (TWO) {
+            if (odd) {
+                acc2[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc2[j][i], 0, 0, 0);
+                return;
+            }
+        }
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc[j][i], 0, 0, 0);
+    };
+    auto mm = [&](const bf16x8* a, const bf16x8* b, int odd) {
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++) mfma1(j, i, a[i], b[j], odd);
     };
     if constexpr (NS >= 3) {
         // the chunk this lane copies in round r: stage chunk c = 64 s + lane (A
@@ -575,7 +598,7 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
             for (int j = 0; j < TN; j++)
 #pragma unroll
                 for (int i = 0; i < TM; i++) {
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+                    mfma1(j, i, a[i], b[j], 1);  // the last k-step of a turn (KS is even)
                     ++q;
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -605,7 +628,7 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
             for (int ks = 0; ks + 1 < KS; ks++) {
                 rd(t, ks + 1, xa[(ks + 1) & 1], xb[(ks + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
-                mm(xa[ks & 1], xb[ks & 1]);
+                mm(xa[ks & 1], xb[ks & 1], ks & 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // tile t+1 must have landed in every wave's share before its first read
@@ -627,7 +650,7 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
                 if (t + NS - 1 < n_turns) issue(t + NS - 1);
                 rd(t + 1, 0, xa[0], xb[0]);  // past the last tile: a stale read, never used
                 __builtin_amdgcn_sched_barrier(0);
-                mm(xa[1], xb[1]);
+                mm(xa[1], xb[1], 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -702,7 +725,7 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
             for (int ks = 0; ks + 1 < KS; ks++) {
                 rd(t, ks + 1, xa[(ks + 1) & 1], xb[(ks + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
-                mm(xa[ks & 1], xb[ks & 1]);
+                mm(xa[ks & 1], xb[ks & 1], ks & 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (NEXT != 0) {
@@ -715,13 +738,22 @@ __device__ __forceinline__ void pipe_tile(u32x4* __restrict__ lds, int b, int sp
                 rd(t + 1, 0, xa[0], xb[0]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            mm(xa[(KS - 1) & 1], xb[(KS - 1) & 1]);
+            mm(xa[(KS - 1) & 1], xb[(KS - 1) & 1], (KS - 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
         };
         int t = 0;
         for (; t + 1 < n_full; t++) turn(t, std::integral_constant<int, 1>{});
         if (t + 1 < n_turns) turn(t++, std::integral_constant<int, 2>{});
         if (t < n_turns) turn(t, std::integral_constant<int, 0>{});
+    }
+
+    if constexpr (TWO) {  // the two chains, added once per output
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int e = 0; e < 16; e++) acc[j][i][e] = acc[j][i][e] + acc2[j][i][e];
     }
 
     // Block (j, i), element e of lane l: row m = wm*WTM + 32i + l%32, columns
@@ -1379,6 +1411,24 @@ hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, cons
     BG_GEMM_RED_TILES(BG_RLAUNCH)
 #undef BG_RLAUNCH
     return hipErrorInvalidValue;
+}
+
+// The free-order twin with two interleaved accumulator chains per output
+// (bench only): the 128x128 tile with 64-deep k tiles in a ring of four, the
+// same main loop as that tile's order-fixed kernel, fp32 C.
+hipError_t launch_gemm_bf16_two_chains(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                       const uint16_t* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream)
+{
+    constexpr int BM = 128, BN = 128, WM = 2, WN = 2, NS = 4, BK = 64;
+    if (!pipe_offsets_fit(BM, BN, lda, ldb)) return hipErrorInvalidValue;
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int group_m = walk_group_m(tiles_m, tiles_n, BM, BN, PipeLds<BM, BN, NS, 0, BK * 2>::WG_PER_CU);
+    Cuts cuts{};
+    cuts.c[0] = 0, cuts.c[1] = K;
+    hipLaunchKernelGGL((gemm_impl::gemm_bf16_pipe_kernel<BM, BN, WM, WN, NS, 4, 0, BK>), dim3(tiles_m * tiles_n),
+                       dim3(64 * WM * WN), 0, stream, A, lda, B, ldb, (void*)C, ldc, (float*)nullptr, M, N, cuts,
+                       tiles_m, tiles_n, group_m, RedArgs{});
+    return hipGetLastError();
 }
 
 }  // namespace bg

@@ -186,5 +186,7 @@ inline bool i8_offsets_fit(int64_t bm, int64_t bn, int64_t lda, int64_t ldw)
 }
 hipError_t launch_gemm_bf16_reduce(const GemmPlan& p, int64_t M, int64_t N, const uint16_t* A, int64_t lda,
                                    const uint16_t* B, int64_t ldb, void* C, int64_t ldc, hipStream_t stream);
+hipError_t launch_gemm_bf16_two_chains(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                       const uint16_t* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream);
 
 }  // namespace bg

@@ -412,6 +412,18 @@ bg_status bg_reduce_tree(const bg_reduce_desc* d, int64_t rows, int64_t cols,
 bg_status bg_bench_gemm_bf16_free(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                   const void* B, int64_t ldb, float* C, int64_t ldc,
                                   int32_t split_k, hipStream_t stream);
+/* Another free-order twin of the same product ([T] 3.2.1: the chain of
+ * roundings across instructions is what survives as the order; 3.2.2: a
+ * strided deal of the axis over accumulators is another order): each output
+ * carries two interleaved fp32 chains, even 16-deep k-steps into one and odd
+ * ones into the other, added once after the walk -- the reassociation an
+ * implementation free to reorder may use to hide the instruction's latency.
+ * The 128x128 tile with 64-deep k tiles in a ring of four (the same main loop
+ * as that tile's order-fixed kernel, selectable through the descriptor's
+ * schedule), fp32 C [M][ldc].  Same argument rules as bg_gemm_bf16 (K a
+ * multiple of 8; 127 x lda x 2 + 128 and 127 x ldb x 2 + 128 below 2^32). */
+bg_status bg_bench_gemm_bf16_two_chains(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                        const void* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream);
 /* W8A8 with the epilogue's order left free: the same tile, main loop and
  * exact int32 sums as bg_gemm_w8a8_pow2, then y = bf16(fp32(acc) *
  * (a_scale[m] * w_scale[n])) -- the two scales combined first, as an

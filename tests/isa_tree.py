@@ -210,6 +210,8 @@ def gemm_variants(asm):
     for name, lines in kernels(asm).items():
         t = template_ints(name)
         if "gemm_bf16_pipe_kernel" in name:          # <BM, BN, WM, WN, NS, OUT, RED, BK>
+            if t[5] == 4:  # the two-chain free-order twin: no single-chain contract
+                continue
             bm, bn, wm, wn, bk = t[0], t[1], t[2], t[3], t[7]
             out.append((name, lines, 0, bk // INSTR_K[0], (bm // wm // 32) * (bn // wn // 32)))
         elif "gemm_bf16_pipe_dual_kernel" in name:   # <BM, BN, WM, WN, NS, BM2, BN2, WM2, WN2, NS2, OUT, BK>

@@ -357,6 +357,20 @@ def test_every_planned_schedule_is_compiled(bg):
     assert n > 0  # some of them take a pair of tiles
 
 
+def test_two_chain_twin_refusals(bg):
+    """The two-chain free-order twin keeps bg_gemm_bf16's argument rules and
+    refuses before any launch (the pointers are never dereferenced)."""
+    p = 0x10000
+    f = bg.lib().bg_bench_gemm_bf16_two_chains
+    assert f(64, 64, 0, p, 64, p, 64, p, 64, None) == 1             # K < 1
+    assert f(64, 64, 256, p, 128, p, 256, p, 64, None) == 1         # lda < K
+    assert f(64, 64, 100, p, 104, p, 104, p, 64, None) == 2         # K off the multiple-of-8 grid
+    assert f(64, 64, 256, p + 4, 256, p, 256, p, 64, None) == 4     # misaligned
+    assert f(64, 64, 256, p, 20_000_000, p, 256, p, 64, None) == 2  # 127 x 2e7 x 2 bytes > 2^32
+    assert "32-bit copy offsets" in bg.lib().bg_last_error().decode()
+    assert f(0, 64, 256, p, 256, p, 256, p, 64, None) == 0          # nothing to do
+
+
 def test_copy_offset_limit(bg):
     """The 64-deep two-stage tiles address their copies by 32-bit byte
     offsets from the tile's first row: an explicit schedule whose

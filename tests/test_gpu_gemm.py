@@ -265,6 +265,35 @@ def test_free_twin_computes_the_product(M, split_k):
         assert np.array_equal(fixed.view(np.uint32), dC.cpu().numpy().view(np.uint32))
 
 
+TILE_128_64DEEP = {"bm": 128, "bn": 128, "bk": 64, "waves_m": 2, "waves_n": 2, "load_path": 2, "stages": 4}
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 2560), (200, 1024, 2560), (333, 520, 1000), (130, 136, 328)])
+def test_two_chain_twin_computes_the_product(M, N, K):
+    """The two-chain free-order twin (bench only): the product within fp32
+    accumulation error, over ragged tiles and a short last k tile, and on deep
+    K other bits than the order-fixed kernel on the same tile -- its chains
+    really are another order."""
+    import torch
+    import fixed_order_fp_amd as bg
+    X, W = synth.gemm_batch_sweep(M=M)
+    X = np.ascontiguousarray(X[:, :K])
+    W = np.ascontiguousarray(W[:N, :K])
+    print_case("two-chain twin", M, N, K)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    bg.bench_gemm_bf16_two_chains(to_dev_u16(X), to_dev_u16(W), dC)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    a = synth.bf16_bits_to_f32(X).astype(np.float64)
+    b = synth.bf16_bits_to_f32(W).astype(np.float64)
+    exact = a @ b.T
+    scale = np.abs(a) @ np.abs(b).T
+    assert np.all(np.abs(got.astype(np.float64) - exact) <= (K / 8 + 64) * 2.0 ** -23 * scale + 1e-30)
+    fixed = run_gemm({"mfma": "F32_32X32X16_BF16", "schedule": TILE_128_64DEEP}, X, W, out="fp32")
+    if K >= 1000:
+        assert np.count_nonzero(fixed.view(np.uint32) != got.view(np.uint32)) > 0
+
+
 # ---------------------------------------------------------------------------
 # the full workloads, in the launch configuration the bench times (default
 # schedules), on outputs sampled for the oracle
