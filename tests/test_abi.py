@@ -4,6 +4,7 @@ signature, cut rule, workspace size, refusals) behaves as documented."""
 import ctypes as C
 import os
 import re
+import sys
 
 import pytest
 
@@ -396,3 +397,14 @@ def test_copy_offset_limit(bg):
     huge = 20_000_000  # 255 x 2e7 bytes > 2^32
     st = bg.lib().bg_gemm_w8a8_pow2(C.byref(w), 1024, 1024, 2048, p, huge, p, 2048, p, p, p, 1024, None, 0, None)
     assert st == 2 and "32-bit offsets" in bg.lib().bg_last_error().decode()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: any other --gpus exits with status 2 and a
+    message, before anything touches a device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "measures one GPU" in r.stderr
