@@ -196,15 +196,18 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
             }
 }
 
-// The pipelined W8A8 kernel: the bf16 pipelined kernel's schedule (NS
-// stages of 64-byte k tiles copied straight to LDS, one barrier per turn
+// The pipelined W8A8 kernel: the bf16 pipelined kernel's schedule (a ring
+// of NS stages of k tiles copied straight to LDS, one barrier per turn
 // placed before the last k-step with the next copies spread among that
-// step's MFMAs, MFMA operands swapped so that a lane holds 4 consecutive
-// columns of one row) on v_mfma_i32_32x32x32_i8, whose int32 sum is exact in
-// any order.  The epilogue applies the fixed order above to 4 columns at a
-// time and stages the bf16 tile in LDS for row-contiguous 16-byte streaming
-// stores.  A short last k tile (K not a multiple of 64) is copied
-// through registers with zeros past K.
+// step's MFMAs; or two stages with the next tile's copies in one burst;
+// MFMA operands swapped so that a lane holds 4 consecutive columns of one
+// row) on v_mfma_i32_32x32x32_i8, whose int32 sum is exact in any order.
+// Two or three stages take 128-byte k tiles (every copy fetches whole
+// 128-byte lines; three stages of the 128x192 tile hold 120 KB), rings of
+// four or more 64-byte ones.  The epilogue applies the fixed order above to
+// 4 columns at a time and stages the bf16 tile in LDS for row-contiguous
+// 16-byte streaming stores.  A short last k tile (K not a multiple of the
+// tile) is copied through registers with zeros past K.
 // MODE 0: Y; 1: Y and the int32 accumulators; 2: the accumulators only (no
 // scales, no Y: the integer products other paths build on); 3: Y with the
 // epilogue's order left free (the bench's free-order twin); 4 and 5: the
@@ -212,18 +215,18 @@ __global__ __launch_bounds__(64 * WM * WN) void w8a8_kernel(
 // outputs written through Y (see the epilogue)
 template <int BM, int BN, int WM, int WN, int NS, int MODE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(
-    PipeOcc<BM, BN, WM, WN, NS, 1, NS == 2 ? 128 : 64>::WAVES_PER_EU,
-    PipeOcc<BM, BN, WM, WN, NS, 1, NS == 2 ? 128 : 64>::WAVES_PER_EU)))
+    PipeOcc<BM, BN, WM, WN, NS, 1, NS <= 3 ? 128 : 64>::WAVES_PER_EU,
+    PipeOcc<BM, BN, WM, WN, NS, 1, NS <= 3 ? 128 : 64>::WAVES_PER_EU)))
 void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* __restrict__ W, int64_t ldw,
                       const float* __restrict__ a_scale, const float* __restrict__ w_scale,
                       uint16_t* __restrict__ Y, int64_t ldy, int32_t* __restrict__ acc_out, int64_t ld_acc,
                       int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, int group_m,
                       const int* __restrict__ ea, const int* __restrict__ eb)
 {
-    // k tile (bytes), chunks per row, k-steps: 64-byte tiles in a ring of
-    // three or more stages, or 128-byte tiles (whole 128-byte lines per copy)
-    // in two stages
-    constexpr int PK = NS == 2 ? 128 : 64, PCPR = PK / kChunk, KS = PK / 32;
+    // k tile (bytes), chunks per row, k-steps: 128-byte tiles (whole
+    // 128-byte lines per copy) in two stages or a ring of three, 64-byte
+    // tiles in a ring of four or more
+    constexpr int PK = NS <= 3 ? 128 : 64, PCPR = PK / kChunk, KS = PK / 32;
     constexpr int NW = WM * WN, NT = 64 * NW;
     constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int A_CH = BM * PCPR, B_CH = BN * PCPR;
@@ -235,7 +238,7 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
     static_assert(A_CH % 64 == 0 && B_CH % 64 == 0, "tile rows must fill whole copy slots");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must hold whole MFMA blocks");
     static_assert(NS == 2 || (NS >= 3 && LOADS_HI * (NS - 2) < 64), "stages: three at least, waits within vmcnt");
-    static_assert(NS == 2 || KS == 2, "two k-steps per turn");
+    static_assert(KS % 2 == 0, "whole pairs of k-steps per turn");
     static_assert(NS != 2 || (EXTRA == 0 && ROUNDS < 64), "128-byte tiles: equal copy rounds");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS holds 160 KiB");
     __shared__ u32x4 lds[LDS_BYTES / 16];
@@ -360,12 +363,18 @@ void w8a8_pipe_kernel(const int8_t* __restrict__ A, int64_t lda, const int8_t* _
 
         i32x4 xa[2][TM], xb[2][TN];
         rd(0, 0, xa[0], xb[0]);
+        // k-steps 0 .. KS-2: read the operands of the next k-step, multiply
+        // this one (the fragment buffers alternate; KS is even, so the last
+        // k-step's operands sit in buffer 1)
         auto turn = [&](int t, auto full_tag) {
             constexpr bool FULL = decltype(full_tag)::value;
-            rd(t, 1, xa[1], xb[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mm(xa[0], xb[0]);
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks + 1 < KS; ks++) {
+                rd(t, ks + 1, xa[(ks + 1) & 1], xb[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                mm(xa[ks & 1], xb[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (FULL) {
                 if (hi) wait_vmcnt<LOADS_HI * (NS - 3)>();
                 else wait_vmcnt<LOADS_LO * (NS - 3)>();
@@ -641,6 +650,7 @@ using namespace w8a8_impl;
 // buffer, 2 pipelined, LDS stages of the pipelined path)
 #define BG_W8A8_TILES(X)                             \
     X(BG_MFMA_I32_32X32X32_I8, 128, 192, 4, 2, 2, 2) \
+    X(BG_MFMA_I32_32X32X32_I8, 128, 192, 4, 2, 2, 3) \
     X(BG_MFMA_I32_32X32X32_I8, 256, 256, 2, 4, 2, 2) \
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 2) \
     X(BG_MFMA_I32_32X32X32_I8, 128, 128, 2, 2, 2, 4) \

@@ -114,8 +114,10 @@ typedef struct {
                                  fewest A and B rows)                      */
     int32_t stages;           /* k tiles held in LDS by path 2 (0 = the
                                  tile's default); for W8A8 on path 2, two
-                                 stages take 128-byte k tiles, three or
-                                 more 64-byte ones                         */
+                                 or three stages take 128-byte k tiles
+                                 (two stages address their copies by
+                                 32-bit offsets), four or more 64-byte
+                                 ones                                      */
     int32_t last_bm, last_bn; /* path 2 with split_k > 1: the last split
                                  (the cut rule's remainder, the deepest)
                                  takes this tile in the same launch; all

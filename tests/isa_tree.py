@@ -235,7 +235,7 @@ def w8a8_variants(asm):
         t = template_ints(name)
         if "w8a8_pipe_kernel" in name:               # <BM, BN, WM, WN, NS, MODE>: k tiles of 64 bytes, 128 at NS 2
             bm, bn, wm, wn, ns = t[0], t[1], t[2], t[3], t[4]
-            pk = 128 if ns == 2 else 64
+            pk = 128 if ns <= 3 else 64  # two or three stages: 128-byte k tiles
             out.append((name, lines, 2, pk // INSTR_K[2], (bm // wm // 32) * (bn // wn // 32)))
         elif "w8a8_kernel" in name:                  # <INSTR, BM, BN, WM, WN, ACC_OUT>, k tiles of 128 bytes
             i, bm, bn, wm, wn = t[0], t[1], t[2], t[3], t[4]

@@ -39,9 +39,10 @@ def bf16_pipe_tiles():
 
 
 def w8a8_pipe_tiles():
-    """(bm, bn, wm, wn, ns, k tile bytes): two stages take 128-byte k tiles."""
+    """(bm, bn, wm, wn, ns, k tile bytes): two or three stages take 128-byte
+    k tiles, rings of four or more 64-byte ones."""
     src = open(os.path.join(CSRC, "bg_w8a8.hip")).read()
-    return [(bm, bn, wm, wn, ns, 128 if ns == 2 else 64)
+    return [(bm, bn, wm, wn, ns, 128 if ns <= 3 else 64)
             for i, bm, bn, wm, wn, path, ns in _macro_rows(src, "BG_W8A8_TILES") if path == 2]
 
 

@@ -14,9 +14,10 @@ from gpu_util import from_dev_u16, print_case, require_gpu
 pytestmark = pytest.mark.gpu
 
 # (instruction, bm, bn, waves_m, waves_n, load path, stages): path 2 is the
-# pipelined kernel (two stages: 128-byte k tiles; three or more: 64-byte
-# ones), path 1 the double-buffered one
-TILES = [("I32_32X32X32_I8", 128, 192, 4, 2, 2, 2), ("I32_32X32X32_I8", 256, 256, 2, 4, 2, 2),
+# pipelined kernel (two or three stages: 128-byte k tiles; four or more:
+# 64-byte ones), path 1 the double-buffered one
+TILES = [("I32_32X32X32_I8", 128, 192, 4, 2, 2, 2), ("I32_32X32X32_I8", 128, 192, 4, 2, 2, 3),
+         ("I32_32X32X32_I8", 256, 256, 2, 4, 2, 2),
          ("I32_32X32X32_I8", 128, 128, 2, 2, 2, 2),
          ("I32_32X32X32_I8", 128, 128, 2, 2, 2, 4), ("I32_32X32X32_I8", 128, 128, 2, 2, 2, 5),
          ("I32_32X32X32_I8", 256, 256, 2, 4, 2, 4), ("I32_32X32X32_I8", 128, 192, 2, 2, 2, 4),
